@@ -1,0 +1,204 @@
+"""Pins of the oracle's quantizer against hand-computed fixtures, library
+conversions (torch's float8_e4m3fn and float16 casts) and invariants that the
+definition fixes. CPU only."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.quant import pack_int4
+from golden_io import load
+
+
+def _golden_block(name):
+    g = load(name)
+    x = np.array(g["input"], dtype=np.float32)
+    n = x.size
+    x = x.reshape(1, 1, *(g.get("layout_rows_by_channels") or (n, 1)))
+    codes, scales = oracle.block_quant(x, g["block_rows"], g["qtype"], g["scale_dtype"])
+    return g, codes, scales
+
+
+@pytest.mark.parametrize("name", ["int8_ties.txt", "int8_scale_half.txt", "e4m3_points.txt",
+                                  "int4_pack.txt"])
+def test_golden_quant(name):
+    g, codes, scales = _golden_block(name)
+    assert float(scales.ravel()[0]) == g["scale"]
+    want = np.array(g["codes"] if isinstance(g["codes"], list) else [g["codes"]])
+    if g["qtype"] == "int8":
+        assert codes.ravel().astype(np.int64).tolist() == want.tolist()
+    else:
+        assert codes.ravel().astype(np.int64).tolist() == (want & 0xFF).tolist()
+
+
+def _torch_e4m3(x32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def _e4m3_test_values() -> np.ndarray:
+    """Every fp16 and bf16 value with |x| <= 448, the 128 fp32 neighbours on each
+    side of every e4m3 rounding midpoint, and random fp32 bit patterns."""
+    parts = []
+    h = np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float32)
+    parts.append(h)
+    bf = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    parts.append(bf)
+    pos = oracle.e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))  # 0 .. 448
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)  # exact in fp32
+    bits = mids.view(np.uint32).astype(np.int64)
+    off = np.arange(-128, 129)
+    near = (bits[:, None] + off[None, :]).ravel()
+    near = near[near >= 0].astype(np.uint32).view(np.float32)
+    parts += [near, -near]
+    rng = np.random.default_rng(0)
+    rb = rng.integers(0, 0x43E00001, size=1 << 20, dtype=np.uint32).view(np.float32)
+    parts += [rb, -rb]
+    x = np.concatenate(parts)
+    x = x[np.isfinite(x) & (np.abs(x) <= 448)]
+    return x
+
+
+def test_e4m3_encode_matches_torch():
+    x = _e4m3_test_values()
+    assert x.size > 300_000
+    np.testing.assert_array_equal(oracle.e4m3fn_encode(x), _torch_e4m3(x))
+
+
+def test_e4m3_decode_matches_torch():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.e4m3fn_decode(codes), ref)
+    assert np.isnan(oracle.e4m3fn_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_e4m3_saturation_of_clamped_values():
+    # 463.999 is clamped to 448 before encoding; encoding itself rejects > 448.
+    t = np.clip(np.float32(463.999), -448, 448)
+    assert oracle.e4m3fn_encode(np.array([t]))[0] == 0x7E
+    with pytest.raises(ValueError):
+        oracle.e4m3fn_encode(np.array([449.0], np.float32))
+
+
+def test_fp16_round_matches_torch():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.standard_normal(1 << 18).astype(np.float32) * 10.0 ** rng.integers(-8, 4, 1 << 18),
+        # float32 values around every fp16 rounding midpoint of the positive range
+        ((np.arange(0x7BFF, dtype=np.uint16).view(np.float16).astype(np.float64)
+          + np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)) / 2
+         ).astype(np.float32),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(x).half().float().numpy()
+    np.testing.assert_array_equal(oracle.fp16_round(x), ref)
+
+
+def test_int4_pack_roundtrip():
+    rng = np.random.default_rng(2)
+    c = rng.integers(-8, 8, size=(3, 5, 128)).astype(np.int8)
+    p = pack_int4(c)
+    assert p.shape == (3, 5, 64) and p.dtype == np.uint8
+    np.testing.assert_array_equal(oracle.unpack_int4(p), c)
+    assert p[0, 0, 0] == ((int(c[0, 0, 0]) & 0xF) | ((int(c[0, 0, 1]) & 0xF) << 4))
+
+
+def _random_input(shape, dtype, seed, zero_block=None, block_rows=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(*shape, generator=g) * torch.exp(torch.randn(shape[:2] + (1, 1), generator=g))
+    if zero_block is not None:
+        b, n, r = zero_block
+        x[b, n, r * block_rows:(r + 1) * block_rows] = 0
+    return x.to(dtype)
+
+
+CASES = [
+    # qtype, block_rows, scale dtype, in dtype, S, D
+    ("int8", 128, "f32", torch.float16, 300, 128),
+    ("int8", 256, "f32", torch.float32, 513, 64),
+    ("int8", 256, "f16", torch.float16, 700, 128),
+    ("fp8", 128, "f32", torch.bfloat16, 260, 128),
+    ("fp8", 256, "f32", torch.bfloat16, 511, 128),
+    ("int4", 1, "f16", torch.float16, 37, 128),
+    ("int4", 16, "f32", torch.float32, 50, 64),
+]
+
+
+@pytest.mark.parametrize("qtype,R,sdt,dt,S,D", CASES)
+def test_quant_invariants(qtype, R, sdt, dt, S, D):
+    qmax = oracle.QMAX[qtype]
+    x = _random_input((2, 3, S, D), dt, seed=S + D, zero_block=(1, 2, 0), block_rows=R)
+    codes, scales = oracle.block_quant(x, R, qtype, sdt)
+    nblk = -(-S // R)
+    assert scales.shape == (2, 3, nblk)
+    assert scales.dtype == (np.float16 if sdt == "f16" else np.float32)
+    vals = oracle.code_values(codes, qtype)
+    x64 = x.double().numpy()
+    s64 = np.repeat(scales.astype(np.float64), R, axis=2)[:, :, :S, None]
+    # I3: |code| <= qmax
+    assert np.abs(vals).max() <= qmax
+    # zero block: scale 0 and all-zero codes
+    assert scales[1, 2, 0] == 0 and np.all(vals[1, 2, :R] == 0)
+    # I1: every nonzero block reaches qmax exactly
+    blk = np.pad(np.abs(vals), ((0, 0), (0, 0), (0, nblk * R - S), (0, 0))).reshape(
+        2, 3, nblk, R * D).max(axis=3)
+    np.testing.assert_array_equal(blk[scales != 0], qmax)
+    # amax definition: scale = fl32(amax / qmax), rounded to fp16 when asked
+    amax = np.pad(np.abs(x.float().numpy()), ((0, 0), (0, 0), (0, nblk * R - S), (0, 0))
+                  ).reshape(2, 3, nblk, R * D).max(axis=3)
+    s_ref = (amax / np.float32(qmax)).astype(np.float32)
+    if sdt == "f16":
+        s_ref = torch.from_numpy(s_ref).half().float().numpy()
+    np.testing.assert_array_equal(scales.astype(np.float32), s_ref)
+    # I2: reconstruction error at most half a code step (plus the fp32 quotient's rounding)
+    err = np.abs(x64 - s64 * vals)
+    if qtype in ("int8", "int4"):
+        bound = s64 * (0.5 + qmax * 2.0 ** -23)
+    else:
+        t = np.abs(vals)
+        e = np.maximum(np.floor(np.log2(np.maximum(t, 2.0 ** -9))), -6)
+        bound = s64 * (2.0 ** (e - 4) * 1.0001 + 448 * 2.0 ** -23)
+    assert np.all(err <= bound + 1e-300)
+
+
+@pytest.mark.parametrize("qtype,R", [("int8", 128), ("fp8", 256), ("int4", 1)])
+def test_quant_layouts_agree(qtype, R):
+    """I4: BSND codes equal BNSD codes transposed, scales identical."""
+    x = _random_input((2, 3, 300, 64), torch.float16, seed=7)
+    c1, s1 = oracle.block_quant(x, R, qtype, "f32", layout="bnsd")
+    c2, s2 = oracle.block_quant(x.transpose(1, 2).contiguous(), R, qtype, "f32", layout="bsnd")
+    np.testing.assert_array_equal(c2, c1.transpose(0, 2, 1, 3))
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_quant_row_permutation_within_block():
+    """I5: permuting rows inside a block permutes the codes and keeps the scale."""
+    x = _random_input((1, 2, 256, 128), torch.float32, seed=9)
+    perm = torch.randperm(128, generator=torch.Generator().manual_seed(3))
+    xp = x.clone()
+    xp[:, :, :128] = x[:, :, perm]
+    c1, s1 = oracle.block_quant(x, 128, "int8")
+    c2, s2 = oracle.block_quant(xp, 128, "int8")
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(c2[:, :, :128], c1[:, :, perm.numpy()])
+    np.testing.assert_array_equal(c2[:, :, 128:], c1[:, :, 128:])
+
+
+def test_quant_fp16_scale_codes_use_rounded_scale():
+    """With fp16 scales, codes come from the stored (rounded) scale."""
+    x = np.array([[[[1.0, -0.3, 0.77, 0.5]]]], dtype=np.float32)  # amax 1 -> 1/7 rounds in fp16
+    codes, scales = oracle.block_quant(x, 1, "int4", "f16")
+    s = np.float32(np.float16(np.float32(1.0) / np.float32(7.0)))
+    assert scales.astype(np.float32)[0, 0, 0] == s
+    t = (x / s).astype(np.float32)
+    expect = np.clip(np.rint(t), -8, 7).astype(np.int64).ravel()
+    np.testing.assert_array_equal(oracle.unpack_int4(codes).ravel(), expect)
+
+
+def test_dequantize_inverse_layouts():
+    x = _random_input((1, 2, 130, 64), torch.bfloat16, seed=11)
+    for layout, xin in (("bnsd", x), ("bsnd", x.transpose(1, 2).contiguous())):
+        codes, scales = oracle.block_quant(xin, 64, "fp8", layout=layout)
+        xh = oracle.dequantize(codes, scales, 64, "fp8", layout=layout)
+        assert xh.shape == (1, 2, 130, 64)
+        s = np.repeat(scales.astype(np.float64), 64, axis=2)[:, :, :130, None]
+        assert np.all(np.abs(xh - x.double().numpy()) <= s * 16 * (1 + 1e-6))
