@@ -1,0 +1,201 @@
+"""Benchmark: block-quantized FlashAttention on one MI355X.
+
+One step = quantize Q, K and V (qfa_block_quant x3) and run the INT8 causal
+attention forward (qfa_fwd) on the LLaMA-2-7B head shape workload
+``int8_causal_h32_s4096`` (B=1, H=32, S=4096, D=128, fp16 inputs with four
+outlier K channels), inputs resident in HBM. ``value`` is the attention's
+algorithmic ops (unmasked pairs, multiply and add counted) per second of the
+whole step. The dominant kernel (the forward) is also timed alone with HIP
+events and reported against the dense INT8 MFMA peak; the decode kernel on the
+``int8_kv_decode_b32_h32`` workload is reported in GB/s against HBM peak.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # dense INT8 MFMA, MI355X
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def bench_prefill(torch, qfa, wl, steps, warmup):
+    w = wl.INT8_CAUSAL
+    q, k, v = wl.make_prefill_inputs(w, device="cuda")
+    sdt = torch.float32
+    qc, qs = qfa.block_quant(q, w.q_block, w.q_qtype, sdt)
+    kc, ks = qfa.block_quant(k, w.kv_block, w.k_qtype, sdt)
+    vc, vs = qfa.block_quant(v, w.kv_block, w.v_qtype, sdt)
+    out = torch.empty_like(q)
+
+    def step(ev=None):
+        qfa.block_quant(q, w.q_block, w.q_qtype, sdt, codes=qc, scales=qs)
+        qfa.block_quant(k, w.kv_block, w.k_qtype, sdt, codes=kc, scales=ks)
+        qfa.block_quant(v, w.kv_block, w.v_qtype, sdt, codes=vc, scales=vs)
+        if ev is not None:
+            ev[0].record()
+        qfa.fwd(qc, qs, kc, ks, vc, vs, q_qtype=w.q_qtype, k_qtype=w.k_qtype, v_qtype=w.v_qtype,
+                q_block=w.q_block, kv_block=w.kv_block, softmax_scale=w.softmax_scale,
+                causal=w.causal, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(torch) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    ops = w.attention_ops()
+    return w, wall, fwd_ms, ops
+
+
+def bench_decode(torch, qfa, wl, steps, warmup):
+    w = wl.DECODE
+    q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
+    sdt = torch.float16
+    kc, ks = qfa.block_quant(k, w.kv_block, w.kv_qtype, sdt)
+    vc, vs = qfa.block_quant(v, w.kv_block, w.kv_qtype, sdt)
+    del k, v
+    out = torch.empty_like(q)
+    ws = torch.empty(qfa.decode_workspace_bytes(w.B, w.Hq, w.S_max, w.D), dtype=torch.uint8,
+                     device="cuda")
+    # A buffer larger than the 256 MiB last-level cache, rewritten between
+    # timed calls so the cache is read from HBM every time.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def call():
+        qfa.decode(q, kc, vc, ks, vs, lens, kv_qtype=w.kv_qtype, kv_block=w.kv_block,
+                   softmax_scale=w.softmax_scale, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        flush.fill_(1)
+        a, b = _events(torch)
+        a.record()
+        call()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times)[len(times) // 2]
+    nbytes = wl.decode_kv_bytes(w, lens.cpu().tolist())
+    return w, ms, nbytes
+
+
+def cpu_baseline(wl, target_s=10.0):
+    """The oracle (quantize + float64 attention) on whole heads of the bench
+    workload, as many as fit in about ``target_s`` seconds; ops/s in TOPS."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    w = wl.INT8_CAUSAL
+    q, k, v = wl.make_prefill_inputs(w)
+    done_heads, ops, t0 = 0, 0, time.perf_counter()
+    for h in range(w.Hq):
+        qc, qs = oracle.block_quant(q[:, h:h + 1], w.q_block, w.q_qtype)
+        kc, ks = oracle.block_quant(k[:, h:h + 1], w.kv_block, w.k_qtype)
+        vc, vs = oracle.block_quant(v[:, h:h + 1], w.kv_block, w.v_qtype)
+        oracle.attention(oracle.dequantize(qc, qs, w.q_block, w.q_qtype),
+                         oracle.dequantize(kc, ks, w.kv_block, w.k_qtype),
+                         oracle.dequantize(vc, vs, w.kv_block, w.v_qtype),
+                         w.softmax_scale, w.causal)
+        done_heads += 1
+        ops += 2 * w.D * w.S * (w.S + 1)
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done_heads} of {w.Hq} heads of {w.name}: quantize Q/K/V + float64 "
+                      f"causal attention, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels shard by head or batch with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_quantized_flashattention_amd as qfa
+    import qfa_workloads as wl
+
+    log(f"prefill: {wl.INT8_CAUSAL.name}, warmup {args.warmup}, steps {args.steps}")
+    w, wall, fwd_ms, ops = bench_prefill(torch, qfa, wl, args.steps, args.warmup)
+    ms_step = wall * 1e3 / args.steps
+    value = ops / (ms_step * 1e-3) / 1e12
+    achieved = ops / (fwd_ms * 1e-3) / 1e12
+    log(f"prefill step {ms_step:.3f} ms, forward kernel {fwd_ms:.3f} ms, {achieved:.1f} TOPS")
+    rec = {
+        "metric": "quantized FA prefill TOPS + decode KV GB/s, % of MI355X MFMA/HBM peak",
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.Hq, "S": w.S, "D": w.D,
+                   "causal": w.causal, "qtype": "int8", "q_block": w.q_block,
+                   "kv_block": w.kv_block, "step": "block_quant(Q,K,V) + fwd"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": None, "kernel": "fwd_kernel<128,int8,causal>",
+                     "kernel_ms": round(fwd_ms, 4)},
+    }
+    if not args.no_decode:
+        log(f"decode: {wl.DECODE.name}")
+        dw, dms, nbytes = bench_decode(torch, qfa, wl, max(args.steps, 10), args.warmup)
+        gbs = nbytes / (dms * 1e-3) / 1e9
+        log(f"decode {dms:.3f} ms, {gbs:.0f} GB/s")
+        rec["decode"] = {"workload": dw.name, "value": round(gbs, 1), "unit": "GB/s",
+                         "ms": round(dms, 4), "bytes": nbytes,
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host")
+        rec["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

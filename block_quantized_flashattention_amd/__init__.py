@@ -1,0 +1,183 @@
+"""Block-quantized FlashAttention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of ``libqfa.so``; the functions keep the C ABI's names
+(``block_quant``, ``fwd``, ``decode``, ``decode_workspace_bytes``). This module
+only marshals arguments: torch tensors supply device memory and the current
+stream, and every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: calling into a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqfa.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "qfa.h")
+
+QTYPES = {"int8": 0, "fp8": 1, "int4": 2}
+LAYOUTS = {"bnsd": 0, "bsnd": 1}
+FLOATS = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+QMAX = {"int8": 127, "fp8": 448, "int4": 7}
+
+_lib = None
+
+
+class QFAError(RuntimeError):
+    """A nonzero status from libqfa."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().qfa_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqfa.so (raises if it was never built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_quantized_flashattention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.qfa_version.argtypes = []
+    L.qfa_version.restype = i
+    L.qfa_status_string.argtypes = [i]
+    L.qfa_status_string.restype = ctypes.c_char_p
+    L.qfa_block_quant.argtypes = [vp, i, i, i, i, i, i, i, i, vp, vp, i, vp]
+    L.qfa_block_quant.restype = i
+    L.qfa_fwd.argtypes = [vp, vp, i, i, i, vp, vp, i, vp, vp, i, i, i,
+                          i, i, i, i, i, i, i, i, f, vp, i, vp]
+    L.qfa_fwd.restype = i
+    L.qfa_decode_workspace_bytes.argtypes = [i, i, i, i]
+    L.qfa_decode_workspace_bytes.restype = sz
+    L.qfa_decode.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, i, i, vp, f, vp, i,
+                             vp, sz, vp]
+    L.qfa_decode.restype = i
+    _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/qfa.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*QFA_API\s+(?:int|size_t|const char\*)\s+(qfa_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise QFAError(fn, status)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+
+
+def code_dtype(qtype: str) -> torch.dtype:
+    return torch.int8 if qtype == "int8" else torch.uint8
+
+
+def block_quant(x: torch.Tensor, block_rows: int, qtype: str, scale_dtype=torch.float32,
+                layout: str = "bnsd", codes=None, scales=None, stream=None):
+    """Quantize ``x`` per block of ``block_rows`` rows; returns (codes, scales).
+
+    x: [B,N,S,D] (bnsd) or [B,S,N,D] (bsnd); codes in the same layout (last dim
+    D/2 for int4, int8 for INT8, uint8 for FP8 e4m3fn and packed INT4); scales
+    [B,N,ceil(S/block_rows)] of ``scale_dtype``.
+    """
+    _dev(x, "x")
+    if layout == "bnsd":
+        B, N, S, D = x.shape
+    else:
+        B, S, N, D = x.shape
+    cshape = list(x.shape[:-1]) + [D // 2 if qtype == "int4" else D]
+    if codes is None:
+        codes = torch.empty(cshape, dtype=code_dtype(qtype), device=x.device)
+    if scales is None:
+        scales = torch.empty(B, N, -(-S // block_rows), dtype=scale_dtype, device=x.device)
+    _dev(codes, "codes")
+    _dev(scales, "scales")
+    _check("qfa_block_quant", lib().qfa_block_quant(
+        _ptr(x), FLOATS[x.dtype], B, N, S, D, LAYOUTS[layout], block_rows, QTYPES[qtype],
+        _ptr(codes), _ptr(scales), FLOATS[scales.dtype], _stream(stream)))
+    return codes, scales
+
+
+def fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, q_qtype: str, k_qtype: str,
+        v_qtype: str, q_block: int, kv_block: int, softmax_scale: float, causal: bool = False,
+        layout: str = "bnsd", out_dtype=torch.float16, out=None, stream=None):
+    """Attention forward on block-quantized codes; returns out [B,Hq,Sq,D] (or BSND)."""
+    for t, n in ((q_codes, "q_codes"), (q_scales, "q_scales"), (k_codes, "k_codes"),
+                 (k_scales, "k_scales"), (v_codes, "v_codes"), (v_scales, "v_scales")):
+        _dev(t, n)
+    if layout == "bnsd":
+        B, Hq, Sq, D = q_codes.shape
+        Hkv, Sk = k_codes.shape[1], k_codes.shape[2]
+    else:
+        B, Sq, Hq, D = q_codes.shape
+        Sk, Hkv = k_codes.shape[1], k_codes.shape[2]
+    if out is None:
+        out = torch.empty(q_codes.shape, dtype=out_dtype, device=q_codes.device)
+    _dev(out, "out")
+    if q_scales.dtype != torch.float32 and q_scales.dtype != torch.float16:
+        raise ValueError("scales must be float32 or float16")
+    _check("qfa_fwd", lib().qfa_fwd(
+        _ptr(q_codes), _ptr(q_scales), QTYPES[q_qtype], q_block, FLOATS[q_scales.dtype],
+        _ptr(k_codes), _ptr(k_scales), QTYPES[k_qtype], _ptr(v_codes), _ptr(v_scales),
+        QTYPES[v_qtype], kv_block, FLOATS[k_scales.dtype], B, Hq, Hkv, Sq, Sk, D,
+        LAYOUTS[layout], int(bool(causal)), float(softmax_scale), _ptr(out), FLOATS[out.dtype],
+        _stream(stream)))
+    return out
+
+
+def decode_workspace_bytes(B: int, Hq: int, S_max: int, D: int) -> int:
+    return int(lib().qfa_decode_workspace_bytes(B, Hq, S_max, D))
+
+
+def decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtype: str, kv_block: int,
+           softmax_scale: float, layout: str = "bnsd", out_dtype=None, out=None, workspace=None,
+           stream=None):
+    """One query token per sequence against a quantized KV cache; returns out [B,Hq,1,D]."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (k_scales, "k_scales"),
+                 (v_scales, "v_scales"), (seq_lens, "seq_lens")):
+        _dev(t, n)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    B, Hq, D = q.shape[0], q.numel() // (q.shape[0] * q.shape[-1]), q.shape[-1]
+    if layout == "bnsd":
+        Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    else:
+        S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _dev(out, "out")
+    need = decode_workspace_bytes(B, Hq, S_max, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("qfa_decode", lib().qfa_decode(
+        _ptr(q), FLOATS[q.dtype], B, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+        _ptr(v_scales), QTYPES[kv_qtype], kv_block, FLOATS[k_scales.dtype], S_max,
+        LAYOUTS[layout], _ptr(seq_lens), float(softmax_scale), _ptr(out), FLOATS[out.dtype],
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+__all__ = ["block_quant", "fwd", "decode", "decode_workspace_bytes", "lib", "header_functions",
+           "QFAError", "QTYPES", "LAYOUTS", "FLOATS", "QMAX", "code_dtype"]

@@ -1,0 +1,122 @@
+// C ABI of libqfa: argument validation and dispatch to the kernel launchers.
+// Every check runs on the host before any HIP call, so an invalid call
+// returns its status without touching the device.
+#include <stdint.h>
+
+#include "qfa.h"
+#include "qfa_launch.h"
+
+namespace {
+
+bool valid_float(int t) { return t == QFA_F32 || t == QFA_F16 || t == QFA_BF16; }
+bool valid_qtype(int t) { return t == QFA_INT8 || t == QFA_FP8_E4M3 || t == QFA_INT4; }
+bool valid_layout(int t) { return t == QFA_BNSD || t == QFA_BSND; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? QFA_OK : QFA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int qfa_version(void) { return 100; }
+
+const char* qfa_status_string(int status) {
+  switch (status) {
+    case QFA_OK: return "ok";
+    case QFA_ERR_NULL: return "a required pointer is NULL";
+    case QFA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case QFA_ERR_ENUM: return "an enumeration value is unknown";
+    case QFA_ERR_UNSUPPORTED: return "valid combination not implemented by this build";
+    case QFA_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case QFA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int qfa_block_quant(const void* x, int x_dtype, int B, int N, int S, int D, int layout,
+                    int block_rows, int qtype, void* codes, void* scales, int scale_dtype,
+                    void* stream) {
+  if (!valid_float(x_dtype) || !valid_layout(layout) || !valid_qtype(qtype) ||
+      (scale_dtype != QFA_F32 && scale_dtype != QFA_F16))
+    return QFA_ERR_ENUM;
+  if (B < 0 || N < 0 || S < 0 || D < 8 || D > 1024 || D % 8 != 0 || block_rows < 1)
+    return QFA_ERR_SHAPE;
+  if ((long)B * N * S == 0) return QFA_OK;
+  if (!x || !codes || !scales) return QFA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, qtype == QFA_INT4 ? 4 : 8) ||
+      !aligned(scales, scale_dtype == QFA_F16 ? 2 : 4))
+    return QFA_ERR_UNSUPPORTED;
+  qfa::QuantArgs a{x, x_dtype, B, N, S, D, layout, block_rows, qtype, codes, scales, scale_dtype};
+  return from_hip(qfa::launch_block_quant(a, (hipStream_t)stream));
+}
+
+int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
+            int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
+            const void* v_codes, const void* v_scales, int v_qtype, int kv_block,
+            int kv_scale_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int layout,
+            int causal, float softmax_scale, void* out, int out_dtype, void* stream) {
+  if (!valid_qtype(q_qtype) || !valid_qtype(k_qtype) || !valid_qtype(v_qtype) ||
+      !valid_layout(layout) || !valid_float(out_dtype) ||
+      (q_scale_dtype != QFA_F32 && q_scale_dtype != QFA_F16) ||
+      (kv_scale_dtype != QFA_F32 && kv_scale_dtype != QFA_F16))
+    return QFA_ERR_ENUM;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 0 || Sk < 0 || q_block < 1 ||
+      kv_block < 1 || (causal != 0 && causal != 1))
+    return QFA_ERR_SHAPE;
+  if (D != 64 && D != 128) return QFA_ERR_UNSUPPORTED;
+  if (causal && Sq != Sk) return QFA_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return QFA_OK;
+  if (Sk < 1) return QFA_ERR_SHAPE;
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f || softmax_scale > 3.0e38f)
+    return QFA_ERR_SHAPE;
+  const bool int8_qk = q_qtype == QFA_INT8 && (k_qtype == QFA_INT8 || k_qtype == QFA_INT4);
+  const bool fp8_qk = q_qtype == QFA_FP8_E4M3 && k_qtype == QFA_FP8_E4M3;
+  if (!int8_qk && !fp8_qk) return QFA_ERR_UNSUPPORTED;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out)
+    return QFA_ERR_NULL;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(out, 16) || !aligned(q_scales, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return QFA_ERR_UNSUPPORTED;
+  qfa::FwdArgs a{q_codes, q_scales, q_qtype, q_block, q_scale_dtype, k_codes, k_scales, k_qtype,
+                 v_codes, v_scales, v_qtype, kv_block, kv_scale_dtype, B, Hq, Hkv, Sq, Sk, D,
+                 layout, causal, softmax_scale, out, out_dtype};
+  return from_hip(qfa::launch_fwd(a, (hipStream_t)stream));
+}
+
+size_t qfa_decode_workspace_bytes(int B, int Hq, int S_max, int D) {
+  if (B < 1 || Hq < 1 || S_max < 1 || (D != 64 && D != 128)) return 0;
+  return qfa::decode_workspace_bytes(B, Hq, S_max, D);
+}
+
+int qfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D, const void* k_cache,
+               const void* v_cache, const void* k_scales, const void* v_scales, int kv_qtype,
+               int kv_block, int kv_scale_dtype, int S_max, int layout, const int32_t* seq_lens,
+               float softmax_scale, void* out, int out_dtype, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!valid_float(q_dtype) || !valid_float(out_dtype) || !valid_qtype(kv_qtype) ||
+      !valid_layout(layout) || (kv_scale_dtype != QFA_F32 && kv_scale_dtype != QFA_F16))
+    return QFA_ERR_ENUM;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 || kv_block < 1)
+    return QFA_ERR_SHAPE;
+  if (D != 64 && D != 128) return QFA_ERR_UNSUPPORTED;
+  if (kv_qtype == QFA_FP8_E4M3) return QFA_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return QFA_ERR_UNSUPPORTED;
+  if (B == 0) return QFA_OK;
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f || softmax_scale > 3.0e38f)
+    return QFA_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !k_scales || !v_scales || !seq_lens || !out)
+    return QFA_ERR_NULL;
+  const size_t need = qfa::decode_workspace_bytes(B, Hq, S_max, D);
+  if (S_max > qfa::kDecodeChunk && (!workspace || workspace_bytes < need))
+    return QFA_ERR_WORKSPACE;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 16) ||
+      !aligned(q, 4) || !aligned(out, 4) || !aligned(seq_lens, 4))
+    return QFA_ERR_UNSUPPORTED;
+  qfa::DecodeArgs a{q, q_dtype, B, Hq, Hkv, D, k_cache, v_cache, k_scales, v_scales, kv_qtype,
+                    kv_block, kv_scale_dtype, S_max, layout, seq_lens, softmax_scale, out,
+                    out_dtype, workspace};
+  return from_hip(qfa::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

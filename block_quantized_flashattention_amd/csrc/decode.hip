@@ -1,0 +1,316 @@
+// Decode attention: one query token per sequence against an INT8 or packed
+// INT4 KV cache with block scales (gfx950).
+//
+// What it computes ([Ascend-INT8] INT8-operator section 3: the decode KV
+// cache is stored as INT8 and attention reads it without writing a
+// dequantized copy; [FA-INT8/INT4] INT4 layer for the INT4 codes):
+//   o_bh = sum_{j < L_b} softmax_j(softmax_scale * q_bh . (sk_j Kc_j)) * sv_j Vc_j
+//
+// Design (HBM-bound: every valid cache byte is read once):
+//   * Split-K: a workgroup of 4 wavefronts owns one (batch, query head,
+//     1024-token chunk); each wavefront owns 256 tokens of the chunk. Chunks
+//     past a sequence's length exit at once. A second small kernel merges the
+//     chunks' partial (max, sum, o) by log-sum-exp; a sequence that fits one
+//     chunk is written directly.
+//   * Lane geometry: a 16-byte load per lane, LPT = row_bytes/16 lanes per
+//     token, so one wavefront load covers 64/LPT consecutive tokens.
+//   * Two passes per 256 tokens: scores for all of them first (dot product
+//     over the lane's channels, then a butterfly over the LPT lanes), their
+//     max, one rescale of the running (max, sum, o), then exp2 and the V
+//     accumulation. Every lane accumulates o for its own channels over its
+//     own tokens; the token groups are summed once at the end.
+//   * Codes are converted with the unsigned-byte converter after flipping the
+//     sign bit (code + 128 for INT8, code + 8 for INT4); the offset is
+//     removed once per token (scores) or once per output channel (values).
+#include "qfa_device.h"
+#include "qfa_launch.h"
+
+namespace qfa {
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kWaveTokens = kDecodeChunk / kDecWaves;  // 256
+
+struct DecParams {
+  const void* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const void* ks;
+  const void* vs;
+  const int32_t* lens;
+  void* out;
+  float* ws;
+  int Hq, Hkv, group, S_max, max_splits;
+  long c_row, c_head, c_batch;  // byte strides of the caches
+  long q_head, q_batch;         // element strides of q and out
+  int kv_block, nkblk, kv_scale_f16, q_dtype, out_dtype;
+  float scale_log2;
+};
+
+__device__ __forceinline__ float load_q(const void* q, long i, int dt) {
+  if (dt == QFA_F32) return ((const float*)q)[i];
+  const uint32_t hb = ((const uint16_t*)q)[i];
+  return dt == QFA_F16 ? f16_bits_to_f32(hb) : bf16_bits_to_f32(hb);
+}
+
+__device__ __forceinline__ void store_out(void* out, long i, float v, int dt) {
+  if (dt == QFA_F32) ((float*)out)[i] = v;
+  else if (dt == QFA_F16) ((uint16_t*)out)[i] = (uint16_t)f32_to_f16_bits(v);
+  else ((uint16_t*)out)[i] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+// Offset codes (code + 128, or code + 8 for INT4) of one 16-byte lane chunk as floats.
+template <bool INT4>
+__device__ __forceinline__ void chunk_to_f32(const uint4& w, float* f) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (!INT4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = ww[i] ^ 0x80808080u;
+      f[4 * i + 0] = (float)(u & 0xFFu);
+      f[4 * i + 1] = (float)((u >> 8) & 0xFFu);
+      f[4 * i + 2] = (float)((u >> 16) & 0xFFu);
+      f[4 * i + 3] = (float)(u >> 24);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = ww[i] ^ 0x88888888u;
+      const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[8 * i + 2 * j] = (float)((lo >> (8 * j)) & 0xFFu);
+        f[8 * i + 2 * j + 1] = (float)((hi >> (8 * j)) & 0xFFu);
+      }
+    }
+  }
+}
+
+template <int D, bool INT4>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams p) {
+  constexpr int kRowBytes = INT4 ? D / 2 : D;
+  constexpr int LPT = kRowBytes / 16;        // lanes per token
+  constexpr int EPL = INT4 ? 32 : 16;        // channels per lane
+  constexpr int TPS = 64 / LPT;              // tokens per wavefront load
+  constexpr int NSUB = kWaveTokens / TPS;    // loads per 256 tokens
+  constexpr float kOff = INT4 ? 8.0f : 128.0f;
+  __shared__ float red_m[kDecWaves], red_l[kDecWaves];
+  __shared__ float red_o[kDecWaves][D];
+
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = min(max(p.lens[b], 1), p.S_max);
+  const int nsplit = (L + kDecodeChunk - 1) / kDecodeChunk;
+  if (split >= nsplit) return;
+  const int kvh = h / p.group;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tg = lane / LPT;          // token within a load
+  const int dc = lane % LPT;          // channel chunk
+  const int d0 = dc * EPL;
+
+  float qf[EPL];
+  float qsum = 0.0f;
+  const long qoff = (long)b * p.q_batch + (long)h * p.q_head;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    qf[e] = load_q(p.q, qoff + d0 + e, p.q_dtype);
+    qsum += qf[e];
+  }
+
+  const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
+  const uint8_t* kp = p.k + cbase + dc * 16;
+  const uint8_t* vp = p.v + cbase + dc * 16;
+  const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
+
+  const int t_begin = split * kDecodeChunk + wave * kWaveTokens;
+  const int t_end = min(t_begin + kWaveTokens, L);
+
+  float m_run = -INFINITY, l_run = 0.0f, wsum = 0.0f;
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
+
+  if (t_begin < t_end) {
+    float sc[NSUB];
+    float mblk = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      const int t = t_begin + j * TPS + tg;
+      const bool ok = t < t_end;
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) w = *(const uint4*)(kp + (long)t * p.c_row);
+      float f[EPL];
+      chunk_to_f32<INT4>(w, f);
+      float acc = -kOff * qsum;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc = __builtin_fmaf(qf[e], f[e], acc);
+#pragma unroll
+      for (int off = LPT / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+      const float sk = ok ? load_scale(p.ks, sbase + t / p.kv_block, p.kv_scale_f16) : 0.0f;
+      sc[j] = ok ? acc * sk * p.scale_log2 : -INFINITY;
+      mblk = fmaxf(mblk, sc[j]);
+    }
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) mblk = fmaxf(mblk, __shfl_xor(mblk, off));
+    m_run = mblk;  // first and only block of this wavefront
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      const int t = t_begin + j * TPS + tg;
+      const bool ok = t < t_end;
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) w = *(const uint4*)(vp + (long)t * p.c_row);
+      const float pr = ok ? exp2f(sc[j] - m_run) : 0.0f;
+      l_run += pr;
+      const float sv = ok ? load_scale(p.vs, sbase + t / p.kv_block, p.kv_scale_f16) : 0.0f;
+      const float wt = pr * sv;
+      wsum += wt;
+      float f[EPL];
+      chunk_to_f32<INT4>(w, f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = __builtin_fmaf(wt, f[e], o[e]);
+    }
+    // Sum the token groups: lanes with the same channel chunk.
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      l_run += __shfl_xor(l_run, off);
+      wsum += __shfl_xor(wsum, off);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], off);
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] -= kOff * wsum;
+  }
+
+  // Merge the wavefronts of the workgroup.
+  if (lane == 0) {
+    red_m[wave] = m_run;
+    red_l[wave] = l_run;
+  }
+  if (lane < LPT) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) red_o[wave][d0 + e] = o[e];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, red_m[w]);
+  float c[kDecWaves];
+  float Lsum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    c[w] = red_m[w] == -INFINITY ? 0.0f : exp2f(red_m[w] - M);
+    Lsum += red_l[w] * c[w];
+  }
+  const long obase = (long)b * p.q_batch + (long)h * p.q_head;
+  if (nsplit == 1) {
+    const float inv = 1.0f / Lsum;
+    for (int d = lane; d < D; d += 64) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) acc += red_o[w][d] * c[w];
+      store_out(p.out, obase + d, acc * inv, p.out_dtype);
+    }
+    return;
+  }
+  float* part = p.ws + (((long)b * p.Hq + h) * p.max_splits + split) * (D + 2);
+  for (int d = lane; d < D; d += 64) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) acc += red_o[w][d] * c[w];
+    part[d] = acc;
+  }
+  if (lane == 0) {
+    part[D] = M;
+    part[D + 1] = Lsum;
+  }
+}
+
+// Log-sum-exp merge of the chunk partials of one (batch, head) per wavefront.
+template <int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(DecParams p) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int L = min(max(p.lens[b], 1), p.S_max);
+  const int nsplit = (L + kDecodeChunk - 1) / kDecodeChunk;
+  if (nsplit <= 1) return;
+  const float* part = p.ws + ((long)b * p.Hq + h) * p.max_splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  float Lsum = 0.0f;
+  float acc[D / 64];
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) acc[i] = 0.0f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* ps = part + s * (D + 2);
+    const float ms = ps[D];
+    const float c = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    Lsum += ps[D + 1] * c;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) acc[i] += ps[threadIdx.x + 64 * i] * c;
+  }
+  const float inv = 1.0f / Lsum;
+  const long obase = (long)b * p.q_batch + (long)h * p.q_head;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) store_out(p.out, obase + threadIdx.x + 64 * i, acc[i] * inv, p.out_dtype);
+}
+
+template <int D, bool INT4>
+hipError_t launch_dec(const DecParams& p, int B, hipStream_t st) {
+  decode_split_kernel<D, INT4><<<dim3(p.max_splits, p.Hq, B), 64 * kDecWaves, 0, st>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.max_splits > 1) {
+    decode_reduce_kernel<D><<<dim3(p.Hq, B), 64, 0, st>>>(p);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int Hq, int S_max, int D) {
+  const long splits = (S_max + kDecodeChunk - 1) / kDecodeChunk;
+  return (size_t)B * Hq * splits * (D + 2) * sizeof(float);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  DecParams p;
+  p.q = a.q;
+  p.k = (const uint8_t*)a.k;
+  p.v = (const uint8_t*)a.v;
+  p.ks = a.ks;
+  p.vs = a.vs;
+  p.lens = a.lens;
+  p.out = a.out;
+  p.ws = (float*)a.workspace;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.group = a.Hq / a.Hkv;
+  p.S_max = a.S_max;
+  p.max_splits = (a.S_max + kDecodeChunk - 1) / kDecodeChunk;
+  const long rb = a.kv_qtype == QFA_INT4 ? a.D / 2 : a.D;
+  if (a.layout == QFA_BNSD) {
+    p.c_row = rb;
+    p.c_head = (long)a.S_max * rb;
+  } else {
+    p.c_row = (long)a.Hkv * rb;
+    p.c_head = rb;
+  }
+  p.c_batch = (long)a.Hkv * a.S_max * rb;
+  p.q_head = a.D;
+  p.q_batch = (long)a.Hq * a.D;
+  p.kv_block = a.kv_block;
+  p.nkblk = (a.S_max + a.kv_block - 1) / a.kv_block;
+  p.kv_scale_f16 = a.kv_scale_dtype == QFA_F16;
+  p.q_dtype = a.q_dtype;
+  p.out_dtype = a.out_dtype;
+  p.scale_log2 = a.softmax_scale * kLog2e;
+  const bool int4 = a.kv_qtype == QFA_INT4;
+  if (a.D == 64) return int4 ? launch_dec<64, true>(p, a.B, stream) : launch_dec<64, false>(p, a.B, stream);
+  return int4 ? launch_dec<128, true>(p, a.B, stream) : launch_dec<128, false>(p, a.B, stream);
+}
+
+}  // namespace qfa

@@ -1,0 +1,70 @@
+// Host-side launcher declarations shared by the C ABI (api.hip) and the kernel
+// translation units. Every launcher assumes its arguments were validated by
+// the C ABI and returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qfa.h"
+
+namespace qfa {
+
+struct QuantArgs {
+  const void* x;
+  int x_dtype;
+  int B, N, S, D;
+  int layout;
+  int block_rows;
+  int qtype;
+  void* codes;
+  void* scales;
+  int scale_dtype;
+};
+
+hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream);
+
+struct FwdArgs {
+  const void* q;
+  const void* qs;
+  int q_qtype, q_block, q_scale_dtype;
+  const void* k;
+  const void* ks;
+  int k_qtype;
+  const void* v;
+  const void* vs;
+  int v_qtype;
+  int kv_block, kv_scale_dtype;
+  int B, Hq, Hkv, Sq, Sk, D, layout, causal;
+  float softmax_scale;
+  void* out;
+  int out_dtype;
+};
+
+// Returns hipErrorInvalidValue for a combination without a compiled kernel.
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  int q_dtype;
+  int B, Hq, Hkv, D;
+  const void* k;
+  const void* v;
+  const void* ks;
+  const void* vs;
+  int kv_qtype, kv_block, kv_scale_dtype, S_max, layout;
+  const int32_t* lens;
+  float softmax_scale;
+  void* out;
+  int out_dtype;
+  void* workspace;
+};
+
+// Token chunk handled by one split of the decode kernel.
+constexpr int kDecodeChunk = 1024;
+
+size_t decode_workspace_bytes(int B, int Hq, int S_max, int D);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace qfa

@@ -1,0 +1,351 @@
+// Block quantizer: symmetric per-block amax scales and INT8 / FP8 e4m3fn /
+// packed INT4 codes.
+//
+// Arithmetic ([Ascend-INT8] section "对称量化 vs 非对称量化"; [MindIE-SD] FA
+// quantization, block-quant step; [OT-Quant] sections 5.1-5.2):
+//   amax = max |x| over R rows x D channels of one (batch, head)
+//   s    = fl32(amax / qmax), optionally rounded to fp16; codes use the stored s
+//   code = clamp(rne(fl32(x / s)))  (INT8 / INT4), e4m3fn(rne(clamp(x / s)))  (FP8)
+//
+// Design (HBM-bound: one read of x, one write of codes):
+//   * A team of T = 2^k threads (16..256) owns one block; each thread holds
+//     up to 16 chunks of 8 consecutive channels in registers, so x is read
+//     from HBM once. Larger blocks take a two-pass path (the second read
+//     mostly hits L2).
+//   * amax is reduced on the raw bit patterns (|x| ordered as an unsigned
+//     integer), across the team with lane shuffles and, for teams wider than
+//     a wavefront, through LDS.
+//   * The quotient fl32(x / s) is formed with a reciprocal r = 1/s (correctly
+//     rounded, once per block) and two FMA residual corrections. With r the
+//     nearest float to 1/s, the first correction makes the estimate faithful
+//     and the second makes it the correctly rounded quotient (Markstein's
+//     theorem on FMA-based division), provided the residuals do not
+//     underflow. That holds for s in [2^-60, 2^100] whenever the quotient can
+//     reach a nonzero code; other scales take the plain IEEE division.
+//   * FP8 codes use the gfx950 converter to OCP e4m3 (nearest-even) after
+//     clamping to +-448.
+#include "qfa_device.h"
+#include "qfa_launch.h"
+
+namespace qfa {
+namespace {
+
+struct QuantParams {
+  const char* x;
+  char* codes;
+  void* scales;
+  int N, S, D, R, nblk;
+  long x_row, x_head, x_batch;  // element strides of x
+  long c_row, c_head, c_batch;  // byte strides of codes
+  int scale_f16;
+  int team_log2;
+  int chunks;      // chunks of 8 channels per thread
+  int step_rows;   // (T*8) / D
+  int step_cols;   // (T*8) % D
+  long total_blocks;
+};
+
+template <int IN>
+struct In;
+template <>
+struct In<QFA_F32> {
+  static constexpr int kBytes = 4;
+  struct Raw { uint4 a, b; };
+  static __device__ __forceinline__ Raw load(const char* p) {
+    Raw r;
+    r.a = *(const uint4*)p;
+    r.b = *(const uint4*)(p + 16);
+    return r;
+  }
+  static __device__ __forceinline__ uint32_t absmax(const Raw& r) {
+    uint32_t m = max(r.a.x & 0x7FFFFFFFu, r.a.y & 0x7FFFFFFFu);
+    m = max(m, max(r.a.z & 0x7FFFFFFFu, r.a.w & 0x7FFFFFFFu));
+    m = max(m, max(r.b.x & 0x7FFFFFFFu, r.b.y & 0x7FFFFFFFu));
+    return max(m, max(r.b.z & 0x7FFFFFFFu, r.b.w & 0x7FFFFFFFu));
+  }
+  static __device__ __forceinline__ float amax_value(uint32_t bits) { return __uint_as_float(bits); }
+  static __device__ __forceinline__ void to_f32(const Raw& r, float* f) {
+    f[0] = __uint_as_float(r.a.x); f[1] = __uint_as_float(r.a.y);
+    f[2] = __uint_as_float(r.a.z); f[3] = __uint_as_float(r.a.w);
+    f[4] = __uint_as_float(r.b.x); f[5] = __uint_as_float(r.b.y);
+    f[6] = __uint_as_float(r.b.z); f[7] = __uint_as_float(r.b.w);
+  }
+};
+
+template <int IN>
+struct In16 {
+  static constexpr int kBytes = 2;
+  struct Raw { uint4 a; };
+  static __device__ __forceinline__ Raw load(const char* p) { return Raw{*(const uint4*)p}; }
+  static __device__ __forceinline__ uint32_t m2(uint32_t w) {
+    return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+  }
+  static __device__ __forceinline__ uint32_t absmax(const Raw& r) {
+    return max(max(m2(r.a.x), m2(r.a.y)), max(m2(r.a.z), m2(r.a.w)));
+  }
+  static __device__ __forceinline__ float cvt(uint32_t h) {
+    return IN == QFA_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+  }
+  static __device__ __forceinline__ float amax_value(uint32_t bits) { return cvt(bits); }
+  static __device__ __forceinline__ void to_f32(const Raw& r, float* f) {
+    const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = cvt(w[i] & 0xFFFFu);
+      f[2 * i + 1] = cvt(w[i] >> 16);
+    }
+  }
+};
+template <>
+struct In<QFA_F16> : In16<QFA_F16> {};
+template <>
+struct In<QFA_BF16> : In16<QFA_BF16> {};
+
+__device__ __forceinline__ float quotient(float x, float s, float r, bool fast) {
+  if (!fast) return x / s;
+  float q = x * r;
+  float e = __builtin_fmaf(-q, s, x);
+  q = __builtin_fmaf(e, r, q);
+  e = __builtin_fmaf(-q, s, x);
+  return __builtin_fmaf(e, r, q);
+}
+
+template <int QT>
+struct Enc;
+template <>
+struct Enc<QFA_INT8> {
+  static constexpr float kQmax = 127.0f;
+  static constexpr int kBytesPerChunk = 8;
+  static __device__ __forceinline__ uint2 encode(const float* t) {
+    uint32_t w[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float n = __builtin_amdgcn_fmed3f(__builtin_rintf(t[4 * j + i]), -128.0f, 127.0f);
+        acc |= ((uint32_t)(int)n & 0xFFu) << (8 * i);
+      }
+      w[j] = acc;
+    }
+    return make_uint2(w[0], w[1]);
+  }
+};
+template <>
+struct Enc<QFA_FP8_E4M3> {
+  static constexpr float kQmax = 448.0f;
+  static constexpr int kBytesPerChunk = 8;
+  static __device__ __forceinline__ uint2 encode(const float* t) {
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_fmed3f(t[i], -448.0f, 448.0f);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], w1, true);
+    return make_uint2((uint32_t)w0, (uint32_t)w1);
+  }
+};
+template <>
+struct Enc<QFA_INT4> {
+  static constexpr float kQmax = 7.0f;
+  static constexpr int kBytesPerChunk = 4;
+  static __device__ __forceinline__ uint32_t encode(const float* t) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float n = __builtin_amdgcn_fmed3f(__builtin_rintf(t[i]), -8.0f, 7.0f);
+      acc |= ((uint32_t)(int)n & 0xFu) << (4 * i);
+    }
+    return acc;
+  }
+};
+
+template <int QT>
+__device__ __forceinline__ void store_codes(char* p, const float* t, bool zero) {
+  if constexpr (QT == QFA_INT4) {
+    *(uint32_t*)p = zero ? 0u : Enc<QT>::encode(t);
+  } else {
+    *(uint2*)p = zero ? make_uint2(0u, 0u) : Enc<QT>::encode(t);
+  }
+}
+
+// Team-wide max of an unsigned value. Teams wider than a wavefront go through
+// LDS; every thread of the workgroup must call this (it may hold a barrier).
+__device__ __forceinline__ uint32_t team_max(uint32_t m, int team_log2, uint32_t* lds) {
+  const int T = 1 << team_log2;
+  const int width = T < 64 ? T : 64;
+  for (int off = width >> 1; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if (T <= 64) return m;
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wave] = m;
+  __syncthreads();
+  const int waves_per_team = T >> 6;
+  const int first = (wave / waves_per_team) * waves_per_team;
+  uint32_t r = 0;
+  for (int w = 0; w < waves_per_team; ++w) r = max(r, lds[first + w]);
+  return r;
+}
+
+template <int IN, int QT, int CH, bool TWO_PASS>
+__global__ __launch_bounds__(256) void block_quant_kernel(QuantParams p) {
+  using I = In<IN>;
+  using E = Enc<QT>;
+  __shared__ uint32_t lds[4];
+  const int T = 1 << p.team_log2;
+  const int team = threadIdx.x >> p.team_log2;
+  const int lt = threadIdx.x & (T - 1);
+  const long gb = (long)blockIdx.x * (256 >> p.team_log2) + team;
+  const bool active = gb < p.total_blocks;
+  const long g = active ? gb : 0;
+  const int r = (int)(g % p.nblk);
+  const long bn = g / p.nblk;
+  const int n = (int)(bn % p.N);
+  const int b = (int)(bn / p.N);
+  const int row0 = r * p.R;
+  const int rows = active ? min(p.R, p.S - row0) : 0;
+  const char* xb = p.x + ((long)b * p.x_batch + (long)n * p.x_head + (long)row0 * p.x_row) * I::kBytes;
+  char* cb = p.codes + (long)b * p.c_batch + (long)n * p.c_head + (long)row0 * p.c_row;
+  const int code_div = QT == QFA_INT4 ? 2 : 1;
+
+  // Chunk k of this thread covers channels [d, d+8) of block row `row`.
+  int row0_t = (lt * 8) / p.D;
+  int col0_t = (lt * 8) - row0_t * p.D;
+
+  uint32_t amax_bits = 0;
+  typename I::Raw raw[TWO_PASS ? 1 : CH];
+  if constexpr (!TWO_PASS) {
+    int row = row0_t, col = col0_t;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      if (k < p.chunks && row < rows) {
+        raw[k] = I::load(xb + ((long)row * p.x_row + col) * I::kBytes);
+        amax_bits = max(amax_bits, I::absmax(raw[k]));
+      }
+      row += p.step_rows;
+      col += p.step_cols;
+      if (col >= p.D) { col -= p.D; ++row; }
+    }
+  } else {
+    int row = row0_t, col = col0_t;
+    for (int k = 0; k < p.chunks && row < rows; ++k) {
+      amax_bits = max(amax_bits, I::absmax(I::load(xb + ((long)row * p.x_row + col) * I::kBytes)));
+      row += p.step_rows;
+      col += p.step_cols;
+      if (col >= p.D) { col -= p.D; ++row; }
+    }
+  }
+  amax_bits = team_max(amax_bits, p.team_log2, lds);
+  if (!active) return;
+
+  const float amax = I::amax_value(amax_bits);
+  float s = amax / E::kQmax;
+  if (p.scale_f16) s = (float)(_Float16)s;
+  if (lt == 0) {
+    const long si = ((long)b * p.N + n) * p.nblk + r;
+    if (p.scale_f16) ((uint16_t*)p.scales)[si] = (uint16_t)f32_to_f16_bits(s);
+    else ((float*)p.scales)[si] = s;
+  }
+  const bool zero = !(s != 0.0f);
+  const bool fast = s >= 0x1p-60f && s <= 0x1p100f;
+  const float rcp = fast ? 1.0f / s : 0.0f;
+
+  if constexpr (!TWO_PASS) {
+    int row = row0_t, col = col0_t;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      if (k < p.chunks && row < rows) {
+        float f[8], t[8];
+        I::to_f32(raw[k], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = quotient(f[i], s, rcp, fast);
+        store_codes<QT>(cb + (long)row * p.c_row + col / code_div, t, zero);
+      }
+      row += p.step_rows;
+      col += p.step_cols;
+      if (col >= p.D) { col -= p.D; ++row; }
+    }
+  } else {
+    int row = row0_t, col = col0_t;
+    for (int k = 0; k < p.chunks && row < rows; ++k) {
+      float f[8], t[8];
+      I::to_f32(I::load(xb + ((long)row * p.x_row + col) * I::kBytes), f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = quotient(f[i], s, rcp, fast);
+      store_codes<QT>(cb + (long)row * p.c_row + col / code_div, t, zero);
+      row += p.step_rows;
+      col += p.step_cols;
+      if (col >= p.D) { col -= p.D; ++row; }
+    }
+  }
+}
+
+template <int IN, int QT>
+hipError_t launch_typed(const QuantParams& p, long grid, hipStream_t stream) {
+  const int ch = p.chunks;
+  if (ch <= 1) block_quant_kernel<IN, QT, 1, false><<<grid, 256, 0, stream>>>(p);
+  else if (ch <= 2) block_quant_kernel<IN, QT, 2, false><<<grid, 256, 0, stream>>>(p);
+  else if (ch <= 4) block_quant_kernel<IN, QT, 4, false><<<grid, 256, 0, stream>>>(p);
+  else if (ch <= 8) block_quant_kernel<IN, QT, 8, false><<<grid, 256, 0, stream>>>(p);
+  else if (ch <= 16) block_quant_kernel<IN, QT, 16, false><<<grid, 256, 0, stream>>>(p);
+  else block_quant_kernel<IN, QT, 1, true><<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int IN>
+hipError_t launch_in(const QuantParams& p, int qtype, long grid, hipStream_t stream) {
+  switch (qtype) {
+    case QFA_INT8: return launch_typed<IN, QFA_INT8>(p, grid, stream);
+    case QFA_FP8_E4M3: return launch_typed<IN, QFA_FP8_E4M3>(p, grid, stream);
+    default: return launch_typed<IN, QFA_INT4>(p, grid, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream) {
+  QuantParams p;
+  p.x = (const char*)a.x;
+  p.codes = (char*)a.codes;
+  p.scales = a.scales;
+  p.N = a.N;
+  p.S = a.S;
+  p.D = a.D;
+  p.R = a.block_rows;
+  p.nblk = (a.S + a.block_rows - 1) / a.block_rows;
+  const long cD = a.qtype == QFA_INT4 ? a.D / 2 : a.D;
+  if (a.layout == QFA_BNSD) {
+    p.x_row = a.D;
+    p.x_head = (long)a.S * a.D;
+    p.c_row = cD;
+    p.c_head = (long)a.S * cD;
+  } else {
+    p.x_row = (long)a.N * a.D;
+    p.x_head = a.D;
+    p.c_row = (long)a.N * cD;
+    p.c_head = cD;
+  }
+  p.x_batch = (long)a.N * a.S * a.D;
+  p.c_batch = (long)a.N * a.S * cD;
+  p.scale_f16 = a.scale_dtype == QFA_F16;
+  // Team size: enough threads that each holds at most 16 chunks, capped at 256.
+  const long chunks_total = ((long)p.R * a.D) / 8;
+  int tl = 0;
+  while ((1L << tl) < chunks_total && tl < 8) ++tl;
+  p.team_log2 = tl;
+  const long T = 1L << tl;
+  p.chunks = (int)((chunks_total + T - 1) / T);
+  p.step_rows = (int)((T * 8) / a.D);
+  p.step_cols = (int)((T * 8) % a.D);
+  p.total_blocks = (long)a.B * a.N * p.nblk;
+  const long teams_per_wg = 256 / T;
+  const long grid = (p.total_blocks + teams_per_wg - 1) / teams_per_wg;
+  if (grid == 0) return hipSuccess;
+  switch (a.x_dtype) {
+    case QFA_F32: return launch_in<QFA_F32>(p, a.qtype, grid, stream);
+    case QFA_F16: return launch_in<QFA_F16>(p, a.qtype, grid, stream);
+    default: return launch_in<QFA_BF16>(p, a.qtype, grid, stream);
+  }
+}
+
+}  // namespace qfa

@@ -1,0 +1,162 @@
+/*
+ * qfa.h -- C ABI of libqfa.so: block-quantized FlashAttention on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Pages cited (titles shortened):
+ *   [FA-INT8/INT4]  "FlashAttention INT8/INT4 quantization" blog post on the
+ *                   ops-transformer library (hwcomputing.csdn.net/6a140ce2...).
+ *   [OT-Quant]      ops-transformer INT8/INT4 quantized-inference article
+ *                   (2048ai.net/6989721354...).
+ *   [Ascend-INT8]   "INT8 量化算子：让大模型在昇腾NPU上减肥不掉肉"
+ *                   (hwcomputing.csdn.net/6a0dcc10...).
+ *   [MindIE-SD]     MindIE-SD quantization feature doc, FA quantization part
+ *                   (gitcode.com/Ascend/MindIE-SD, docs/zh/features/quantization.md).
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never frees or keeps them; it allocates no device memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *     default stream). Arguments are validated on the host before any launch;
+ *     an invalid call returns a nonzero status and launches nothing.
+ *   - A kernel-launch failure returns QFA_ERR_HIP. Faults inside a kernel
+ *     surface at the caller's next synchronisation with the stream.
+ *   - Enumerations are passed as int. Sizes are elements unless stated.
+ *   - Layouts: QFA_BNSD is [batch, heads, seq, dim]; QFA_BSND is
+ *     [batch, seq, heads, dim]; both dense, dim fastest. INT4 codes hold two
+ *     codes per byte, so their innermost extent is dim/2 bytes.
+ *   - A "block" is `block_rows` consecutive sequence rows times all `dim`
+ *     channels of one (batch, head); the last block of a sequence may be short.
+ *   - The library holds no mutable global state; calls are reentrant.
+ */
+#ifndef QFA_H
+#define QFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef QFA_API
+#define QFA_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  QFA_OK = 0,
+  QFA_ERR_NULL = 1,         /* a required pointer is NULL */
+  QFA_ERR_SHAPE = 2,        /* a size is out of range or inconsistent */
+  QFA_ERR_ENUM = 3,         /* an enumeration value is unknown */
+  QFA_ERR_UNSUPPORTED = 4,  /* a valid combination this build does not implement */
+  QFA_ERR_WORKSPACE = 5,    /* decode workspace missing or too small */
+  QFA_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
+} qfa_status;
+
+typedef enum { QFA_F32 = 0, QFA_F16 = 1, QFA_BF16 = 2 } qfa_float;
+typedef enum { QFA_INT8 = 0, QFA_FP8_E4M3 = 1, QFA_INT4 = 2 } qfa_qtype;
+typedef enum { QFA_BNSD = 0, QFA_BSND = 1 } qfa_layout;
+
+/* Library version as 10000*major + 100*minor + patch. */
+QFA_API int qfa_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+QFA_API const char* qfa_status_string(int status);
+
+/*
+ * qfa_block_quant -- symmetric per-block amax quantization.
+ *
+ * Defined by [Ascend-INT8] section "对称量化 vs 非对称量化" (scale =
+ * max(abs(x))/127, code = round(x/scale) clamped to [-128, 127], zero point
+ * 0), [MindIE-SD] FA quantization "块量化" (dynamic block quantization to
+ * float8_e4m3fn, Q block 128 rows, K/V block 256 rows) and [OT-Quant]
+ * sections 5.1-5.2 (INT4 groups with one FP16 scale, two codes per byte,
+ * element 2k in the low nibble).
+ *
+ * For each block: amax = max|x| (x upcast to fp32), s = fl32(amax / qmax) with
+ * qmax = 127 (INT8), 448 (FP8 e4m3fn), 7 (INT4); if scale_dtype is QFA_F16, s
+ * is rounded to fp16 (nearest-even) and the codes use that rounded value.
+ * t = fl32(x / s) (correctly rounded), then
+ *   INT8: clamp(rne(t), -128, 127);  INT4: clamp(rne(t), -8, 7), packed;
+ *   FP8 : OCP e4m3fn of clamp(t, -448, 448), nearest-even, sign kept.
+ * A block whose stored scale is 0 gets all-zero codes.
+ *
+ *   x          [B,N,S,D] or [B,S,N,D] (layout), dtype x_dtype (F32/F16/BF16).
+ *   codes      same layout; int8 / e4m3 bytes: D bytes per row; INT4: D/2.
+ *   scales     [B, N, ceil(S/block_rows)] of scale_dtype (F32 or F16).
+ * Limits: B,N,S >= 0 (an empty tensor launches nothing); 8 <= D <= 1024 and
+ * D % 8 == 0; block_rows >= 1. Inputs must be finite.
+ */
+QFA_API int qfa_block_quant(const void* x, int x_dtype, int B, int N, int S, int D, int layout,
+                    int block_rows, int qtype, void* codes, void* scales, int scale_dtype,
+                    void* stream);
+
+/*
+ * qfa_fwd -- prefill attention forward run on block-quantized codes.
+ *
+ * Computes, for query row i of head h and key row j of KV head
+ * h / (Hq/Hkv) (grouped-query attention),
+ *     x_ij = softmax_scale * (sq_i * q_i) . (sk_j * k_j)
+ *     o_i  = sum_j softmax_j(x_ij) * (sv_j * v_j)
+ * with j <= i kept when `causal` (Sq == Sk required), where q, k, v are the
+ * codes and sq, sk, sv their block scales: the low-bit products are formed
+ * directly on the codes with wide accumulation and the scales are applied to
+ * the products ([Ascend-INT8] INT8-operator section 1: INT8 x INT8 -> INT32,
+ * one conversion at the output; section 2: scales kept on chip), then online
+ * softmax and P.V ([MindIE-SD] FA quantization, "FP8 Attention": the
+ * attention runs on FP8 codes and the output returns to the original
+ * precision; [FA-INT8/INT4] INT8 and INT4 layers, with INT4 widened to INT8
+ * before the product).
+ *
+ *   q_codes    [B,Hq,Sq,D] (layout), q_qtype INT8 or FP8_E4M3.
+ *   q_scales   [B,Hq,ceil(Sq/q_block)], q_scale_dtype F32/F16.
+ *   k_codes    [B,Hkv,Sk,D or D/2], k_qtype: INT8 or INT4 with INT8 Q; FP8 with FP8 Q.
+ *   v_codes    [B,Hkv,Sk,D or D/2], v_qtype INT8, INT4 or FP8_E4M3 (any Q/K type).
+ *   k_scales, v_scales [B,Hkv,ceil(Sk/kv_block)], kv_scale_dtype F32/F16.
+ *   out        [B,Hq,Sq,D] (same layout as q), out_dtype F32/F16/BF16.
+ * Limits: D in {64, 128}; Hq % Hkv == 0; Sk >= 1 when Sq >= 1; q_block and
+ * kv_block >= 1; finite scales. Sq == 0 returns QFA_OK without a launch.
+ */
+QFA_API int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
+            int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
+            const void* v_codes, const void* v_scales, int v_qtype, int kv_block,
+            int kv_scale_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int layout,
+            int causal, float softmax_scale, void* out, int out_dtype, void* stream);
+
+/*
+ * qfa_decode_workspace_bytes -- bytes of device workspace qfa_decode needs for
+ * these sizes (split-K partial results). Returns 0 for invalid sizes.
+ */
+QFA_API size_t qfa_decode_workspace_bytes(int B, int Hq, int S_max, int D);
+
+/*
+ * qfa_decode -- one query token per sequence against a quantized KV cache.
+ *
+ * The cache holds K/V as INT8 (or INT4) codes with block scales, and attention
+ * is computed on the codes without writing a dequantized cache
+ * ([Ascend-INT8] INT8-operator section 3, KV cache quantized to INT8 for
+ * decode, attention computed directly on INT8; [FA-INT8/INT4] INT4 layer for
+ * the INT4 codes). The query is used unquantized.
+ *     o_bh = sum_{j < seq_lens[b]} softmax_j(softmax_scale * q_bh . (sk_j k_j)) * (sv_j v_j)
+ *
+ *   q          [B,Hq,1,D] (BNSD; for BSND the same bytes as [B,1,Hq,D]), q_dtype F16/BF16/F32.
+ *   k_cache, v_cache [B,Hkv,S_max,D or D/2] (layout), kv_qtype INT8 or INT4.
+ *   k_scales, v_scales [B,Hkv,ceil(S_max/kv_block)], kv_scale_dtype F16/F32.
+ *   seq_lens   device int32 [B], each in [1, S_max] (values outside are clamped
+ *              to that range by the kernel).
+ *   out        [B,Hq,1,D], out_dtype F16/BF16/F32.
+ *   workspace  device buffer of at least qfa_decode_workspace_bytes(B,Hq,S_max,D)
+ *              bytes; its contents on entry do not matter. Calls that share a
+ *              workspace must be ordered on one stream.
+ * Limits: D in {64, 128}; Hq % Hkv == 0; 1 <= Hq/Hkv <= 16.
+ */
+QFA_API int qfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D, const void* k_cache,
+               const void* v_cache, const void* k_scales, const void* v_scales, int kv_qtype,
+               int kv_block, int kv_scale_dtype, int S_max, int layout, const int32_t* seq_lens,
+               float softmax_scale, void* out, int out_dtype, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QFA_H */

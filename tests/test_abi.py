@@ -1,0 +1,110 @@
+"""The C ABI: the library loads, exports every function the header declares,
+and rejects invalid calls with the documented status before touching the
+device. CPU only: every call here returns during host-side validation."""
+import ctypes
+
+import pytest
+
+import block_quantized_flashattention_amd as qfa
+
+OK, NULL, SHAPE, ENUM, UNSUP, WS = 0, 1, 2, 3, 4, 5
+I8, F8, I4 = 0, 1, 2
+F32, F16, BF16 = 0, 1, 2
+BNSD, BSND = 0, 1
+P = ctypes.c_void_p(256)  # a non-null, 256-byte-aligned stand-in never dereferenced
+MIS = ctypes.c_void_p(258)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qfa.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = qfa.header_functions()
+    assert set(names) == {"qfa_version", "qfa_status_string", "qfa_block_quant", "qfa_fwd",
+                          "qfa_decode_workspace_bytes", "qfa_decode"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.qfa_status_string(s)
+    assert L.qfa_status_string(99) == b"unknown status"
+    assert L.qfa_version() >= 100
+
+
+def quant(L, x=P, dt=F16, B=1, N=2, S=300, D=128, layout=BNSD, R=128, qt=I8, codes=P, scales=P,
+          sdt=F32):
+    return L.qfa_block_quant(x, dt, B, N, S, D, layout, R, qt, codes, scales, sdt, None)
+
+
+def test_block_quant_validation(L):
+    assert quant(L, dt=7) == ENUM
+    assert quant(L, layout=2) == ENUM
+    assert quant(L, qt=3) == ENUM
+    assert quant(L, sdt=BF16) == ENUM
+    assert quant(L, D=12) == SHAPE
+    assert quant(L, D=0) == SHAPE
+    assert quant(L, D=2048) == SHAPE
+    assert quant(L, R=0) == SHAPE
+    assert quant(L, B=-1) == SHAPE
+    assert quant(L, x=None) == NULL
+    assert quant(L, scales=None) == NULL
+    assert quant(L, x=MIS) == UNSUP
+    # empty tensors are valid and launch nothing, even with null pointers
+    assert quant(L, S=0, x=None, codes=None, scales=None) == OK
+    assert quant(L, B=0, x=None, codes=None, scales=None) == OK
+
+
+def fwd(L, q=P, qs=P, qqt=I8, qb=128, qsd=F32, k=P, ks=P, kqt=I8, v=P, vs=P, vqt=I8, kb=256,
+        ksd=F32, B=1, Hq=4, Hkv=2, Sq=100, Sk=100, D=128, layout=BNSD, causal=1, scale=0.1,
+        out=P, odt=F16):
+    return L.qfa_fwd(q, qs, qqt, qb, qsd, k, ks, kqt, v, vs, vqt, kb, ksd, B, Hq, Hkv, Sq, Sk, D,
+                     layout, causal, ctypes.c_float(scale), out, odt, None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, qqt=5) == ENUM
+    assert fwd(L, odt=4) == ENUM
+    assert fwd(L, qsd=BF16) == ENUM
+    assert fwd(L, Hq=3, Hkv=2) == SHAPE
+    assert fwd(L, Hkv=0) == SHAPE
+    assert fwd(L, qb=0) == SHAPE
+    assert fwd(L, causal=2) == SHAPE
+    assert fwd(L, D=96) == UNSUP
+    assert fwd(L, Sq=10, Sk=20, causal=1) == UNSUP
+    assert fwd(L, Sq=10, Sk=0, causal=0) == SHAPE
+    assert fwd(L, scale=float("nan")) == SHAPE
+    assert fwd(L, qqt=F8) == UNSUP             # fp8 Q with int8 K
+    assert fwd(L, qqt=I4) == UNSUP             # int4 Q
+    assert fwd(L, kqt=I4, qqt=F8) == UNSUP
+    assert fwd(L, out=None) == NULL
+    assert fwd(L, v=None) == NULL
+    assert fwd(L, q=MIS) == UNSUP
+    assert fwd(L, Sq=0, Sk=0, q=None, k=None, v=None, out=None) == OK
+
+
+def dec(L, q=P, qdt=F16, B=2, Hq=4, Hkv=2, D=128, k=P, v=P, ks=P, vs=P, qt=I8, kb=256, sdt=F16,
+        S_max=4096, layout=BNSD, lens=P, scale=0.1, out=P, odt=F16, ws=P, wsb=1 << 20):
+    return L.qfa_decode(q, qdt, B, Hq, Hkv, D, k, v, ks, vs, qt, kb, sdt, S_max, layout, lens,
+                        ctypes.c_float(scale), out, odt, ws, wsb, None)
+
+
+def test_decode_validation(L):
+    need = L.qfa_decode_workspace_bytes(2, 4, 4096, 128)
+    assert need == 2 * 4 * 4 * 130 * 4
+    assert L.qfa_decode_workspace_bytes(2, 4, 4096, 96) == 0
+    assert dec(L, qdt=9) == ENUM
+    assert dec(L, qt=7) == ENUM
+    assert dec(L, Hq=5) == SHAPE
+    assert dec(L, S_max=0) == SHAPE
+    assert dec(L, D=32) == UNSUP
+    assert dec(L, qt=F8) == UNSUP
+    assert dec(L, Hq=64, Hkv=2) == UNSUP
+    assert dec(L, lens=None) == NULL
+    assert dec(L, ws=None) == WS
+    assert dec(L, wsb=need - 1) == WS
+    assert dec(L, k=MIS, wsb=need) == UNSUP
+    assert dec(L, B=0, q=None, k=None, v=None) == OK

@@ -1,0 +1,88 @@
+"""GPU parity of qfa_decode (split-K over the KV cache plus the merge) against
+the oracle's float64 decode attention on the same cache codes."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_flashattention_amd as qfa
+import oracle
+import qfa_workloads as wl
+from gpu_util import SDT, assert_close, quantize_both, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w: wl.DecodeWorkload, q, k, v, lens, layout="bnsd", sample=None):
+    say(f"decode case {w.name} B={q.shape[0]} Hq={w.Hq} Hkv={w.Hkv} S_max={k.shape[2]} "
+        f"D={w.D} kv={w.kv_qtype} R={w.kv_block} lens={lens.tolist()[:6]}")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    B, S_max = q.shape[0], k.shape[2]
+    if layout == "bsnd":
+        kd, vd = kd.transpose(1, 2).contiguous(), vd.transpose(1, 2).contiguous()
+    heads = None if sample is None else sorted({h for _, h in sample})
+    kc, ks = quantize_both(kd, w.kv_block, w.kv_qtype, w.kv_scale_dtype, layout, "K cache", heads)
+    vc, vs = quantize_both(vd, w.kv_block, w.kv_qtype, w.kv_scale_dtype, layout, "V cache", heads)
+    out = qfa.decode(qd, kc, vc, ks, vs, lens.cuda(), kv_qtype=w.kv_qtype, kv_block=w.kv_block,
+                     softmax_scale=w.softmax_scale, layout=layout,
+                     out_dtype=wl.torch_dtype(w.out_dtype))
+    torch.cuda.synchronize()
+    pairs = sample or [(b, h) for b in range(B) for h in range(w.Hkv)]
+    group = w.Hq // w.Hkv
+    got, ref = [], []
+    for b, kvh in pairs:
+        L = int(lens[b])
+        sl = (slice(b, b + 1), slice(kvh, kvh + 1), slice(0, L))
+        if layout == "bnsd":
+            kcs, vcs = kc[sl].cpu().numpy(), vc[sl].cpu().numpy()
+        else:
+            kcs = kc[b:b + 1, :L, kvh:kvh + 1].cpu().numpy()
+            vcs = vc[b:b + 1, :L, kvh:kvh + 1].cpu().numpy()
+        kss, vss = ks[b:b + 1, kvh:kvh + 1].cpu().numpy(), vs[b:b + 1, kvh:kvh + 1].cpu().numpy()
+        nb = -(-L // w.kv_block)
+        kh = oracle.dequantize(kcs, kss[..., :nb], w.kv_block, w.kv_qtype, layout)
+        vh = oracle.dequantize(vcs, vss[..., :nb], w.kv_block, w.kv_qtype, layout)
+        qs = q[b:b + 1, kvh * group:(kvh + 1) * group].double().numpy()
+        ref.append(oracle.decode(qs, kh, vh, [L], w.softmax_scale))
+        got.append(out[b:b + 1, kvh * group:(kvh + 1) * group].double().cpu().numpy())
+    assert_close(np.concatenate(got), np.concatenate(ref), f"{w.name} decode")
+    return out
+
+
+SMALL = [
+    # name, B, Hq, Hkv, D, S_max, lens, kv qtype, kv_block, scale dtype
+    ("i8_gqa2", 3, 4, 2, 128, 3000, [1, 1024, 2999], "int8", 256, "f16"),
+    ("i8_splits", 2, 2, 2, 128, 4100, [1025, 4100], "int8", 256, "f16"),
+    ("i8_d64_f32s", 2, 3, 3, 64, 700, [700, 17], "int8", 64, "f32"),
+    ("i4_tok", 2, 8, 2, 128, 2500, [2500, 300], "int4", 1, "f16"),
+    ("i4_blk", 2, 2, 1, 128, 1500, [1200, 1500], "int4", 256, "f16"),
+    ("i4_d64", 1, 4, 4, 64, 2100, [2049], "int4", 128, "f32"),
+    ("i8_gqa16", 1, 16, 1, 128, 2000, [1999], "int8", 256, "f16"),
+]
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,S_max,lens,qt,R,sdt", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("layout", ["bnsd", "bsnd"])
+def test_small_decode(name, B, Hq, Hkv, D, S_max, lens, qt, R, sdt, layout):
+    w = wl.DecodeWorkload(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, S_max=S_max, len_lo=S_max,
+                          len_hi=S_max, seed=40 + B + Hq, kv_qtype=qt, kv_block=R,
+                          kv_scale_dtype=sdt, q_dtype="f16", out_dtype="f16",
+                          softmax_scale=float(np.float32(1 / np.sqrt(D))))
+    q, k, v, _ = wl.make_decode_inputs(w)
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    for b, L in enumerate(lens):   # rows past the length are zero in the sources
+        k[b, :, L:] = 0
+        v[b, :, L:] = 0
+    _run(w, q, k, v, lens_t, layout=layout)
+
+
+def test_full_size_decode_sampled():
+    """The full decode workload (B=32, 32 heads, S_max=8192, L in [4096, 8192]),
+    inputs drawn on the GPU; 24 (batch, head) pairs compared with the oracle."""
+    w = wl.DECODE
+    say("full-size decode: generating inputs on the GPU")
+    q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
+    rng = np.random.default_rng(7)
+    sample = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 24), rng.integers(0, w.Hkv, 24))]
+    sample[0] = (int(torch.argmax(lens)), 0)
+    sample[1] = (int(torch.argmin(lens)), w.Hkv - 1)
+    _run(w, q.cpu(), k, v, lens.cpu(), sample=sample)
