@@ -6,29 +6,41 @@
 //   o_i  = sum_j softmax_j(x_ij) * sv_j * Vc_j             online softmax, P.V on MFMA
 //
 // Design:
-//   * A workgroup owns 32*NW query rows of one (batch, head); each wavefront
-//     owns 32 rows. Key tiles of BLOCK_N rows stream through LDS.
+//   * A workgroup of 4 wavefronts owns 128 query rows of one (batch, head);
+//     each wavefront owns 32 rows. Two workgroups share a CU (at most 256
+//     registers per lane), so one's softmax arithmetic overlaps the other's
+//     matrix work. Key tiles of 64 rows are double-buffered in LDS: the next
+//     tile's codes are fetched into registers while the current one is
+//     computed, then written to the free buffer; one barrier per tile.
 //   * Scores are formed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_32x32x32_i8 (INT8 Q/K; INT4 K is widened to INT8 while it is
 //     staged) or v_mfma_f32_32x32x64_f8f6f4 (FP8 e4m3 Q/K). In the MFMA result
-//     layout each lane then holds one query row and 16 of the 32 keys, so
+//     layout each lane then holds one query row and 16 of every 32 keys, so
 //     row max and row sum are register reductions plus one exchange between
-//     the two lane halves, and the probabilities are already in the register
-//     layout of the B operand of the P.V product (O^T = V^T . P^T) on
-//     v_mfma_f32_32x32x16_f16: P never goes through LDS.
-//   * V is staged into LDS transposed ([d][key], fp16), its codes converted
-//     once per workgroup (INT8, INT4 and e4m3 values are exact in fp16).
-//     Keys are permuted inside each group of 16 so that every lane reads its
-//     A-operand slice with one 16-byte LDS read.
-//   * Scale fold: one multiply per score by sq_i * sk_j * softmax_scale *
-//     log2(e); scores then go through exp2. sv_j multiplies the probability
-//     before its fp16 rounding; the row sum uses the unscaled probability.
+//     the lane halves, and the probabilities are already in the register
+//     layout of the B operand of O^T += V^T . P^T on v_mfma_f32_32x32x16_f16:
+//     P never goes through LDS.
+//   * V is staged transposed ([channel][key], fp16): INT8, INT4 and e4m3 codes
+//     are exact in fp16 and are converted once per workgroup. Keys are
+//     permuted inside each group of 16 so that every lane reads its operand
+//     slice with one 16-byte LDS read.
+//   * Scale fold: with one K scale per tile, the row max is taken on the
+//     integer dot products and each probability costs one FMA and one exp2:
+//     p = exp2(dot * (sq * sk * softmax_scale * log2 e) - m). The V block
+//     scale is folded into the accumulator (O is kept in units of the current
+//     V scale and rescaled when it changes). With per-token scales (INT4 K/V)
+//     each score and probability takes one more multiply.
 //   * The running row max is only raised when a tile's max exceeds it by more
-//     than 8 (in log2 units), so the O rescale is skipped on most tiles; the
-//     probabilities stay below 2^8 and the result is unchanged.
-//   * Causal: key tiles past the workgroup's last row are skipped; the mask is
-//     applied per element only on tiles that cross the diagonal. Workgroups
-//     with the most tiles are launched first.
+//     than 8 (log2 units), so the O rescale is skipped on most tiles; the
+//     probabilities stay below 2^8 (exact softmax, fp16-safe).
+//   * Row sums add the fp16-rounded probabilities with v_dot2_f32_f16, i.e.
+//     exactly the weights the P.V product uses.
+//   * Causal: tiles past a workgroup's last row are skipped, wavefronts skip
+//     tiles entirely above their rows, and the mask is applied per element
+//     only on tiles crossing the diagonal. Work is ordered longest first.
+//   * XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
+//     all query heads and row blocks of one (batch, KV head) are given ids on
+//     the same XCD and its K/V codes stay in that XCD's L2.
 #include "qfa_device.h"
 #include "qfa_launch.h"
 
@@ -36,8 +48,10 @@ namespace qfa {
 namespace {
 
 constexpr int kNW = 4;            // wavefronts per workgroup
+constexpr int kThreads = 64 * kNW;
 constexpr int kBM = 32 * kNW;     // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
+constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.0f;
 
 struct FwdParams {
@@ -48,7 +62,7 @@ struct FwdParams {
   const uint8_t* v;
   const void* vs;
   void* out;
-  int Hq, Hkv, Sq, Sk, group;
+  int B, Hq, Hkv, Sq, Sk, group;
   long q_row, q_head, q_batch;  // byte strides of Q codes
   long k_row, k_head, k_batch;  // byte strides of K codes
   long v_row, v_head, v_batch;  // byte strides of V codes
@@ -58,12 +72,13 @@ struct FwdParams {
   int k_qtype, v_qtype, out_dtype;
   float scale_log2;  // softmax_scale * log2(e)
   int n_mblocks;
+  int xcd_order;     // 1: XCD-grouped workgroup order
 };
 
 template <int D>
-struct Smem {
-  static constexpr int kKStride = D + 16;         // bytes per staged K row
-  static constexpr int kVStride = kBN + 8;        // fp16 elements per staged V^T row
+struct Stage {
+  static constexpr int kKStride = D + 16;   // bytes per staged K row
+  static constexpr int kVStride = kBN + 8;  // fp16 elements per staged V^T row
   uint8_t k[kBN * kKStride];
   _Float16 vt[D * kVStride];
   float ksc[kBN];
@@ -77,108 +92,137 @@ __device__ __forceinline__ int vt_pos(int key) {
   return g * 16 + ((((a & 1) << 1) | (a >> 1)) << 2) + i;
 }
 
-// Sign-extend eight packed two's-complement nibbles of `w` (element 2k low)
-// into eight int8 bytes returned as two dwords.
+// Sign-extend eight packed two's-complement nibbles of `w` (element 2k in the
+// low nibble of byte k) into eight int8 bytes, returned as two dwords.
 __device__ __forceinline__ uint2 unpack_int4x8(uint32_t w) {
   uint32_t lo = w & 0x0F0F0F0Fu;         // elements 0,2,4,6
   uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // elements 1,3,5,7
   lo |= (lo & 0x08080808u) * 0x1Eu;      // copy bit 3 into bits 4..7
   hi |= (hi & 0x08080808u) * 0x1Eu;
-  // interleave: out0 = [lo.b0, hi.b0, lo.b1, hi.b1], out1 = [lo.b2, hi.b2, lo.b3, hi.b3]
   const uint32_t o0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
   const uint32_t o1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
   return make_uint2(o0, o1);
 }
 
-__device__ __forceinline__ _Float16 i8_to_h(uint32_t byte) {
-  return (_Float16)(float)(int8_t)(uint8_t)byte;
+// Four signed bytes of `w` as two packed fp16 pairs (exact): the byte is
+// placed in the mantissa of 1024 + (byte ^ 0x80) and 1152 is subtracted.
+__device__ __forceinline__ void i8x4_to_h(uint32_t w, f16x2& lo, f16x2& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);  // bytes 0,1
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u);  // bytes 2,3
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = __builtin_bit_cast(f16x2, a) - bias;
+  hi = __builtin_bit_cast(f16x2, b) - bias;
 }
 
-// Stage one K tile (codes as bytes; INT4 widened to INT8) into LDS.
+// Registers holding one prefetched tile of K and V codes for this thread.
+struct Prefetch {
+  uint4 k[2];
+  uint2 v[4];
+  float ks, vs;
+};
+
 template <int D>
-__device__ __forceinline__ void stage_k(Smem<D>& sm, const FwdParams& p, const uint8_t* kbase,
-                                        int n0) {
+__device__ __forceinline__ void fetch_tile(Prefetch& f, const FwdParams& p, const uint8_t* kbase,
+                                           const uint8_t* vbase, long sbase, int n0) {
   const int tid = threadIdx.x;
-  if (p.k_qtype == QFA_INT4) {
-    constexpr int kChunks = kBN * D / 16;  // 16 codes (8 bytes) per chunk
+  // K: 16-byte chunks of codes (8-byte chunks of packed INT4).
+  constexpr int kChunks = kBN * D / 16;
 #pragma unroll
-    for (int c = tid; c < kChunks; c += 64 * kNW) {
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + i * kThreads;
+    f.k[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (c < kChunks) {
       const int key = c / (D / 16);
       const int col = (c % (D / 16)) * 16;
-      uint2 w = make_uint2(0u, 0u);
-      if (n0 + key < p.Sk) w = *(const uint2*)(kbase + (long)(n0 + key) * p.k_row + col / 2);
-      const uint2 a = unpack_int4x8(w.x), b = unpack_int4x8(w.y);
-      *(uint4*)(sm.k + key * Smem<D>::kKStride + col) = make_uint4(a.x, a.y, b.x, b.y);
-    }
-  } else {
-    constexpr int kChunks = kBN * D / 16;
-#pragma unroll
-    for (int c = tid; c < kChunks; c += 64 * kNW) {
-      const int key = c / (D / 16);
-      const int col = (c % (D / 16)) * 16;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (n0 + key < p.Sk) w = *(const uint4*)(kbase + (long)(n0 + key) * p.k_row + col);
-      *(uint4*)(sm.k + key * Smem<D>::kKStride + col) = w;
-    }
-  }
-}
-
-// Stage one V tile transposed into LDS as fp16: each thread converts 4 keys x 8 channels.
-template <int D>
-__device__ __forceinline__ void stage_v(Smem<D>& sm, const FwdParams& p, const uint8_t* vbase,
-                                        int n0) {
-  constexpr int kUnits = (kBN / 4) * (D / 8);
-  for (int u = threadIdx.x; u < kUnits; u += 64 * kNW) {
-    const int kg = u % (kBN / 4);
-    const int dg = u / (kBN / 4);
-    const int key0 = kg * 4;
-    _Float16 val[4][8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = n0 + key0 + r;
-      const bool ok = key < p.Sk;
-      const uint8_t* src = vbase + (long)key * p.v_row;
-      if (p.v_qtype == QFA_INT4) {
-        const uint32_t w = ok ? *(const uint32_t*)(src + dg * 4) : 0u;
-        const uint2 b = unpack_int4x8(w);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          val[r][e] = i8_to_h((b.x >> (8 * e)) & 0xFF);
-          val[r][4 + e] = i8_to_h((b.y >> (8 * e)) & 0xFF);
-        }
-      } else {
-        const uint2 w = ok ? *(const uint2*)(src + dg * 8) : make_uint2(0u, 0u);
-        if (p.v_qtype == QFA_INT8) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            val[r][e] = i8_to_h((w.x >> (8 * e)) & 0xFF);
-            val[r][4 + e] = i8_to_h((w.y >> (8 * e)) & 0xFF);
-          }
+      if (n0 + key < p.Sk) {
+        if (p.k_qtype == QFA_INT4) {
+          const uint2 w = *(const uint2*)(kbase + (long)(n0 + key) * p.k_row + col / 2);
+          f.k[i] = make_uint4(w.x, w.y, 0u, 0u);
         } else {
-          const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-          const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-          const f32x2 a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-          const f32x2 a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-          val[r][0] = (_Float16)a0[0]; val[r][1] = (_Float16)a0[1];
-          val[r][2] = (_Float16)a1[0]; val[r][3] = (_Float16)a1[1];
-          val[r][4] = (_Float16)a2[0]; val[r][5] = (_Float16)a2[1];
-          val[r][6] = (_Float16)a3[0]; val[r][7] = (_Float16)a3[1];
+          f.k[i] = *(const uint4*)(kbase + (long)(n0 + key) * p.k_row + col);
         }
       }
     }
-    const int pos = vt_pos(key0);
+  }
+  // V: 4 keys x 8 channels per thread.
+  constexpr int kUnits = (kBN / 4) * (D / 8);
+  const int kg = tid % (kBN / 4), dg = tid / (kBN / 4);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    f.v[r] = make_uint2(0u, 0u);
+    const int key = n0 + kg * 4 + r;
+    if (tid < kUnits && key < p.Sk) {
+      const uint8_t* src = vbase + (long)key * p.v_row;
+      if (p.v_qtype == QFA_INT4) f.v[r].x = *(const uint32_t*)(src + dg * 4);
+      else f.v[r] = *(const uint2*)(src + dg * 8);
+    }
+  }
+  f.ks = f.vs = 0.0f;
+  if (tid < kBN && n0 + tid < p.Sk && (p.kv_block % kBN) != 0) {
+    const long si = sbase + (n0 + tid) / p.kv_block;
+    f.ks = load_scale(p.ks, si, p.kv_scale_f16);
+    f.vs = load_scale(p.vs, si, p.kv_scale_f16);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(Stage<D>& st, const Prefetch& f, const FwdParams& p) {
+  const int tid = threadIdx.x;
+  constexpr int kChunks = kBN * D / 16;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + i * kThreads;
+    if (c < kChunks) {
+      const int key = c / (D / 16);
+      const int col = (c % (D / 16)) * 16;
+      uint4 w = f.k[i];
+      if (p.k_qtype == QFA_INT4) {
+        const uint2 a = unpack_int4x8(w.x), b = unpack_int4x8(w.y);
+        w = make_uint4(a.x, a.y, b.x, b.y);
+      }
+      *(uint4*)(st.k + key * Stage<D>::kKStride + col) = w;
+    }
+  }
+  constexpr int kUnits = (kBN / 4) * (D / 8);
+  if (tid < kUnits) {
+    const int kg = tid % (kBN / 4), dg = tid / (kBN / 4);
+    f16x2 val[4][4];  // [key][channel pair]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint2 w = f.v[r];
+      if (p.v_qtype == QFA_INT4) w = unpack_int4x8(w.x);
+      if (p.v_qtype == QFA_FP8_E4M3) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t ww = j ? w.y : w.x;
+          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww, false);
+          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww, true);
+          val[r][2 * j] = (f16x2){(_Float16)a[0], (_Float16)a[1]};
+          val[r][2 * j + 1] = (f16x2){(_Float16)b[0], (_Float16)b[1]};
+        }
+      } else {
+        i8x4_to_h(w.x, val[r][0], val[r][1]);
+        i8x4_to_h(w.y, val[r][2], val[r][3]);
+      }
+    }
+    const int pos = vt_pos(kg * 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      f16x4 col = {val[0][e], val[1][e], val[2][e], val[3][e]};
-      *(f16x4*)(sm.vt + (dg * 8 + e) * Smem<D>::kVStride + pos) = col;
+      const int j = e >> 1, s = e & 1;
+      f16x4 col = {val[0][j][s], val[1][j][s], val[2][j][s], val[3][j][s]};
+      *(f16x4*)(st.vt + (dg * 8 + e) * Stage<D>::kVStride + pos) = col;
     }
+  }
+  if (tid < kBN) {
+    st.ksc[tid] = f.ks;
+    st.vsc[tid] = f.vs;
   }
 }
 
 template <int D, bool FP8>
 struct QK {
-  // Bytes of one MFMA operand slice per lane and the number of MFMAs over D.
-  static constexpr int kSlice = FP8 ? 32 : 16;
+  static constexpr int kSlice = FP8 ? 32 : 16;  // operand bytes per lane per MFMA
   static constexpr int kSteps = D / (2 * kSlice);
   typedef typename std::conditional<FP8, i32x8, i32x4>::type Op;
   typedef typename std::conditional<FP8, f32x16, i32x16>::type Acc;
@@ -189,26 +233,59 @@ struct QK {
       return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
     }
   }
+  static __device__ __forceinline__ Op load(const uint8_t* p) {
+    if constexpr (FP8) {
+      const i32x4 lo = *(const i32x4*)p;
+      const i32x4 hi = *(const i32x4*)(p + 16);
+      return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return *(const i32x4*)p;
+    }
+  }
 };
 
-template <int D, bool FP8, bool CAUSAL, bool TOK_SCALE>
-__global__ __launch_bounds__(64 * kNW) void fwd_kernel(FwdParams p) {
+template <int D, bool FP8, bool CAUSAL, bool TOK>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   using T = QK<D, FP8>;
   using Op = typename T::Op;
   using Acc = typename T::Acc;
   constexpr int kDB = D / 32;  // 32-channel blocks of the output
-  __shared__ Smem<D> sm;
+  __shared__ Stage<D> stage[2];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;   // which half of the 32-key MFMA rows this lane holds
-  const int col = lane & 31;    // query column of this lane
-  const int mb = CAUSAL ? (p.n_mblocks - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const int half = lane >> 5;  // lane half: keys 4*half + {0..3} of every 8
+  const int col = lane & 31;   // query row of this lane within the wavefront
+
+  // Work item of this workgroup.
+  int mb, h, b;
+  {
+    const int id = blockIdx.x;
+    const int G = p.group;
+    const int ngroups = p.B * p.Hkv;
+    int mrank, gidx, hig;
+    if (p.xcd_order) {
+      const int xcd = id % kXcds, k = id / kXcds;
+      const int per_rank = (ngroups / kXcds) * G;
+      mrank = k / per_rank;
+      const int rem = k % per_rank;
+      gidx = (rem / G) * kXcds + xcd;
+      hig = rem % G;
+    } else {
+      const int per_rank = ngroups * G;
+      mrank = id / per_rank;
+      const int rem = id % per_rank;
+      gidx = rem / G;
+      hig = rem % G;
+    }
+    mb = CAUSAL ? p.n_mblocks - 1 - mrank : mrank;
+    b = gidx / p.Hkv;
+    h = (gidx % p.Hkv) * G + hig;
+  }
   const int kvh = h / p.group;
   const int m0 = mb * kBM;
-  const int qrow = m0 + wave * 32 + col;
+  const int wrow0 = m0 + wave * 32;
+  const int qrow = wrow0 + col;
   const bool qvalid = qrow < p.Sq;
 
   // Q slice of this lane (B operand of S^T = K . Q^T), kept in registers.
@@ -217,20 +294,8 @@ __global__ __launch_bounds__(64 * kNW) void fwd_kernel(FwdParams p) {
     const uint8_t* qp = p.q + (long)b * p.q_batch + (long)h * p.q_head + (long)qrow * p.q_row;
 #pragma unroll
     for (int s = 0; s < T::kSteps; ++s) {
-      const int off = s * 2 * T::kSlice + half * T::kSlice;
-      if constexpr (FP8) {
-        i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (qvalid) {
-          const i32x4 lo = *(const i32x4*)(qp + off);
-          const i32x4 hi = *(const i32x4*)(qp + off + 16);
-          v = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        qop[s] = v;
-      } else {
-        i32x4 v = {0, 0, 0, 0};
-        if (qvalid) v = *(const i32x4*)(qp + off);
-        qop[s] = v;
-      }
+      qop[s] = (Op){};
+      if (qvalid) qop[s] = T::load(qp + s * 2 * T::kSlice + half * T::kSlice);
     }
   }
   const float sq = qvalid ? load_scale(p.qs, ((long)b * p.Hq + h) * p.nqblk + qrow / p.q_block,
@@ -245,115 +310,179 @@ __global__ __launch_bounds__(64 * kNW) void fwd_kernel(FwdParams p) {
   f32x16 o[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i) o[i] = (f32x16){};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+  float m_run = -INFINITY;  // reference row max (log2 units)
+  float l_run = 0.0f;       // row sum of this lane half, in units of exp2(-m_run)
+  float sv_cur = 0.0f;      // V scale O is expressed in (per-tile scales)
 
   const int n_end = CAUSAL ? min(p.Sk, m0 + kBM) : p.Sk;
-  for (int n0 = 0; n0 < n_end; n0 += kBN) {
-    __syncthreads();
-    stage_k<D>(sm, p, kbase, n0);
-    stage_v<D>(sm, p, vbase, n0);
-    if constexpr (TOK_SCALE) {
-      for (int t = threadIdx.x; t < kBN; t += 64 * kNW) {
-        const int key = n0 + t;
-        const bool ok = key < p.Sk;
-        sm.ksc[t] = ok ? load_scale(p.ks, sbase + key / p.kv_block, p.kv_scale_f16) : 0.0f;
-        const float sv = ok ? load_scale(p.vs, sbase + key / p.kv_block, p.kv_scale_f16) : 0.0f;
-        sm.vsc[t] = sv;
-      }
-    }
-    __syncthreads();
+  const int ntiles = (n_end + kBN - 1) / kBN;
 
-    // S^T tile: two 32-key blocks.
-    Acc sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = (Acc){};
-      const uint8_t* krow = sm.k + (kb * 32 + col) * Smem<D>::kKStride;
-#pragma unroll
-      for (int s = 0; s < T::kSteps; ++s) {
-        const int off = s * 2 * T::kSlice + half * T::kSlice;
-        Op kop;
-        if constexpr (FP8) {
-          const i32x4 lo = *(const i32x4*)(krow + off);
-          const i32x4 hi = *(const i32x4*)(krow + off + 16);
-          kop = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-          kop = *(const i32x4*)(krow + off);
-        }
-        sacc[kb] = T::mma(kop, qop[s], sacc[kb]);
-      }
-    }
+  Prefetch pf;
+  fetch_tile<D>(pf, p, kbase, vbase, sbase, 0);
+  store_tile<D>(stage[0], pf, p);
+  __syncthreads();
 
-    // Scale fold and mask: x in log2 units.
-    float x[2][16];
-    float ck_tile = 0.0f;
-    if constexpr (!TOK_SCALE) ck_tile = cq * load_scale(p.ks, sbase + n0 / p.kv_block, p.kv_scale_f16);
-    const bool need_mask = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > m0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int n0 = t * kBN;
+    const Stage<D>& st = stage[t & 1];
+    const bool more = t + 1 < ntiles;
+    if (more) fetch_tile<D>(pf, p, kbase, vbase, sbase, n0 + kBN);
+
+    const bool wave_active = !CAUSAL || n0 <= wrow0 + 31;
+    if (wave_active) {
+      // S^T tile: two 32-key blocks.
+      Acc sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = (Acc){};
+        const uint8_t* krow = st.k + (kb * 32 + col) * Stage<D>::kKStride + half * T::kSlice;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const float c = TOK_SCALE ? cq * sm.ksc[kl] : ck_tile;
-        x[kb][r] = (float)sacc[kb][r] * c;
+        for (int s = 0; s < T::kSteps; ++s) sacc[kb] = T::mma(T::load(krow + s * 2 * T::kSlice), qop[s], sacc[kb]);
+      }
+
+      const bool need_mask = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
+      float x[2][16];
+      float mt;
+      float sv_t = 1.0f;
+      if constexpr (!TOK) {
+        // One K and one V scale for the whole tile.
+        const long si = sbase + n0 / p.kv_block;
+        const float ck = cq * load_scale(p.ks, si, p.kv_scale_f16);
+        sv_t = load_scale(p.vs, si, p.kv_scale_f16);
+        // Masked keys (bit kb*16+r) only occur on tiles crossing the diagonal or the end.
+        uint32_t mbits = 0;
         if (need_mask) {
-          const int key = n0 + kl;
-          if (key >= p.Sk || (CAUSAL && key > qrow)) x[kb][r] = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (key >= p.Sk || (CAUSAL && key > qrow)) mbits |= 1u << (kb * 16 + r);
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            x[kb][r] = (float)sacc[kb][r];
+            mx = fmaxf(mx, (mbits >> (kb * 16 + r)) & 1u ? -INFINITY : x[kb][r]);
+          }
+        mt = mx == -INFINITY ? -INFINITY : mx * ck;  // ck >= 0: the max commutes with it
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        // Rescale when the max grew past the slack or the V scale changed.
+        const float sv_eff = sv_t > 0.0f ? sv_t : (sv_cur > 0.0f ? sv_cur : 1.0f);
+        const bool need = mt > m_run + kRescaleSlack;
+        if (__any(need) || sv_eff != sv_cur) {
+          const float m_new = need ? fmaxf(m_run, mt) : m_run;
+          const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+          const float f = sv_cur > 0.0f ? alpha * (sv_cur / sv_eff) : 0.0f;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < kDB; ++i) o[i] *= f;
+          m_run = m_new;
+          sv_cur = sv_eff;
+        }
+        const float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
+        // Probabilities as the B operand of O^T += V^T . P^T.
+        f16x8 pb[2][2];
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            float a0 = __builtin_fmaf(x[kb][r], ck, msub);
+            float a1 = __builtin_fmaf(x[kb][r + 1], ck, msub);
+            if (need_mask) {
+              if ((mbits >> (kb * 16 + r)) & 1u) a0 = -INFINITY;
+              if ((mbits >> (kb * 16 + r + 1)) & 1u) a1 = -INFINITY;
+            }
+            const float p0 = __builtin_amdgcn_exp2f(a0);
+            const float p1 = __builtin_amdgcn_exp2f(a1);
+            const f16x2 h2 = {(_Float16)p0, (_Float16)p1};
+            l_run = __builtin_amdgcn_fdot2(h2, one, l_run, false);
+            pb[kb][r >> 3][r & 7] = h2[0];
+            pb[kb][r >> 3][(r & 7) + 1] = h2[1];
+          }
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const _Float16* vrow = st.vt + (db * 32 + col) * Stage<D>::kVStride + half * 8;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f16x8 a = *(const f16x8*)(vrow + g * 16);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
+          }
+        }
+      } else {
+        // Per-key scales (e.g. INT4 K/V with one scale per token).
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int kl = kb * 32 + 8 * rg + 4 * half;
+            const f32x4 s4 = *(const f32x4*)(st.ksc + kl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[kb][4 * rg + i] = (float)sacc[kb][4 * rg + i] * (cq * s4[i]);
+          }
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (key >= p.Sk || (CAUSAL && key > qrow)) x[kb][r] = -INFINITY;
+            }
+        }
+        mt = x[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[kb][r]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const bool need = mt > m_run + kRescaleSlack;
+        if (__any(need)) {
+          const float m_new = fmaxf(m_run, mt);
+          const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < kDB; ++i) o[i] *= alpha;
+          m_run = m_new;
+        }
+        const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+        f16x8 pb[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int kl = kb * 32 + 8 * rg + 4 * half;
+            const f32x4 v4 = *(const f32x4*)(st.vsc + kl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * rg + i;
+              const float pr = __builtin_amdgcn_exp2f(x[kb][r] - msub);
+              l_run += pr;
+              pb[kb][r >> 3][r & 7] = (_Float16)(pr * v4[i]);
+            }
+          }
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const _Float16* vrow = st.vt + (db * 32 + col) * Stage<D>::kVStride + half * 8;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f16x8 a = *(const f16x8*)(vrow + g * 16);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
+          }
         }
       }
     }
-    float mt = x[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[kb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-
-    const bool need = mt > m_run + kRescaleSlack;
-    if (__any(need)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < kDB; ++i) o[i] *= alpha;
-      m_run = m_new;
-    }
-    const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-
-    // Probabilities (fp16, sv folded in) as the B operand of O^T += V^T . P^T.
-    f16x8 pb[2][2];
-    float sv_tile = 0.0f;
-    if constexpr (!TOK_SCALE) {
-      sv_tile = load_scale(p.vs, sbase + n0 / p.kv_block, p.kv_scale_f16);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = exp2f(x[kb][r] - msub);
-        l_run += pr;
-        const int kl = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const float sv = TOK_SCALE ? sm.vsc[kl] : sv_tile;
-        pb[kb][r >> 3][r & 7] = (_Float16)(pr * sv);
-      }
-    }
-
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      const _Float16* vrow = sm.vt + (db * 32 + col) * Smem<D>::kVStride;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f16x8 a = *(const f16x8*)(vrow + g * 16 + half * 8);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
-      }
-    }
+    if (more) store_tile<D>(stage[(t + 1) & 1], pf, p);
+    __syncthreads();
   }
 
-  // Epilogue: O^T lane layout -> row qrow, channels 32*db + 8*(r/4) + 4*half + (r%4).
+  // Epilogue: lane holds row qrow, channels 32*db + 8*(r/4) + 4*half + (r%4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
-  const float inv = 1.0f / l_tot;
+  const float inv = (TOK ? 1.0f : sv_cur) / l_tot;
   const long obase = (long)b * p.o_batch + (long)h * p.o_head + (long)qrow * p.o_row;
 #pragma unroll
   for (int db = 0; db < kDB; ++db) {
@@ -377,14 +506,13 @@ __global__ __launch_bounds__(64 * kNW) void fwd_kernel(FwdParams p) {
 }
 
 template <int D, bool FP8>
-hipError_t launch_d(const FwdParams& p, dim3 grid, bool causal, bool tok, hipStream_t st) {
-  const dim3 block(64 * kNW);
+hipError_t launch_d(const FwdParams& p, int grid, bool causal, bool tok, hipStream_t st) {
   if (causal) {
-    if (tok) fwd_kernel<D, FP8, true, true><<<grid, block, 0, st>>>(p);
-    else fwd_kernel<D, FP8, true, false><<<grid, block, 0, st>>>(p);
+    if (tok) fwd_kernel<D, FP8, true, true><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, FP8, true, false><<<grid, kThreads, 0, st>>>(p);
   } else {
-    if (tok) fwd_kernel<D, FP8, false, true><<<grid, block, 0, st>>>(p);
-    else fwd_kernel<D, FP8, false, false><<<grid, block, 0, st>>>(p);
+    if (tok) fwd_kernel<D, FP8, false, true><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, FP8, false, false><<<grid, kThreads, 0, st>>>(p);
   }
   return hipGetLastError();
 }
@@ -400,6 +528,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.v = (const uint8_t*)a.v;
   p.vs = a.vs;
   p.out = a.out;
+  p.B = a.B;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.Sq = a.Sq;
@@ -433,15 +562,18 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.out_dtype = a.out_dtype;
   p.scale_log2 = a.softmax_scale * kLog2e;
   p.n_mblocks = (a.Sq + kBM - 1) / kBM;
-  const dim3 grid(p.n_mblocks, a.Hq, a.B);
+  p.xcd_order = ((long)a.B * a.Hkv) % kXcds == 0;
+  const long grid = (long)p.n_mblocks * a.B * a.Hq;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // Per-key scales unless every tile lies inside one scale block.
   const bool tok = (a.kv_block % kBN) != 0;
   const bool fp8 = a.q_qtype == QFA_FP8_E4M3;
   if (a.D == 64) {
-    return fp8 ? launch_d<64, true>(p, grid, a.causal, tok, stream)
-               : launch_d<64, false>(p, grid, a.causal, tok, stream);
+    return fp8 ? launch_d<64, true>(p, (int)grid, a.causal, tok, stream)
+               : launch_d<64, false>(p, (int)grid, a.causal, tok, stream);
   }
-  return fp8 ? launch_d<128, true>(p, grid, a.causal, tok, stream)
-             : launch_d<128, false>(p, grid, a.causal, tok, stream);
+  return fp8 ? launch_d<128, true>(p, (int)grid, a.causal, tok, stream)
+             : launch_d<128, false>(p, (int)grid, a.causal, tok, stream);
 }
 
 }  // namespace qfa

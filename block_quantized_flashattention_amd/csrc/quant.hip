@@ -101,13 +101,17 @@ struct In<QFA_F16> : In16<QFA_F16> {};
 template <>
 struct In<QFA_BF16> : In16<QFA_BF16> {};
 
+// fl32(x / s) given r = fl32(1 / s). KEEP_ZERO_SIGN restores the sign of an
+// exact zero quotient, which the FMA corrections turn into +0 (e4m3 encodes -0).
+template <bool KEEP_ZERO_SIGN>
 __device__ __forceinline__ float quotient(float x, float s, float r, bool fast) {
   if (!fast) return x / s;
   float q = x * r;
   float e = __builtin_fmaf(-q, s, x);
   q = __builtin_fmaf(e, r, q);
   e = __builtin_fmaf(-q, s, x);
-  return __builtin_fmaf(e, r, q);
+  q = __builtin_fmaf(e, r, q);
+  return KEEP_ZERO_SIGN ? __builtin_copysignf(q, x) : q;
 }
 
 template <int QT>
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QuantParams p) {
         float f[8], t[8];
         I::to_f32(raw[k], f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = quotient(f[i], s, rcp, fast);
+        for (int i = 0; i < 8; ++i) t[i] = quotient<QT == QFA_FP8_E4M3>(f[i], s, rcp, fast);
         store_codes<QT>(cb + (long)row * p.c_row + col / code_div, t, zero);
       }
       row += p.step_rows;
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QuantParams p) {
       float f[8], t[8];
       I::to_f32(I::load(xb + ((long)row * p.x_row + col) * I::kBytes), f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = quotient(f[i], s, rcp, fast);
+      for (int i = 0; i < 8; ++i) t[i] = quotient<QT == QFA_FP8_E4M3>(f[i], s, rcp, fast);
       store_codes<QT>(cb + (long)row * p.c_row + col / code_div, t, zero);
       row += p.step_rows;
       col += p.step_cols;

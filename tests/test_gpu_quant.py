@@ -81,7 +81,8 @@ def test_fp8_encoding_boundaries():
     rng = np.random.default_rng(5)
     rb = rng.integers(0, 0x43E00001, size=1 << 18, dtype=np.uint32).view(np.float32)
     h = np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float32)
-    vals = np.concatenate([near, -near, rb, -rb, h, [0.0, -0.0, 448.0, -448.0]]).astype(np.float32)
+    vals = np.concatenate([near, -near, rb, -rb, h,
+                           np.array([0.0, -0.0, 448.0, -448.0], np.float32)])
     vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448)]
     R, D = 64, 128
     per_block = R * D - 1
@@ -111,7 +112,7 @@ def test_int8_rounding_near_ties():
     n = rng.integers(-127, 127, size=R * D - 1).astype(np.float32)
     base = ((n + np.float32(0.5)) * s).astype(np.float32)
     jitter = rng.integers(-3, 4, size=base.size)
-    xv = (base.view(np.int32) + jitter).view(np.float32)
+    xv = (base.view(np.int32) + jitter.astype(np.int32)).view(np.float32)
     xv = np.clip(xv, -amax, amax)
     x = np.concatenate([[amax], xv]).astype(np.float32).reshape(1, 1, R, D)
     xt = torch.from_numpy(x)
