@@ -70,11 +70,18 @@ int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
   if (Sk < 1) return QFA_ERR_SHAPE;
   if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f || softmax_scale > 3.0e38f)
     return QFA_ERR_SHAPE;
-  const bool int8_qk = q_qtype == QFA_INT8 && (k_qtype == QFA_INT8 || k_qtype == QFA_INT4);
-  const bool fp8_qk = q_qtype == QFA_FP8_E4M3 && k_qtype == QFA_FP8_E4M3;
-  if (!int8_qk && !fp8_qk) return QFA_ERR_UNSUPPORTED;
+  // Compiled code-type combinations (Q, K, V).
+  const bool ok_types =
+      (q_qtype == QFA_INT8 && k_qtype == QFA_INT8 && v_qtype == QFA_INT8) ||
+      (q_qtype == QFA_INT8 && k_qtype == QFA_INT4 && v_qtype == QFA_INT4) ||
+      (q_qtype == QFA_INT8 && k_qtype == QFA_INT8 && v_qtype == QFA_INT4) ||
+      (q_qtype == QFA_FP8_E4M3 && k_qtype == QFA_FP8_E4M3 && v_qtype == QFA_FP8_E4M3);
+  if (!ok_types) return QFA_ERR_UNSUPPORTED;
   if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !out)
     return QFA_ERR_NULL;
+  // The kernel addresses K/V rows of one head with 32-bit offsets.
+  const long kv_row_bytes = (long)(layout == QFA_BSND ? Hkv : 1) * D;
+  if ((long)Sk * kv_row_bytes >= (1L << 32)) return QFA_ERR_UNSUPPORTED;
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
       !aligned(out, 16) || !aligned(q_scales, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
     return QFA_ERR_UNSUPPORTED;

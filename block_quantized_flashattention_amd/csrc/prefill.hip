@@ -9,9 +9,9 @@
 //   * A workgroup of 4 wavefronts owns 128 query rows of one (batch, head);
 //     each wavefront owns 32 rows. Two workgroups share a CU (at most 256
 //     registers per lane), so one's softmax arithmetic overlaps the other's
-//     matrix work. Key tiles of 64 rows are double-buffered in LDS: the next
-//     tile's codes are fetched into registers while the current one is
-//     computed, then written to the free buffer; one barrier per tile.
+//     matrix work. Key tiles of 64 rows are double-buffered in LDS and their
+//     codes are fetched into registers two tiles ahead (two register sets),
+//     so a load has two tiles of compute to arrive; one barrier per tile.
 //   * Scores are formed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_32x32x32_i8 (INT8 Q/K; INT4 K is widened to INT8 while it is
 //     staged) or v_mfma_f32_32x32x64_f8f6f4 (FP8 e4m3 Q/K). In the MFMA result
@@ -41,6 +41,8 @@
 //   * XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
 //     all query heads and row blocks of one (batch, KV head) are given ids on
 //     the same XCD and its K/V codes stay in that XCD's L2.
+#include <type_traits>
+
 #include "qfa_device.h"
 #include "qfa_launch.h"
 
@@ -76,12 +78,15 @@ struct FwdParams {
 };
 
 template <int D>
-struct Stage {
-  static constexpr int kKStride = D + 16;   // bytes per staged K row
-  static constexpr int kVStride = kBN + 8;  // fp16 elements per staged V^T row
-  uint8_t k[kBN * kKStride];
-  _Float16 vt[D * kVStride];
-  float ksc[kBN];
+struct KStage {
+  static constexpr int kStride = D + 16;    // bytes per staged K row
+  uint8_t k[kBN * kStride];
+};
+template <int D>
+struct VStage {
+  static constexpr int kStride = kBN + 8;   // fp16 elements per staged V^T row
+  _Float16 vt[D * kStride];
+  float ksc[kBN];                           // K and V scales of the same tile's keys
   float vsc[kBN];
 };
 
@@ -115,75 +120,97 @@ __device__ __forceinline__ void i8x4_to_h(uint32_t w, f16x2& lo, f16x2& hi) {
   hi = __builtin_bit_cast(f16x2, b) - bias;
 }
 
-// Registers holding one prefetched tile of K and V codes for this thread.
+// Code types of K and V handled by one kernel instance.
+enum KVMode { KV_I8_I8 = 0, KV_I4_I4 = 1, KV_I8_I4 = 2, KV_F8_F8 = 3 };
+template <int M> struct KVTypes;
+template <> struct KVTypes<KV_I8_I8> { static constexpr int K = QFA_INT8, V = QFA_INT8; };
+template <> struct KVTypes<KV_I4_I4> { static constexpr int K = QFA_INT4, V = QFA_INT4; };
+template <> struct KVTypes<KV_I8_I4> { static constexpr int K = QFA_INT8, V = QFA_INT4; };
+template <> struct KVTypes<KV_F8_F8> { static constexpr int K = QFA_FP8_E4M3, V = QFA_FP8_E4M3; };
+
+// Registers holding one prefetched tile of K and V codes (and scales) for this thread.
 struct Prefetch {
-  uint4 k[2];
+  uint4 k[kBN * 128 / 16 / kThreads];
   uint2 v[4];
-  float ks, vs;
+  uint32_t ks, vs;  // raw dwords holding this thread's key's scales
+  uint32_t shift;   // bit offset of an fp16 scale inside its dword
 };
 
-template <int D>
+__device__ __forceinline__ float scale_from_bits(uint32_t bits, bool f16) {
+  return f16 ? f16_bits_to_f32(bits) : __uint_as_float(bits);
+}
+
+// Issue the loads of one tile's codes and scales into registers. Every load is
+// unconditional (keys past the end are clamped to the last key, whose codes
+// are finite and whose scores are masked) and nothing reads the loaded values
+// before store_tile, so the loads stay in flight across the compute of the
+// tiles in between. In-head offsets are 32-bit (checked on the host).
+template <int D, int KQT, int VQT>
 __device__ __forceinline__ void fetch_tile(Prefetch& f, const FwdParams& p, const uint8_t* kbase,
-                                           const uint8_t* vbase, long sbase, int n0) {
+                                           const uint8_t* vbase, long sbase, int kn0, int vn0) {
   const int tid = threadIdx.x;
-  // K: 16-byte chunks of codes (8-byte chunks of packed INT4).
-  constexpr int kChunks = kBN * D / 16;
+  const int last = p.Sk - 1;
+  int n0 = kn0;
+  const uint32_t krow = (uint32_t)p.k_row, vrow = (uint32_t)p.v_row;
+  constexpr int kChunks = kBN * D / 16;  // 16 codes per chunk
+  static_assert(kChunks % kThreads == 0, "K chunks per thread");
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kChunks / kThreads; ++i) {
     const int c = tid + i * kThreads;
-    f.k[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (c < kChunks) {
-      const int key = c / (D / 16);
-      const int col = (c % (D / 16)) * 16;
-      if (n0 + key < p.Sk) {
-        if (p.k_qtype == QFA_INT4) {
-          const uint2 w = *(const uint2*)(kbase + (long)(n0 + key) * p.k_row + col / 2);
-          f.k[i] = make_uint4(w.x, w.y, 0u, 0u);
-        } else {
-          f.k[i] = *(const uint4*)(kbase + (long)(n0 + key) * p.k_row + col);
-        }
-      }
+    const uint32_t key = (uint32_t)min(n0 + c / (D / 16), last);
+    const uint32_t col = (uint32_t)(c % (D / 16)) * 16u;
+    if constexpr (KQT == QFA_INT4) {
+      const uint2 w = *(const uint2*)(kbase + (key * krow + col / 2u));
+      f.k[i] = make_uint4(w.x, w.y, 0u, 0u);
+    } else {
+      f.k[i] = *(const uint4*)(kbase + (key * krow + col));
     }
   }
-  // V: 4 keys x 8 channels per thread.
+  // V: 4 keys x 8 channels per thread (threads past the last unit repeat a unit).
+  n0 = vn0;
   constexpr int kUnits = (kBN / 4) * (D / 8);
-  const int kg = tid % (kBN / 4), dg = tid / (kBN / 4);
+  const int u = tid % kUnits;
+  const int kg = u % (kBN / 4), dg = u / (kBN / 4);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    f.v[r] = make_uint2(0u, 0u);
-    const int key = n0 + kg * 4 + r;
-    if (tid < kUnits && key < p.Sk) {
-      const uint8_t* src = vbase + (long)key * p.v_row;
-      if (p.v_qtype == QFA_INT4) f.v[r].x = *(const uint32_t*)(src + dg * 4);
-      else f.v[r] = *(const uint2*)(src + dg * 8);
+    const uint32_t key = (uint32_t)min(n0 + kg * 4 + r, last);
+    if constexpr (VQT == QFA_INT4) {
+      f.v[r] = make_uint2(*(const uint32_t*)(vbase + (key * vrow + (uint32_t)dg * 4u)), 0u);
+    } else {
+      f.v[r] = *(const uint2*)(vbase + (key * vrow + (uint32_t)dg * 8u));
     }
   }
-  f.ks = f.vs = 0.0f;
-  if (tid < kBN && n0 + tid < p.Sk && (p.kv_block % kBN) != 0) {
-    const long si = sbase + (n0 + tid) / p.kv_block;
-    f.ks = load_scale(p.ks, si, p.kv_scale_f16);
-    f.vs = load_scale(p.vs, si, p.kv_scale_f16);
+  // Scale of this thread's key (slot 0 alone is read when one scale covers the
+  // tile), as the aligned dword holding it, for either scale type.
+  const int key = min(n0 + (tid % kBN), last);
+  const long g = sbase + (p.kv_block == 1 ? key : key / p.kv_block);
+  const long widx = p.kv_scale_f16 ? (g >> 1) : g;
+  f.shift = p.kv_scale_f16 ? (uint32_t)(g & 1) * 16u : 0u;
+  f.ks = ((const uint32_t*)p.ks)[widx];
+  f.vs = ((const uint32_t*)p.vs)[widx];
+}
+
+template <int D, int KQT>
+__device__ __forceinline__ void store_k(KStage<D>& st, const Prefetch& f) {
+  const int tid = threadIdx.x;
+  constexpr int kChunks = kBN * D / 16;
+#pragma unroll
+  for (int i = 0; i < kChunks / kThreads; ++i) {
+    const int c = tid + i * kThreads;
+    const int key = c / (D / 16);
+    const int col = (c % (D / 16)) * 16;
+    uint4 w = f.k[i];
+    if constexpr (KQT == QFA_INT4) {
+      const uint2 a = unpack_int4x8(w.x), b = unpack_int4x8(w.y);
+      w = make_uint4(a.x, a.y, b.x, b.y);
+    }
+    *(uint4*)(st.k + key * KStage<D>::kStride + col) = w;
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(Stage<D>& st, const Prefetch& f, const FwdParams& p) {
+template <int D, int VQT>
+__device__ __forceinline__ void store_v(VStage<D>& st, const Prefetch& f, bool scale_f16) {
   const int tid = threadIdx.x;
-  constexpr int kChunks = kBN * D / 16;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + i * kThreads;
-    if (c < kChunks) {
-      const int key = c / (D / 16);
-      const int col = (c % (D / 16)) * 16;
-      uint4 w = f.k[i];
-      if (p.k_qtype == QFA_INT4) {
-        const uint2 a = unpack_int4x8(w.x), b = unpack_int4x8(w.y);
-        w = make_uint4(a.x, a.y, b.x, b.y);
-      }
-      *(uint4*)(st.k + key * Stage<D>::kKStride + col) = w;
-    }
-  }
   constexpr int kUnits = (kBN / 4) * (D / 8);
   if (tid < kUnits) {
     const int kg = tid % (kBN / 4), dg = tid / (kBN / 4);
@@ -191,8 +218,8 @@ __device__ __forceinline__ void store_tile(Stage<D>& st, const Prefetch& f, cons
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       uint2 w = f.v[r];
-      if (p.v_qtype == QFA_INT4) w = unpack_int4x8(w.x);
-      if (p.v_qtype == QFA_FP8_E4M3) {
+      if constexpr (VQT == QFA_INT4) w = unpack_int4x8(w.x);
+      if constexpr (VQT == QFA_FP8_E4M3) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const uint32_t ww = j ? w.y : w.x;
@@ -211,12 +238,13 @@ __device__ __forceinline__ void store_tile(Stage<D>& st, const Prefetch& f, cons
     for (int e = 0; e < 8; ++e) {
       const int j = e >> 1, s = e & 1;
       f16x4 col = {val[0][j][s], val[1][j][s], val[2][j][s], val[3][j][s]};
-      *(f16x4*)(st.vt + (dg * 8 + e) * Stage<D>::kVStride + pos) = col;
+      *(f16x4*)(st.vt + (dg * 8 + e) * VStage<D>::kStride + pos) = col;
     }
   }
   if (tid < kBN) {
-    st.ksc[tid] = f.ks;
-    st.vsc[tid] = f.vs;
+    const uint32_t mask = scale_f16 ? 0xFFFFu : 0xFFFFFFFFu;
+    st.ksc[tid] = scale_from_bits((f.ks >> f.shift) & mask, scale_f16);
+    st.vsc[tid] = scale_from_bits((f.vs >> f.shift) & mask, scale_f16);
   }
 }
 
@@ -244,13 +272,20 @@ struct QK {
   }
 };
 
-template <int D, bool FP8, bool CAUSAL, bool TOK>
+// Key offset (within the tile) of accumulator register r of 32-key block kb,
+// for the lane half `half`: MFMA 32x32 result rows 8*(r/4) + 4*half + r%4.
+__device__ __forceinline__ constexpr int key_of(int kb, int r) { return kb * 32 + 8 * (r >> 2) + (r & 3); }
+
+template <int D, int KVM, bool CAUSAL, bool TOK>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
+  constexpr bool FP8 = KVM == KV_F8_F8;
+  constexpr int KQT = KVTypes<KVM>::K, VQT = KVTypes<KVM>::V;
   using T = QK<D, FP8>;
   using Op = typename T::Op;
   using Acc = typename T::Acc;
   constexpr int kDB = D / 32;  // 32-channel blocks of the output
-  __shared__ Stage<D> stage[2];
+  __shared__ KStage<D> kst[2];
+  __shared__ VStage<D> vst[2];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -312,171 +347,171 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   for (int i = 0; i < kDB; ++i) o[i] = (f32x16){};
   float m_run = -INFINITY;  // reference row max (log2 units)
   float l_run = 0.0f;       // row sum of this lane half, in units of exp2(-m_run)
-  float sv_cur = 0.0f;      // V scale O is expressed in (per-tile scales)
+  float sv_cur = 0.0f;      // V scale O is expressed in (one scale per tile)
 
   const int n_end = CAUSAL ? min(p.Sk, m0 + kBM) : p.Sk;
   const int ntiles = (n_end + kBN - 1) / kBN;
+  // Keys beyond this offset from the tile start are masked for this lane
+  // (causal diagonal or end of the keys), per lane half.
+  const int lim_base = (CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1) - 4 * half;
+  auto wave_active = [&](int t) { return !CAUSAL || t * kBN <= wrow0 + 31; };
 
-  Prefetch pf;
-  fetch_tile<D>(pf, p, kbase, vbase, sbase, 0);
-  store_tile<D>(stage[0], pf, p);
-  __syncthreads();
+  // S^T tile t = K_t . Q^T from K buffer t % 2 (two 32-key blocks).
+  auto qk = [&](Acc* sacc, const KStage<D>& ks) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = (Acc){};
+      const uint8_t* krow = ks.k + (kb * 32 + col) * KStage<D>::kStride + half * T::kSlice;
+#pragma unroll
+      for (int s = 0; s < T::kSteps; ++s)
+        sacc[kb] = T::mma(T::load(krow + s * 2 * T::kSlice), qop[s], sacc[kb]);
+    }
+  };
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Softmax of tile t and O^T += V_t^T . P_t^T (V and scales from V buffer t % 2).
+  auto softmax_pv = [&](const Acc* sacc, const VStage<D>& vs, int t) {
     const int n0 = t * kBN;
-    const Stage<D>& st = stage[t & 1];
-    const bool more = t + 1 < ntiles;
-    if (more) fetch_tile<D>(pf, p, kbase, vbase, sbase, n0 + kBN);
-
-    const bool wave_active = !CAUSAL || n0 <= wrow0 + 31;
-    if (wave_active) {
-      // S^T tile: two 32-key blocks.
-      Acc sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = (Acc){};
-        const uint8_t* krow = st.k + (kb * 32 + col) * Stage<D>::kKStride + half * T::kSlice;
-#pragma unroll
-        for (int s = 0; s < T::kSteps; ++s) sacc[kb] = T::mma(T::load(krow + s * 2 * T::kSlice), qop[s], sacc[kb]);
-      }
-
-      const bool need_mask = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
+    const bool need_mask = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
+    const int lim = lim_base - n0;  // masked iff key_of(kb, r) > lim
+    f16x8 pb[2][2];
+    if constexpr (!TOK) {
+      // One K and one V scale for the whole tile, staged in slot 0.
+      const float ck = cq * vs.ksc[0];
+      const float sv_t = vs.vsc[0];
       float x[2][16];
-      float mt;
-      float sv_t = 1.0f;
-      if constexpr (!TOK) {
-        // One K and one V scale for the whole tile.
-        const long si = sbase + n0 / p.kv_block;
-        const float ck = cq * load_scale(p.ks, si, p.kv_scale_f16);
-        sv_t = load_scale(p.vs, si, p.kv_scale_f16);
-        // Masked keys (bit kb*16+r) only occur on tiles crossing the diagonal or the end.
-        uint32_t mbits = 0;
-        if (need_mask) {
+      float mx = -INFINITY;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (key >= p.Sk || (CAUSAL && key > qrow)) mbits |= 1u << (kb * 16 + r);
-            }
-        }
-        float mx = -INFINITY;
+        for (int r = 0; r < 16; ++r) x[kb][r] = (float)sacc[kb][r];
+      if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            x[kb][r] = (float)sacc[kb][r];
-            mx = fmaxf(mx, (mbits >> (kb * 16 + r)) & 1u ? -INFINITY : x[kb][r]);
-          }
-        mt = mx == -INFINITY ? -INFINITY : mx * ck;  // ck >= 0: the max commutes with it
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        // Rescale when the max grew past the slack or the V scale changed.
-        const float sv_eff = sv_t > 0.0f ? sv_t : (sv_cur > 0.0f ? sv_cur : 1.0f);
-        const bool need = mt > m_run + kRescaleSlack;
-        if (__any(need) || sv_eff != sv_cur) {
-          const float m_new = need ? fmaxf(m_run, mt) : m_run;
-          const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-          const float f = sv_cur > 0.0f ? alpha * (sv_cur / sv_eff) : 0.0f;
-          l_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < kDB; ++i) o[i] *= f;
-          m_run = m_new;
-          sv_cur = sv_eff;
-        }
-        const float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
-        // Probabilities as the B operand of O^T += V^T . P^T.
-        f16x8 pb[2][2];
-        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            float a0 = __builtin_fmaf(x[kb][r], ck, msub);
-            float a1 = __builtin_fmaf(x[kb][r + 1], ck, msub);
-            if (need_mask) {
-              if ((mbits >> (kb * 16 + r)) & 1u) a0 = -INFINITY;
-              if ((mbits >> (kb * 16 + r + 1)) & 1u) a1 = -INFINITY;
-            }
-            const float p0 = __builtin_amdgcn_exp2f(a0);
-            const float p1 = __builtin_amdgcn_exp2f(a1);
-            const f16x2 h2 = {(_Float16)p0, (_Float16)p1};
-            l_run = __builtin_amdgcn_fdot2(h2, one, l_run, false);
-            pb[kb][r >> 3][r & 7] = h2[0];
-            pb[kb][r >> 3][(r & 7) + 1] = h2[1];
-          }
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const _Float16* vrow = st.vt + (db * 32 + col) * Stage<D>::kVStride + half * 8;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f16x8 a = *(const f16x8*)(vrow + g * 16);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
-          }
-        }
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, key_of(kb, r) > lim ? -INFINITY : x[kb][r]);
       } else {
-        // Per-key scales (e.g. INT4 K/V with one scale per token).
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const int kl = kb * 32 + 8 * rg + 4 * half;
-            const f32x4 s4 = *(const f32x4*)(st.ksc + kl);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
+      }
+      // Max of this lane half; the row max over both halves is only formed when
+      // some row needs a rescale (or the V scale changes), which is rare.
+      const float mt = mx == -INFINITY ? -INFINITY : mx * ck;  // ck >= 0
+      const float sv_eff = sv_t > 0.0f ? sv_t : (sv_cur > 0.0f ? sv_cur : 1.0f);
+      if (__any(mt > m_run + kRescaleSlack) || sv_eff != sv_cur) {
+        const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = mrow > m_run + kRescaleSlack ? fmaxf(m_run, mrow) : m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float f = sv_cur > 0.0f ? alpha * (sv_cur / sv_eff) : 0.0f;
+        l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[kb][4 * rg + i] = (float)sacc[kb][4 * rg + i] * (cq * s4[i]);
+        for (int i = 0; i < kDB; ++i) o[i] *= f;
+        m_run = m_new;
+        sv_cur = sv_eff;
+      }
+      const float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
+      const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float a0 = __builtin_fmaf(x[kb][r], ck, msub);
+          float a1 = __builtin_fmaf(x[kb][r + 1], ck, msub);
+          if (need_mask) {
+            a0 = key_of(kb, r) > lim ? -INFINITY : a0;
+            a1 = key_of(kb, r + 1) > lim ? -INFINITY : a1;
           }
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (key >= p.Sk || (CAUSAL && key > qrow)) x[kb][r] = -INFINITY;
-            }
+          const f16x2 h2 = {(_Float16)__builtin_amdgcn_exp2f(a0),
+                            (_Float16)__builtin_amdgcn_exp2f(a1)};
+          l_run = __builtin_amdgcn_fdot2(h2, one, l_run, false);
+          pb[kb][r >> 3][r & 7] = h2[0];
+          pb[kb][r >> 3][(r & 7) + 1] = h2[1];
         }
-        mt = x[0][0];
+    } else {
+      // Per-key scales (e.g. INT4 K/V with one scale per token).
+      float x[2][16];
+      float mt = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[kb][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const bool need = mt > m_run + kRescaleSlack;
-        if (__any(need)) {
-          const float m_new = fmaxf(m_run, mt);
-          const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 s4 = *(const f32x4*)(vs.ksc + kb * 32 + 8 * rg + 4 * half);
 #pragma unroll
-          for (int i = 0; i < kDB; ++i) o[i] *= alpha;
-          m_run = m_new;
-        }
-        const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-        f16x8 pb[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            const int kl = kb * 32 + 8 * rg + 4 * half;
-            const f32x4 v4 = *(const f32x4*)(st.vsc + kl);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * rg + i;
-              const float pr = __builtin_amdgcn_exp2f(x[kb][r] - msub);
-              l_run += pr;
-              pb[kb][r >> 3][r & 7] = (_Float16)(pr * v4[i]);
-            }
-          }
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) {
-          const _Float16* vrow = st.vt + (db * 32 + col) * Stage<D>::kVStride + half * 8;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f16x8 a = *(const f16x8*)(vrow + g * 16);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rg + i;
+            float xv = (float)sacc[kb][r] * (cq * s4[i]);
+            if (need_mask) xv = key_of(kb, r) > lim ? -INFINITY : xv;
+            x[kb][r] = xv;
+            mt = fmaxf(mt, xv);
           }
         }
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = mrow > m_run + kRescaleSlack ? fmaxf(m_run, mrow) : m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < kDB; ++i) o[i] *= alpha;
+        m_run = m_new;
+      }
+      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 v4 = *(const f32x4*)(vs.vsc + kb * 32 + 8 * rg + 4 * half);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rg + i;
+            const float pr = __builtin_amdgcn_exp2f(x[kb][r] - msub);
+            l_run += pr;
+            pb[kb][r >> 3][r & 7] = (_Float16)(pr * v4[i]);
+          }
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+      const _Float16* vrow = vs.vt + (db * 32 + col) * VStage<D>::kStride + half * 8;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f16x8 a = *(const f16x8*)(vrow + g * 16);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
       }
     }
-    if (more) store_tile<D>(stage[(t + 1) & 1], pf, p);
+  };
+
+  // Pipeline: K runs one tile ahead of V. Step t issues S(t+1) = K_{t+1} Q^T on
+  // the matrix unit, computes the softmax of S(t) on the vector unit meanwhile,
+  // issues P(t) V_t, then writes the prefetched K_{t+2} and V_{t+1} (loaded
+  // during the previous step) to the buffers freed by the last barrier.
+  const int last_tile = ntiles - 1;
+  auto tile_n0 = [&](int t) { return min(t, last_tile) * kBN; };
+  Prefetch pf;
+  fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, 0, 0);
+  store_k<D, KQT>(kst[0], pf);
+  store_v<D, VQT>(vst[0], pf, p.kv_scale_f16);
+  fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, tile_n0(1), tile_n0(1));
+  store_k<D, KQT>(kst[1], pf);
+  fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, tile_n0(2), tile_n0(1));
+  __syncthreads();
+
+  Acc sa[2], sb[2];
+  if (wave_active(0)) qk(sa, kst[0]);
+  auto step = [&](const int t, Acc* scur, Acc* snext, auto par) {
+    constexpr int PAR = decltype(par)::value;  // t % 2
+    if (t + 1 < ntiles && wave_active(t + 1)) qk(snext, kst[PAR ^ 1]);
+    if (wave_active(t)) softmax_pv(scur, vst[PAR], t);
+    // K_{t+2} into K buffer t % 2 (K_t was last read in step t-1) and V_{t+1}
+    // into V buffer (t+1) % 2 (V_{t-1} was last read in step t-1).
+    store_k<D, KQT>(kst[PAR], pf);
+    store_v<D, VQT>(vst[PAR ^ 1], pf, p.kv_scale_f16);
     __syncthreads();
+    fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, tile_n0(t + 3), tile_n0(t + 2));
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sa, sb, std::integral_constant<int, 0>());
+    if (t + 1 < ntiles) step(t + 1, sb, sa, std::integral_constant<int, 1>());
   }
 
   // Epilogue: lane holds row qrow, channels 32*db + 8*(r/4) + 4*half + (r%4).
@@ -505,16 +540,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool FP8>
-hipError_t launch_d(const FwdParams& p, int grid, bool causal, bool tok, hipStream_t st) {
+template <int D, int KVM>
+hipError_t launch_kv(const FwdParams& p, int grid, bool causal, bool tok, hipStream_t st) {
   if (causal) {
-    if (tok) fwd_kernel<D, FP8, true, true><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, FP8, true, false><<<grid, kThreads, 0, st>>>(p);
+    if (tok) fwd_kernel<D, KVM, true, true><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, true, false><<<grid, kThreads, 0, st>>>(p);
   } else {
-    if (tok) fwd_kernel<D, FP8, false, true><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, FP8, false, false><<<grid, kThreads, 0, st>>>(p);
+    if (tok) fwd_kernel<D, KVM, false, true><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, false, false><<<grid, kThreads, 0, st>>>(p);
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams& p, int kvm, int grid, bool causal, bool tok, hipStream_t st) {
+  switch (kvm) {
+    case KV_I8_I8: return launch_kv<D, KV_I8_I8>(p, grid, causal, tok, st);
+    case KV_I4_I4: return launch_kv<D, KV_I4_I4>(p, grid, causal, tok, st);
+    case KV_I8_I4: return launch_kv<D, KV_I8_I4>(p, grid, causal, tok, st);
+    case KV_F8_F8: return launch_kv<D, KV_F8_F8>(p, grid, causal, tok, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -567,13 +613,14 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   // Per-key scales unless every tile lies inside one scale block.
   const bool tok = (a.kv_block % kBN) != 0;
-  const bool fp8 = a.q_qtype == QFA_FP8_E4M3;
-  if (a.D == 64) {
-    return fp8 ? launch_d<64, true>(p, (int)grid, a.causal, tok, stream)
-               : launch_d<64, false>(p, (int)grid, a.causal, tok, stream);
-  }
-  return fp8 ? launch_d<128, true>(p, (int)grid, a.causal, tok, stream)
-             : launch_d<128, false>(p, (int)grid, a.causal, tok, stream);
+  int kvm = -1;
+  if (a.q_qtype == QFA_FP8_E4M3 && a.k_qtype == QFA_FP8_E4M3 && a.v_qtype == QFA_FP8_E4M3) kvm = KV_F8_F8;
+  if (a.q_qtype == QFA_INT8 && a.k_qtype == QFA_INT8 && a.v_qtype == QFA_INT8) kvm = KV_I8_I8;
+  if (a.q_qtype == QFA_INT8 && a.k_qtype == QFA_INT4 && a.v_qtype == QFA_INT4) kvm = KV_I4_I4;
+  if (a.q_qtype == QFA_INT8 && a.k_qtype == QFA_INT8 && a.v_qtype == QFA_INT4) kvm = KV_I8_I4;
+  if (kvm < 0) return hipErrorInvalidValue;
+  if (a.D == 64) return launch_d<64>(p, kvm, (int)grid, a.causal, tok, stream);
+  return launch_d<128>(p, kvm, (int)grid, a.causal, tok, stream);
 }
 
 }  // namespace qfa

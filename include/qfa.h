@@ -107,14 +107,18 @@ QFA_API int qfa_block_quant(const void* x, int x_dtype, int B, int N, int S, int
  * precision; [FA-INT8/INT4] INT8 and INT4 layers, with INT4 widened to INT8
  * before the product).
  *
- *   q_codes    [B,Hq,Sq,D] (layout), q_qtype INT8 or FP8_E4M3.
+ *   q_codes    [B,Hq,Sq,D] (layout); k_codes, v_codes [B,Hkv,Sk,D] (D/2 bytes for INT4).
+ *              Code types (q, k, v): (INT8, INT8, INT8), (INT8, INT4, INT4),
+ *              (INT8, INT8, INT4) or (FP8_E4M3, FP8_E4M3, FP8_E4M3); others
+ *              return QFA_ERR_UNSUPPORTED.
  *   q_scales   [B,Hq,ceil(Sq/q_block)], q_scale_dtype F32/F16.
- *   k_codes    [B,Hkv,Sk,D or D/2], k_qtype: INT8 or INT4 with INT8 Q; FP8 with FP8 Q.
- *   v_codes    [B,Hkv,Sk,D or D/2], v_qtype INT8, INT4 or FP8_E4M3 (any Q/K type).
  *   k_scales, v_scales [B,Hkv,ceil(Sk/kv_block)], kv_scale_dtype F32/F16.
  *   out        [B,Hq,Sq,D] (same layout as q), out_dtype F32/F16/BF16.
  * Limits: D in {64, 128}; Hq % Hkv == 0; Sk >= 1 when Sq >= 1; q_block and
- * kv_block >= 1; finite scales. Sq == 0 returns QFA_OK without a launch.
+ * kv_block >= 1; finite scales; code pointers and out 16-byte aligned, scales
+ * 4-byte aligned (else QFA_ERR_UNSUPPORTED). Sq == 0 returns QFA_OK without a
+ * launch. The output of a row whose scores are all equal to -inf cannot occur
+ * (every row keeps at least key 0).
  */
 QFA_API int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
             int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
