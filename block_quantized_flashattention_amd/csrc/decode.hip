@@ -8,20 +8,24 @@
 //
 // Design (HBM-bound: every valid cache byte is read once):
 //   * Split-K: a workgroup of 4 wavefronts owns one (batch, query head,
-//     1024-token chunk); each wavefront owns 256 tokens of the chunk. Chunks
+//     1024-token chunk); each wavefront owns 256 consecutive tokens. Chunks
 //     past a sequence's length exit at once. A second small kernel merges the
 //     chunks' partial (max, sum, o) by log-sum-exp; a sequence that fits one
 //     chunk is written directly.
 //   * Lane geometry: a 16-byte load per lane, LPT = row_bytes/16 lanes per
-//     token, so one wavefront load covers 64/LPT consecutive tokens.
-//   * Two passes per 256 tokens: scores for all of them first (dot product
-//     over the lane's channels, then a butterfly over the LPT lanes), their
-//     max, one rescale of the running (max, sum, o), then exp2 and the V
-//     accumulation. Every lane accumulates o for its own channels over its
-//     own tokens; the token groups are summed once at the end.
-//   * Codes are converted with the unsigned-byte converter after flipping the
-//     sign bit (code + 128 for INT8, code + 8 for INT4); the offset is
-//     removed once per token (scores) or once per output channel (values).
+//     token, so one wavefront load covers 64/LPT consecutive tokens; loads are
+//     issued four at a time ahead of their use.
+//   * Two passes per 256 tokens: all scores first (a per-lane partial dot
+//     product, then a DPP butterfly over the LPT lanes of the token), their
+//     max, then exp2 and the V accumulation; every lane accumulates o for its
+//     own channels over its own tokens and the token groups are summed once.
+//   * With an fp16 query, K codes are converted exactly to packed fp16 (the
+//     byte goes into the mantissa of 1024 + byte) and dotted with
+//     v_dot2_f32_f16 (fp32 accumulation). V codes are converted with the
+//     unsigned-byte converter after flipping the sign bit (code + 128, or code
+//     + 8 for INT4); the offset is removed once per output channel.
+//   * When one scale block covers a wavefront's 256 tokens (block size a
+//     multiple of 256), its K and V scales are two scalar loads.
 #include "qfa_device.h"
 #include "qfa_launch.h"
 
@@ -30,6 +34,7 @@ namespace {
 
 constexpr int kDecWaves = 4;
 constexpr int kWaveTokens = kDecodeChunk / kDecWaves;  // 256
+constexpr int kGroup = 4;                              // loads issued together
 
 struct DecParams {
   const void* q;
@@ -59,7 +64,42 @@ __device__ __forceinline__ void store_out(void* out, long i, float v, int dt) {
   else ((uint16_t*)out)[i] = (uint16_t)f32_to_bf16_bits(v);
 }
 
-// Offset codes (code + 128, or code + 8 for INT4) of one 16-byte lane chunk as floats.
+// Sum over groups of LPT consecutive lanes (LPT in {2, 4, 8}) with DPP moves.
+template <int LPT>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  // quad_perm [1,0,3,2] and [2,3,0,1]: partners at lane xor 1 and xor 2.
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  if constexpr (LPT >= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  if constexpr (LPT >= 8)  // row_half_mirror: lane i <-> 7-i within each 8 lanes
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  return v;
+}
+
+// Four signed bytes as two exact fp16 pairs (1024 + (byte ^ 0x80) - 1152).
+__device__ __forceinline__ void i8x4_to_h(uint32_t w, f16x2& lo, f16x2& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u);
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = __builtin_bit_cast(f16x2, a) - bias;
+  hi = __builtin_bit_cast(f16x2, b) - bias;
+}
+
+// Eight packed two's-complement nibbles (element 2k low) as four exact fp16 pairs.
+__device__ __forceinline__ void i4x8_to_h(uint32_t w, f16x2* h) {
+  const uint32_t u = w ^ 0x88888888u;              // nibble + 8 in [0, 15]
+  const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+  const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // e0 e1 e2 e3
+  const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // e4 e5 e6 e7
+  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, p0, 0x05010400u)) - bias;
+  h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, p0, 0x07030602u)) - bias;
+  h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, p1, 0x05010400u)) - bias;
+  h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, p1, 0x07030602u)) - bias;
+}
+
+// Offset codes (code + 128, or code + 8 for INT4) of one 16-byte chunk as floats.
 template <bool INT4>
 __device__ __forceinline__ void chunk_to_f32(const uint4& w, float* f) {
   const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -86,14 +126,16 @@ __device__ __forceinline__ void chunk_to_f32(const uint4& w, float* f) {
   }
 }
 
-template <int D, bool INT4>
+template <int D, bool INT4, bool QF16, bool BLOCK_SCALE>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams p) {
   constexpr int kRowBytes = INT4 ? D / 2 : D;
   constexpr int LPT = kRowBytes / 16;        // lanes per token
   constexpr int EPL = INT4 ? 32 : 16;        // channels per lane
   constexpr int TPS = 64 / LPT;              // tokens per wavefront load
-  constexpr int NSUB = kWaveTokens / TPS;    // loads per 256 tokens
+  constexpr int NSUB = kWaveTokens / TPS;    // loads per lane per 256 tokens
+  constexpr int NG = NSUB / kGroup;
   constexpr float kOff = INT4 ? 8.0f : 128.0f;
+  static_assert(NSUB % kGroup == 0, "load groups");
   __shared__ float red_m[kDecWaves], red_l[kDecWaves];
   __shared__ float red_o[kDecWaves][D];
 
@@ -106,18 +148,22 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
   const int kvh = h / p.group;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tg = lane / LPT;          // token within a load
-  const int dc = lane % LPT;          // channel chunk
+  const int tg = lane / LPT;  // token within a load
+  const int dc = lane % LPT;  // channel chunk
   const int d0 = dc * EPL;
 
+  // This lane's query channels: fp16 pairs for the dot2 path, else floats.
+  const long qoff = (long)b * p.q_batch + (long)h * p.q_head;
+  f16x2 qh[EPL / 2];
   float qf[EPL];
   float qsum = 0.0f;
-  const long qoff = (long)b * p.q_batch + (long)h * p.q_head;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     qf[e] = load_q(p.q, qoff + d0 + e, p.q_dtype);
     qsum += qf[e];
   }
+#pragma unroll
+  for (int e = 0; e < EPL / 2; ++e) qh[e] = (f16x2){(_Float16)qf[2 * e], (_Float16)qf[2 * e + 1]};
 
   const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
   const uint8_t* kp = p.k + cbase + dc * 16;
@@ -126,67 +172,127 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
 
   const int t_begin = split * kDecodeChunk + wave * kWaveTokens;
   const int t_end = min(t_begin + kWaveTokens, L);
+  const int t_last = t_end - 1;
 
-  float m_run = -INFINITY, l_run = 0.0f, wsum = 0.0f;
+  float m_blk = -INFINITY, l_blk = 0.0f, wsum = 0.0f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
+  float sk_blk = 1.0f, sv_blk = 1.0f;
 
   if (t_begin < t_end) {
+    if constexpr (BLOCK_SCALE) {
+      sk_blk = load_scale(p.ks, sbase + t_begin / p.kv_block, p.kv_scale_f16);
+      sv_blk = load_scale(p.vs, sbase + t_begin / p.kv_block, p.kv_scale_f16);
+    }
+    const float csk = p.scale_log2 * sk_blk;
+    // ---- scores: sc[j] for token t_begin + j*TPS + tg (log2 units) ----
     float sc[NSUB];
-    float mblk = -INFINITY;
+    uint4 kw[2][kGroup];
+    auto kload = [&](uint4* dst, int g) {
 #pragma unroll
-    for (int j = 0; j < NSUB; ++j) {
-      const int t = t_begin + j * TPS + tg;
-      const bool ok = t < t_end;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) w = *(const uint4*)(kp + (long)t * p.c_row);
-      float f[EPL];
-      chunk_to_f32<INT4>(w, f);
-      float acc = -kOff * qsum;
+      for (int i = 0; i < kGroup; ++i) {
+        const int t = min(t_begin + (g * kGroup + i) * TPS + tg, t_last);
+        dst[i] = *(const uint4*)(kp + (long)t * p.c_row);
+      }
+    };
+    kload(kw[0], 0);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc = __builtin_fmaf(qf[e], f[e], acc);
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) kload(kw[(g + 1) & 1], g + 1);
 #pragma unroll
-      for (int off = LPT / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-      const float sk = ok ? load_scale(p.ks, sbase + t / p.kv_block, p.kv_scale_f16) : 0.0f;
-      sc[j] = ok ? acc * sk * p.scale_log2 : -INFINITY;
-      mblk = fmaxf(mblk, sc[j]);
+      for (int i = 0; i < kGroup; ++i) {
+        const int j = g * kGroup + i;
+        const uint4 w = kw[g & 1][i];
+        float acc;
+        if constexpr (QF16) {
+          f16x2 kh[EPL / 2];
+          if constexpr (INT4) {
+            i4x8_to_h(w.x, kh + 0);
+            i4x8_to_h(w.y, kh + 4);
+            i4x8_to_h(w.z, kh + 8);
+            i4x8_to_h(w.w, kh + 12);
+          } else {
+            i8x4_to_h(w.x, kh[0], kh[1]);
+            i8x4_to_h(w.y, kh[2], kh[3]);
+            i8x4_to_h(w.z, kh[4], kh[5]);
+            i8x4_to_h(w.w, kh[6], kh[7]);
+          }
+          float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+          for (int e = 0; e < EPL / 2; e += 2) {
+            a0 = __builtin_amdgcn_fdot2(qh[e], kh[e], a0, false);
+            a1 = __builtin_amdgcn_fdot2(qh[e + 1], kh[e + 1], a1, false);
+          }
+          acc = a0 + a1;
+        } else {
+          float f[EPL];
+          chunk_to_f32<INT4>(w, f);
+          acc = -kOff * qsum;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc = __builtin_fmaf(qf[e], f[e], acc);
+        }
+        acc = lane_group_sum<LPT>(acc);
+        const int t = t_begin + j * TPS + tg;
+        float c = csk;
+        if constexpr (!BLOCK_SCALE) {
+          c = p.scale_log2 * load_scale(p.ks, sbase + min(t, t_last) / p.kv_block, p.kv_scale_f16);
+        }
+        sc[j] = t < t_end ? acc * c : -INFINITY;
+        m_blk = fmaxf(m_blk, sc[j]);
+      }
     }
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) mblk = fmaxf(mblk, __shfl_xor(mblk, off));
-    m_run = mblk;  // first and only block of this wavefront
+    for (int off = LPT; off < 64; off <<= 1) m_blk = fmaxf(m_blk, __shfl_xor(m_blk, off));
+
+    // ---- values ----
+    uint4 vw[2][kGroup];
+    auto vload = [&](uint4* dst, int g) {
 #pragma unroll
-    for (int j = 0; j < NSUB; ++j) {
-      const int t = t_begin + j * TPS + tg;
-      const bool ok = t < t_end;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (ok) w = *(const uint4*)(vp + (long)t * p.c_row);
-      const float pr = ok ? exp2f(sc[j] - m_run) : 0.0f;
-      l_run += pr;
-      const float sv = ok ? load_scale(p.vs, sbase + t / p.kv_block, p.kv_scale_f16) : 0.0f;
-      const float wt = pr * sv;
-      wsum += wt;
-      float f[EPL];
-      chunk_to_f32<INT4>(w, f);
+      for (int i = 0; i < kGroup; ++i) {
+        const int t = min(t_begin + (g * kGroup + i) * TPS + tg, t_last);
+        dst[i] = *(const uint4*)(vp + (long)t * p.c_row);
+      }
+    };
+    vload(vw[0], 0);
+    float lp[2] = {0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = __builtin_fmaf(wt, f[e], o[e]);
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) vload(vw[(g + 1) & 1], g + 1);
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const int j = g * kGroup + i;
+        const float pr = __builtin_amdgcn_exp2f(sc[j] - m_blk);  // 0 for masked tokens
+        lp[i & 1] += pr;
+        float wt = pr;
+        if constexpr (!BLOCK_SCALE) {
+          const int t = min(t_begin + j * TPS + tg, t_last);
+          wt *= load_scale(p.vs, sbase + t / p.kv_block, p.kv_scale_f16);
+        }
+        wsum += wt;
+        float f[EPL];
+        chunk_to_f32<INT4>(vw[g & 1][i], f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = __builtin_fmaf(wt, f[e], o[e]);
+      }
     }
+    l_blk = lp[0] + lp[1];
     // Sum the token groups: lanes with the same channel chunk.
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
-      l_run += __shfl_xor(l_run, off);
+      l_blk += __shfl_xor(l_blk, off);
       wsum += __shfl_xor(wsum, off);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], off);
     }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] -= kOff * wsum;
+    for (int e = 0; e < EPL; ++e) o[e] = (o[e] - kOff * wsum) * sv_blk;
   }
 
   // Merge the wavefronts of the workgroup.
   if (lane == 0) {
-    red_m[wave] = m_run;
-    red_l[wave] = l_run;
+    red_m[wave] = m_blk;
+    red_l[wave] = l_blk;
   }
   if (lane < LPT) {
 #pragma unroll
@@ -201,7 +307,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
   float Lsum = 0.0f;
 #pragma unroll
   for (int w = 0; w < kDecWaves; ++w) {
-    c[w] = red_m[w] == -INFINITY ? 0.0f : exp2f(red_m[w] - M);
+    c[w] = red_m[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(red_m[w] - M);
     Lsum += red_l[w] * c[w];
   }
   const long obase = (long)b * p.q_batch + (long)h * p.q_head;
@@ -246,7 +352,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecParams p) {
   for (int s = 0; s < nsplit; ++s) {
     const float* ps = part + s * (D + 2);
     const float ms = ps[D];
-    const float c = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+    const float c = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
     Lsum += ps[D + 1] * c;
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) acc[i] += ps[threadIdx.x + 64 * i] * c;
@@ -257,9 +363,9 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecParams p) {
   for (int i = 0; i < D / 64; ++i) store_out(p.out, obase + threadIdx.x + 64 * i, acc[i] * inv, p.out_dtype);
 }
 
-template <int D, bool INT4>
-hipError_t launch_dec(const DecParams& p, int B, hipStream_t st) {
-  decode_split_kernel<D, INT4><<<dim3(p.max_splits, p.Hq, B), 64 * kDecWaves, 0, st>>>(p);
+template <int D, bool INT4, bool QF16, bool BS>
+hipError_t launch_dec4(const DecParams& p, int B, hipStream_t st) {
+  decode_split_kernel<D, INT4, QF16, BS><<<dim3(p.max_splits, p.Hq, B), 64 * kDecWaves, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.max_splits > 1) {
@@ -267,6 +373,14 @@ hipError_t launch_dec(const DecParams& p, int B, hipStream_t st) {
     e = hipGetLastError();
   }
   return e;
+}
+
+template <int D, bool INT4>
+hipError_t launch_dec(const DecParams& p, int B, hipStream_t st) {
+  const bool qf16 = p.q_dtype == QFA_F16;
+  const bool bs = p.kv_block % kWaveTokens == 0;
+  if (qf16) return bs ? launch_dec4<D, INT4, true, true>(p, B, st) : launch_dec4<D, INT4, true, false>(p, B, st);
+  return bs ? launch_dec4<D, INT4, false, true>(p, B, st) : launch_dec4<D, INT4, false, false>(p, B, st);
 }
 
 }  // namespace

@@ -379,22 +379,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       const float ck = cq * vs.ksc[0];
       const float sv_t = vs.vsc[0];
       float x[2][16];
-      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[kb][r] = (float)sacc[kb][r];
+      // Tile max as four independent chains (short dependency depth).
+      float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, key_of(kb, r) > lim ? -INFINITY : x[kb][r]);
+          for (int r = 0; r < 16; ++r)
+            mc[r & 3] = fmaxf(mc[r & 3], key_of(kb, r) > lim ? -INFINITY : x[kb][r]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
+          for (int r = 0; r < 16; ++r) mc[r & 3] = fmaxf(mc[r & 3], x[kb][r]);
       }
+      const float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
       // Max of this lane half; the row max over both halves is only formed when
       // some row needs a rescale (or the V scale changes), which is rare.
       const float mt = mx == -INFINITY ? -INFINITY : mx * ck;  // ck >= 0
@@ -412,6 +415,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
       }
       const float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
       const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -424,14 +428,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
           }
           const f16x2 h2 = {(_Float16)__builtin_amdgcn_exp2f(a0),
                             (_Float16)__builtin_amdgcn_exp2f(a1)};
-          l_run = __builtin_amdgcn_fdot2(h2, one, l_run, false);
+          ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2(h2, one, ls[(r >> 1) & 3], false);
           pb[kb][r >> 3][r & 7] = h2[0];
           pb[kb][r >> 3][(r & 7) + 1] = h2[1];
         }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     } else {
       // Per-key scales (e.g. INT4 K/V with one scale per token).
       float x[2][16];
-      float mt = -INFINITY;
+      float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -443,9 +448,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
             float xv = (float)sacc[kb][r] * (cq * s4[i]);
             if (need_mask) xv = key_of(kb, r) > lim ? -INFINITY : xv;
             x[kb][r] = xv;
-            mt = fmaxf(mt, xv);
+            mc[i] = fmaxf(mc[i], xv);
           }
         }
+      const float mt = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
       if (__any(mt > m_run + kRescaleSlack)) {
         const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
         const float m_new = mrow > m_run + kRescaleSlack ? fmaxf(m_run, mrow) : m_run;
@@ -456,6 +462,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         m_run = m_new;
       }
       const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
+      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -465,10 +472,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * rg + i;
             const float pr = __builtin_amdgcn_exp2f(x[kb][r] - msub);
-            l_run += pr;
+            ls[i] += pr;
             pb[kb][r >> 3][r & 7] = (_Float16)(pr * v4[i]);
           }
         }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
