@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -191,6 +193,15 @@ def main():
                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+    if args.copy_probe:
+        # A plain elementwise copy of known size: reads 1 GiB (fp32), writes 512 MiB (fp16).
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty(1 << 28, dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 3 fp32->fp16 copies, 1 GiB read + 512 MiB written each")
+        del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host")
         rec["cpu_baseline"] = cpu_baseline(wl)
