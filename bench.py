@@ -1,6 +1,6 @@
 """Benchmark: block-quantized FlashAttention on one MI355X.
 
-One step = quantize Q, K and V (qfa_block_quant x3) and run the INT8 causal
+One step = quantize Q, K and V (one qfa_block_quant_multi call) and run the INT8 causal
 attention forward (qfa_fwd) on the LLaMA-2-7B head shape workload
 ``int8_causal_h32_s4096`` (B=1, H=32, S=4096, D=128, fp16 inputs with four
 outlier K channels), inputs resident in HBM. ``value`` is the attention's
@@ -44,10 +44,14 @@ def bench_prefill(torch, qfa, wl, steps, warmup):
     vc, vs = qfa.block_quant(v, w.kv_block, w.v_qtype, sdt)
     out = torch.empty_like(q)
 
+    jobs = [dict(x=q, block_rows=w.q_block, qtype=w.q_qtype, scale_dtype=sdt, codes=qc, scales=qs),
+            dict(x=k, block_rows=w.kv_block, qtype=w.k_qtype, scale_dtype=sdt, codes=kc, scales=ks),
+            dict(x=v, block_rows=w.kv_block, qtype=w.v_qtype, scale_dtype=sdt, codes=vc, scales=vs)]
+
     def step(ev=None):
-        qfa.block_quant(q, w.q_block, w.q_qtype, sdt, codes=qc, scales=qs)
-        qfa.block_quant(k, w.kv_block, w.k_qtype, sdt, codes=kc, scales=ks)
-        qfa.block_quant(v, w.kv_block, w.v_qtype, sdt, codes=vc, scales=vs)
+        if ev is not None:
+            ev[2].record()
+        qfa.block_quant_multi(jobs)
         if ev is not None:
             ev[0].record()
         qfa.fwd(qc, qs, kc, ks, vc, vs, q_qtype=w.q_qtype, k_qtype=w.k_qtype, v_qtype=w.v_qtype,
@@ -59,15 +63,16 @@ def bench_prefill(torch, qfa, wl, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [_events(torch) for _ in range(steps)]
+    evs = [_events(torch) + (torch.cuda.Event(enable_timing=True),) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    quant_ms = sum(c.elapsed_time(a) for a, b, c in evs) / steps
     ops = w.attention_ops()
-    return w, wall, fwd_ms, ops
+    return w, wall, fwd_ms, quant_ms, ops
 
 
 def bench_decode(torch, qfa, wl, steps, warmup):
@@ -176,11 +181,16 @@ def main():
     import qfa_workloads as wl
 
     log(f"prefill: {wl.INT8_CAUSAL.name}, warmup {args.warmup}, steps {args.steps}")
-    w, wall, fwd_ms, ops = bench_prefill(torch, qfa, wl, args.steps, args.warmup)
+    w, wall, fwd_ms, quant_ms, ops = bench_prefill(torch, qfa, wl, args.steps, args.warmup)
     ms_step = wall * 1e3 / args.steps
+    # Algorithmic bytes of the three quantizer calls: fp16 inputs read once,
+    # int8 codes and fp32 scales written once.
+    nel = w.B * w.Hq * w.S * w.D
+    qbytes = 3 * nel * 2 + 3 * nel + 4 * (w.B * w.Hq * (w.S // w.q_block) + 2 * w.B * w.Hkv * (w.S // w.kv_block))
     value = ops / (ms_step * 1e-3) / 1e12
     achieved = ops / (fwd_ms * 1e-3) / 1e12
-    log(f"prefill step {ms_step:.3f} ms, forward kernel {fwd_ms:.3f} ms, {achieved:.1f} TOPS")
+    log(f"prefill step {ms_step:.3f} ms, forward kernel {fwd_ms:.3f} ms, {achieved:.1f} TOPS, "
+        f"quantize Q/K/V {quant_ms:.3f} ms")
     rec = {
         "metric": "quantized FA prefill TOPS + decode KV GB/s, % of MI355X MFMA/HBM peak",
         "value": round(value, 3),
@@ -196,13 +206,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.Hq, "S": w.S, "D": w.D,
                    "causal": w.causal, "qtype": "int8", "q_block": w.q_block,
-                   "kv_block": w.kv_block, "step": "block_quant(Q,K,V) + fwd"},
+                   "kv_block": w.kv_block, "step": "block_quant_multi(Q,K,V) + fwd"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": profiled_traffic("fwd_int8_causal_h32_s4096.md",
                                                  "block_quantized_flashattention_amd/csrc/prefill.hip"),
                      "kernel": "fwd_kernel<128,int8,causal>",
                      "kernel_ms": round(fwd_ms, 4)},
+        "quantize": {"ms": round(quant_ms, 4), "bytes": qbytes,
+                     "GB/s": round(qbytes / (quant_ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
     if not args.no_decode:
         log(f"decode: {wl.DECODE.name}")

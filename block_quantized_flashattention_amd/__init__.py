@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.qfa_status_string.restype = ctypes.c_char_p
     L.qfa_block_quant.argtypes = [vp, i, i, i, i, i, i, i, i, vp, vp, i, vp]
     L.qfa_block_quant.restype = i
+    L.qfa_block_quant_multi.argtypes = [ctypes.POINTER(QuantJob), i, vp]
+    L.qfa_block_quant_multi.restype = i
     L.qfa_fwd.argtypes = [vp, vp, i, i, i, vp, vp, i, vp, vp, i, i, i,
                           i, i, i, i, i, i, i, i, f, vp, i, vp]
     L.qfa_fwd.restype = i
@@ -92,6 +94,53 @@ def _dev(t: torch.Tensor, name: str):
 
 def code_dtype(qtype: str) -> torch.dtype:
     return torch.int8 if qtype == "int8" else torch.uint8
+
+
+class QuantJob(ctypes.Structure):
+    """Mirror of qfa_quant_job (include/qfa.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int), ("B", ctypes.c_int),
+                ("N", ctypes.c_int), ("S", ctypes.c_int), ("D", ctypes.c_int),
+                ("layout", ctypes.c_int), ("block_rows", ctypes.c_int), ("qtype", ctypes.c_int),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("scale_dtype", ctypes.c_int)]
+
+
+def _quant_outputs(x, block_rows, qtype, scale_dtype, layout, codes, scales):
+    _dev(x, "x")
+    if layout == "bnsd":
+        B, N, S, D = x.shape
+    else:
+        B, S, N, D = x.shape
+    cshape = list(x.shape[:-1]) + [D // 2 if qtype == "int4" else D]
+    if codes is None:
+        codes = torch.empty(cshape, dtype=code_dtype(qtype), device=x.device)
+    if scales is None:
+        scales = torch.empty(B, N, -(-S // block_rows), dtype=scale_dtype, device=x.device)
+    _dev(codes, "codes")
+    _dev(scales, "scales")
+    job = QuantJob(_ptr(x), FLOATS[x.dtype], B, N, S, D, LAYOUTS[layout], block_rows,
+                   QTYPES[qtype], _ptr(codes), _ptr(scales), FLOATS[scales.dtype])
+    return job, codes, scales
+
+
+def block_quant_multi(jobs, stream=None):
+    """Quantize several tensors in shared launches; returns [(codes, scales), ...].
+
+    Each job is a dict with the arguments of ``block_quant``: x, block_rows,
+    qtype, and optionally scale_dtype (float32), layout ("bnsd"), codes, scales.
+    Results are bit-identical to one ``block_quant`` call per job.
+    """
+    descs, outs = [], []
+    for j in jobs:
+        job, codes, scales = _quant_outputs(j["x"], j["block_rows"], j["qtype"],
+                                            j.get("scale_dtype", torch.float32),
+                                            j.get("layout", "bnsd"), j.get("codes"),
+                                            j.get("scales"))
+        descs.append(job)
+        outs.append((codes, scales))
+    arr = (QuantJob * max(len(descs), 1))(*descs)
+    _check("qfa_block_quant_multi", lib().qfa_block_quant_multi(arr, len(descs), _stream(stream)))
+    return outs
 
 
 def block_quant(x: torch.Tensor, block_rows: int, qtype: str, scale_dtype=torch.float32,

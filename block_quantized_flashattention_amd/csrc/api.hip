@@ -15,6 +15,24 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? QFA_OK : QFA_ERR_HIP; }
 
+// Validation shared by the single and multi-tensor quantizer entry points.
+int check_quant(const void* x, int x_dtype, int B, int N, int S, int D, int layout,
+                int block_rows, int qtype, const void* codes, const void* scales,
+                int scale_dtype) {
+  if (!valid_float(x_dtype) || !valid_layout(layout) || !valid_qtype(qtype) ||
+      (scale_dtype != QFA_F32 && scale_dtype != QFA_F16))
+    return QFA_ERR_ENUM;
+  if (B < 0 || N < 0 || S < 0 || D < 8 || D > 1024 || D % 8 != 0 || block_rows < 1)
+    return QFA_ERR_SHAPE;
+  if ((long)B * N * S == 0) return QFA_OK;
+  if (!x || !codes || !scales) return QFA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, qtype == QFA_INT4 ? 4 : 8) ||
+      !aligned(scales, scale_dtype == QFA_F16 ? 2 : 4))
+    return QFA_ERR_UNSUPPORTED;
+  return QFA_OK;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -34,21 +52,34 @@ const char* qfa_status_string(int status) {
   }
 }
 
+
 int qfa_block_quant(const void* x, int x_dtype, int B, int N, int S, int D, int layout,
                     int block_rows, int qtype, void* codes, void* scales, int scale_dtype,
                     void* stream) {
-  if (!valid_float(x_dtype) || !valid_layout(layout) || !valid_qtype(qtype) ||
-      (scale_dtype != QFA_F32 && scale_dtype != QFA_F16))
-    return QFA_ERR_ENUM;
-  if (B < 0 || N < 0 || S < 0 || D < 8 || D > 1024 || D % 8 != 0 || block_rows < 1)
-    return QFA_ERR_SHAPE;
-  if ((long)B * N * S == 0) return QFA_OK;
-  if (!x || !codes || !scales) return QFA_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(codes, qtype == QFA_INT4 ? 4 : 8) ||
-      !aligned(scales, scale_dtype == QFA_F16 ? 2 : 4))
-    return QFA_ERR_UNSUPPORTED;
+  const int st = check_quant(x, x_dtype, B, N, S, D, layout, block_rows, qtype, codes, scales,
+                             scale_dtype);
+  if (st != QFA_OK || (long)B * N * S == 0) return st;
   qfa::QuantArgs a{x, x_dtype, B, N, S, D, layout, block_rows, qtype, codes, scales, scale_dtype};
   return from_hip(qfa::launch_block_quant(a, (hipStream_t)stream));
+}
+
+int qfa_block_quant_multi(const qfa_quant_job* jobs, int njobs, void* stream) {
+  if (njobs < 0 || njobs > QFA_MAX_QUANT_JOBS) return QFA_ERR_SHAPE;
+  if (njobs == 0) return QFA_OK;
+  if (!jobs) return QFA_ERR_NULL;
+  qfa::QuantArgs a[QFA_MAX_QUANT_JOBS];
+  int n = 0;
+  for (int i = 0; i < njobs; ++i) {
+    const qfa_quant_job& j = jobs[i];
+    const int st = check_quant(j.x, j.x_dtype, j.B, j.N, j.S, j.D, j.layout, j.block_rows,
+                               j.qtype, j.codes, j.scales, j.scale_dtype);
+    if (st != QFA_OK) return st;
+    if ((long)j.B * j.N * j.S == 0) continue;
+    a[n++] = qfa::QuantArgs{j.x, j.x_dtype, j.B, j.N, j.S, j.D, j.layout, j.block_rows, j.qtype,
+                            j.codes, j.scales, j.scale_dtype};
+  }
+  if (n == 0) return QFA_OK;
+  return from_hip(qfa::launch_block_quant_multi(a, n, (hipStream_t)stream));
 }
 
 int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,

@@ -24,6 +24,8 @@ struct QuantArgs {
 };
 
 hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream);
+// Several tensors, grouped by input and code type into shared launches.
+hipError_t launch_block_quant_multi(const QuantArgs* a, int n, hipStream_t stream);
 
 struct FwdArgs {
   const void* q;

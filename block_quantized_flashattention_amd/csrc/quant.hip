@@ -8,10 +8,13 @@
 //   code = clamp(rne(fl32(x / s)))  (INT8 / INT4), e4m3fn(rne(clamp(x / s)))  (FP8)
 //
 // Design (HBM-bound: one read of x, one write of codes):
-//   * A team of T = 2^k threads (16..256) owns one block; each thread holds
-//     up to 16 chunks of 8 consecutive channels in registers, so x is read
-//     from HBM once. Larger blocks take a two-pass path (the second read
-//     mostly hits L2).
+//   * A team of T = 2^k threads (up to 1024) owns one block; each thread
+//     holds about four (at most 16) chunks of 8 consecutive channels in
+//     registers, so x is read from HBM once and many blocks are in flight per
+//     CU. Larger blocks take a two-pass path (the second read mostly hits L2).
+//   * Several tensors (Q, K, V) can share one launch, the workgroups of each
+//     in a contiguous range, so the loads of one block overlap the reduction
+//     and stores of others across the whole chip.
 //   * amax is reduced on the raw bit patterns (|x| ordered as an unsigned
 //     integer), across the team with lane shuffles and, for teams wider than
 //     a wavefront, through LDS.
@@ -24,6 +27,8 @@
 //     reach a nonzero code; other scales take the plain IEEE division.
 //   * FP8 codes use the gfx950 converter to OCP e4m3 (nearest-even) after
 //     clamping to +-448.
+#include <algorithm>
+
 #include "qfa_device.h"
 #include "qfa_launch.h"
 
@@ -191,15 +196,15 @@ __device__ __forceinline__ uint32_t team_max(uint32_t m, int team_log2, uint32_t
   return r;
 }
 
+// Blocks of workgroup `wg` of one tensor (blockDim / 2^team_log2 blocks per workgroup).
 template <int IN, int QT, int CH, bool TWO_PASS>
-__global__ __launch_bounds__(256) void block_quant_kernel(QuantParams p) {
+__device__ __forceinline__ void quant_blocks(const QuantParams& p, long wg, uint32_t* lds) {
   using I = In<IN>;
   using E = Enc<QT>;
-  __shared__ uint32_t lds[4];
   const int T = 1 << p.team_log2;
   const int team = threadIdx.x >> p.team_log2;
   const int lt = threadIdx.x & (T - 1);
-  const long gb = (long)blockIdx.x * (256 >> p.team_log2) + team;
+  const long gb = wg * ((int)blockDim.x >> p.team_log2) + team;
   const bool active = gb < p.total_blocks;
   const long g = active ? gb : 0;
   const int r = (int)(g % p.nblk);
@@ -284,31 +289,75 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QuantParams p) {
   }
 }
 
+constexpr int kMaxTeam = 1024;     // threads per block team (and per workgroup)
+constexpr int kTargetChunks = 4;   // chunks of 8 channels per thread, when the team allows
+
+// Up to kMaxJobs tensors of one input type and code type per launch: the
+// workgroups of job j are [start[j], start[j+1]). Launching several tensors
+// together (Q, K and V) gives the chip enough blocks that one workgroup's
+// loads overlap another's reduction and stores.
+constexpr int kMaxJobs = 4;
+struct MultiParams {
+  QuantParams job[kMaxJobs];
+  long start[kMaxJobs];
+  int njobs;
+};
+
+template <int IN, int QT, int CH, bool TWO_PASS>
+__global__ __launch_bounds__(kMaxTeam) void block_quant_kernel(MultiParams mp) {
+  __shared__ uint32_t lds[kMaxTeam / 64];
+  const long bid = blockIdx.x;
+  // Job of this workgroup, selected with uniform (scalar) moves only.
+  QuantParams p = mp.job[0];
+  long wg = bid;
+#pragma unroll
+  for (int j = 1; j < kMaxJobs; ++j) {
+    if (j < mp.njobs && bid >= mp.start[j]) {
+      p = mp.job[j];
+      wg = bid - mp.start[j];
+    }
+  }
+  quant_blocks<IN, QT, CH, TWO_PASS>(p, wg, lds);
+}
+
+// Registers per thread: the single-pass path keeps up to 16 chunks of 8
+// channels (8 for fp32 inputs); the chunk count is rounded up to a power of
+// two. 0: the two-pass path.
+int chunk_class(int chunks, int x_dtype) {
+  if (chunks > (x_dtype == QFA_F32 ? 8 : 16)) return 0;
+  int c = 1;
+  while (c < chunks) c <<= 1;
+  return c;
+}
+
 template <int IN, int QT>
-hipError_t launch_typed(const QuantParams& p, long grid, hipStream_t stream) {
-  const int ch = p.chunks;
-  if (ch <= 1) block_quant_kernel<IN, QT, 1, false><<<grid, 256, 0, stream>>>(p);
-  else if (ch <= 2) block_quant_kernel<IN, QT, 2, false><<<grid, 256, 0, stream>>>(p);
-  else if (ch <= 4) block_quant_kernel<IN, QT, 4, false><<<grid, 256, 0, stream>>>(p);
-  else if (ch <= 8) block_quant_kernel<IN, QT, 8, false><<<grid, 256, 0, stream>>>(p);
-  else if (ch <= 16) block_quant_kernel<IN, QT, 16, false><<<grid, 256, 0, stream>>>(p);
-  else block_quant_kernel<IN, QT, 1, true><<<grid, 256, 0, stream>>>(p);
+hipError_t launch_typed(const MultiParams& mp, int cls, long grid, int threads, hipStream_t stream) {
+  switch (cls) {
+    case 1: block_quant_kernel<IN, QT, 1, false><<<grid, threads, 0, stream>>>(mp); break;
+    case 2: block_quant_kernel<IN, QT, 2, false><<<grid, threads, 0, stream>>>(mp); break;
+    case 4: block_quant_kernel<IN, QT, 4, false><<<grid, threads, 0, stream>>>(mp); break;
+    case 8: block_quant_kernel<IN, QT, 8, false><<<grid, threads, 0, stream>>>(mp); break;
+    case 16:
+      if constexpr (IN != QFA_F32) block_quant_kernel<IN, QT, 16, false><<<grid, threads, 0, stream>>>(mp);
+      break;
+    default: block_quant_kernel<IN, QT, 1, true><<<grid, threads, 0, stream>>>(mp); break;
+  }
   return hipGetLastError();
 }
 
 template <int IN>
-hipError_t launch_in(const QuantParams& p, int qtype, long grid, hipStream_t stream) {
+hipError_t launch_in(const MultiParams& mp, int qtype, int cls, long grid, int threads,
+                     hipStream_t stream) {
   switch (qtype) {
-    case QFA_INT8: return launch_typed<IN, QFA_INT8>(p, grid, stream);
-    case QFA_FP8_E4M3: return launch_typed<IN, QFA_FP8_E4M3>(p, grid, stream);
-    default: return launch_typed<IN, QFA_INT4>(p, grid, stream);
+    case QFA_INT8: return launch_typed<IN, QFA_INT8>(mp, cls, grid, threads, stream);
+    case QFA_FP8_E4M3: return launch_typed<IN, QFA_FP8_E4M3>(mp, cls, grid, threads, stream);
+    default: return launch_typed<IN, QFA_INT4>(mp, cls, grid, threads, stream);
   }
 }
 
-}  // namespace
+// Kernel parameters and workgroup count of one tensor.
+long prepare(const QuantArgs& a, QuantParams& p) {
 
-hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream) {
-  QuantParams p;
   p.x = (const char*)a.x;
   p.codes = (char*)a.codes;
   p.scales = a.scales;
@@ -332,24 +381,68 @@ hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream) {
   p.x_batch = (long)a.N * a.S * a.D;
   p.c_batch = (long)a.N * a.S * cD;
   p.scale_f16 = a.scale_dtype == QFA_F16;
-  // Team size: enough threads that each holds at most 16 chunks, capped at 256.
+  // Team size: the power of two giving each thread about kTargetChunks
+  // chunks (more threads in flight per block), capped at kMaxTeam.
   const long chunks_total = ((long)p.R * a.D) / 8;
+  const long want = (chunks_total + kTargetChunks - 1) / kTargetChunks;
   int tl = 0;
-  while ((1L << tl) < chunks_total && tl < 8) ++tl;
+  while ((1L << tl) < want && (1L << tl) < kMaxTeam) ++tl;
   p.team_log2 = tl;
   const long T = 1L << tl;
   p.chunks = (int)((chunks_total + T - 1) / T);
   p.step_rows = (int)((T * 8) / a.D);
   p.step_cols = (int)((T * 8) % a.D);
   p.total_blocks = (long)a.B * a.N * p.nblk;
-  const long teams_per_wg = 256 / T;
-  const long grid = (p.total_blocks + teams_per_wg - 1) / teams_per_wg;
-  if (grid == 0) return hipSuccess;
-  switch (a.x_dtype) {
-    case QFA_F32: return launch_in<QFA_F32>(p, a.qtype, grid, stream);
-    case QFA_F16: return launch_in<QFA_F16>(p, a.qtype, grid, stream);
-    default: return launch_in<QFA_BF16>(p, a.qtype, grid, stream);
+  return p.total_blocks;
+}
+
+}  // namespace
+
+hipError_t launch_block_quant_multi(const QuantArgs* a, int n, hipStream_t stream) {
+  // Group the tensors by (input type, code type, single or two-pass) in order
+  // of first appearance; each group goes out in launches of up to kMaxJobs.
+  if (n > 64) return hipErrorInvalidValue;
+  QuantParams prm[64];
+  bool done[64];
+  for (int i = 0; i < n; ++i) done[i] = prepare(a[i], prm[i]) == 0;
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    const int xd = a[i].x_dtype;
+    const bool two_pass = chunk_class(prm[i].chunks, xd) == 0;
+    int sel[kMaxJobs], ns = 0, cls = 1, threads = 256;
+    for (int j = i; j < n && ns < kMaxJobs; ++j) {
+      if (done[j] || a[j].x_dtype != a[i].x_dtype || a[j].qtype != a[i].qtype ||
+          (chunk_class(prm[j].chunks, xd) == 0) != two_pass)
+        continue;
+      sel[ns++] = j;
+      done[j] = true;
+      cls = two_pass ? 0 : std::max(cls, chunk_class(prm[j].chunks, xd));
+      threads = std::max(threads, 1 << prm[j].team_log2);
+    }
+    MultiParams mp{};
+    long grid = 0;
+    for (int k = 0; k < ns; ++k) {
+      const QuantParams& pj = prm[sel[k]];
+      const long teams_per_wg = threads >> pj.team_log2;
+      mp.job[k] = pj;
+      mp.start[k] = grid;
+      grid += (pj.total_blocks + teams_per_wg - 1) / teams_per_wg;
+    }
+    mp.njobs = ns;
+    if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
+    hipError_t e;
+    switch (a[i].x_dtype) {
+      case QFA_F32: e = launch_in<QFA_F32>(mp, a[i].qtype, cls, grid, threads, stream); break;
+      case QFA_F16: e = launch_in<QFA_F16>(mp, a[i].qtype, cls, grid, threads, stream); break;
+      default: e = launch_in<QFA_BF16>(mp, a[i].qtype, cls, grid, threads, stream); break;
+    }
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
+}
+
+hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream) {
+  return launch_block_quant_multi(&a, 1, stream);
 }
 
 }  // namespace qfa

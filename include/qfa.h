@@ -91,6 +91,37 @@ QFA_API int qfa_block_quant(const void* x, int x_dtype, int B, int N, int S, int
                     void* stream);
 
 /*
+ * qfa_block_quant_multi -- qfa_block_quant on several tensors in as few
+ * launches as possible (the Q, K and V of one attention call).
+ *
+ * Same arithmetic as qfa_block_quant (see there): the codes and scales of
+ * every job are bit-identical to those of one qfa_block_quant call with the
+ * job's arguments. Jobs with the same x_dtype and qtype share one kernel
+ * launch (up to four per launch), which lets the blocks of one tensor
+ * overlap the loads of another.
+ *
+ *   jobs   host array of njobs descriptors (read during the call only).
+ *   njobs  0 <= njobs <= QFA_MAX_QUANT_JOBS.
+ * Every job is validated as by qfa_block_quant before anything is launched;
+ * the first failing job's status is returned and nothing runs. The output
+ * buffers of one job must not overlap the input or outputs of another.
+ */
+#define QFA_MAX_QUANT_JOBS 16
+typedef struct qfa_quant_job {
+  const void* x;     /* [B,N,S,D] or [B,S,N,D], x_dtype */
+  int x_dtype;
+  int B, N, S, D;
+  int layout;
+  int block_rows;
+  int qtype;
+  void* codes;       /* same layout; INT4: D/2 bytes per row */
+  void* scales;      /* [B, N, ceil(S/block_rows)], scale_dtype */
+  int scale_dtype;
+} qfa_quant_job;
+
+QFA_API int qfa_block_quant_multi(const qfa_quant_job* jobs, int njobs, void* stream);
+
+/*
  * qfa_fwd -- prefill attention forward run on block-quantized codes.
  *
  * Computes, for query row i of head h and key row j of KV head

@@ -22,8 +22,9 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = qfa.header_functions()
-    assert set(names) == {"qfa_version", "qfa_status_string", "qfa_block_quant", "qfa_fwd",
-                          "qfa_decode_workspace_bytes", "qfa_decode"}
+    assert set(names) == {"qfa_version", "qfa_status_string", "qfa_block_quant",
+                          "qfa_block_quant_multi", "qfa_fwd", "qfa_decode_workspace_bytes",
+                          "qfa_decode"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -56,6 +57,29 @@ def test_block_quant_validation(L):
     # empty tensors are valid and launch nothing, even with null pointers
     assert quant(L, S=0, x=None, codes=None, scales=None) == OK
     assert quant(L, B=0, x=None, codes=None, scales=None) == OK
+
+
+def job(x=P, dt=F16, B=1, N=2, S=300, D=128, layout=BNSD, R=128, qt=I8, codes=P, scales=P,
+        sdt=F32):
+    return qfa.QuantJob(x, dt, B, N, S, D, layout, R, qt, codes, scales, sdt)
+
+
+def multi(L, *jobs, n=None):
+    arr = (qfa.QuantJob * max(len(jobs), 1))(*jobs)
+    return L.qfa_block_quant_multi(arr, len(jobs) if n is None else n, None)
+
+
+def test_block_quant_multi_validation(L):
+    assert multi(L) == OK                      # no jobs: nothing to do
+    assert multi(L, job(), n=-1) == SHAPE
+    assert multi(L, job(), n=17) == SHAPE
+    assert L.qfa_block_quant_multi(None, 2, None) == NULL
+    # every job is checked before anything runs; the first failure is returned
+    assert multi(L, job(dt=7), job(x=None)) == ENUM
+    assert multi(L, job(S=0, x=None), job(D=12)) == SHAPE
+    assert multi(L, job(S=0, x=None), job(scales=None)) == NULL
+    assert multi(L, job(B=0, x=None, codes=None, scales=None)) == OK
+    assert multi(L, job(S=0, x=None), job(x=MIS)) == UNSUP
 
 
 def fwd(L, q=P, qs=P, qqt=I8, qb=128, qsd=F32, k=P, ks=P, kqt=I8, v=P, vs=P, vqt=I8, kb=256,

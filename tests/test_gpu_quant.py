@@ -34,7 +34,9 @@ CASES = [
     ("int4", 1, "f16", torch.float16, 1, 4, 37, 128, "bnsd"),
     ("int4", 1, "f16", torch.float16, 2, 3, 41, 128, "bsnd"),
     ("int4", 16, "f32", torch.float32, 1, 2, 50, 64, "bnsd"),
-    ("int8", 512, "f32", torch.float16, 1, 1, 1200, 128, "bnsd"),   # two-pass path
+    ("int8", 512, "f32", torch.float16, 1, 1, 1200, 128, "bnsd"),   # 1024-thread teams
+    ("int8", 1100, "f32", torch.float16, 1, 1, 2300, 128, "bnsd"),  # two-pass path
+    ("fp8", 600, "f16", torch.float32, 1, 1, 1300, 128, "bsnd"),    # two-pass (fp32 input)
     ("int8", 1, "f32", torch.float16, 1, 2, 9, 1024, "bnsd"),
 ]
 
@@ -131,3 +133,41 @@ def test_quant_full_size(w):
     quantize_both(q.cuda(), w.q_block, w.q_qtype, w.q_scale_dtype, "bnsd", "Q", qheads)
     quantize_both(k.cuda(), w.kv_block, w.k_qtype, w.kv_scale_dtype, "bnsd", "K")
     quantize_both(v.cuda(), w.kv_block, w.v_qtype, w.kv_scale_dtype, "bnsd", "V")
+
+
+def test_quant_multi_matches_oracle():
+    """Every case above in one qfa_block_quant_multi call (several groups of
+    input and code type, the two-pass path among them): each job's codes and
+    scales equal the oracle's byte for byte."""
+    say("quant multi: all small cases in one call")
+    jobs, xs = [], []
+    for qt, R, sdt, dt, B, N, S, D, layout in CASES:
+        x = _x((B, N, S, D), dt, seed=S * 7 + D + 1, zero=(0, N - 1, slice(0, R)))
+        if layout == "bsnd":
+            x = x.transpose(1, 2).contiguous()
+        xs.append((x, qt, R, sdt, layout))
+        jobs.append(dict(x=x.cuda(), block_rows=R, qtype=qt,
+                         scale_dtype=torch.float16 if sdt == "f16" else torch.float32,
+                         layout=layout))
+    outs = qfa.block_quant_multi(jobs)
+    torch.cuda.synchronize()
+    for (x, qt, R, sdt, layout), (c, s) in zip(xs, outs):
+        rc, rs = oracle.block_quant(x, R, qt, sdt, layout)
+        assert_codes_equal(c, s, rc, rs, f"multi {qt} R={R} {layout}")
+
+
+def test_quant_multi_qkv_full_size():
+    """The Q, K and V of the INT8 causal workload in one call, equal to three
+    single calls byte for byte (those are checked against the oracle above)."""
+    w = wl.INT8_CAUSAL
+    say(f"quant multi full size {w.name}")
+    q, k, v = wl.make_prefill_inputs(w, device="cuda")
+    outs = qfa.block_quant_multi([dict(x=q, block_rows=w.q_block, qtype=w.q_qtype),
+                                  dict(x=k, block_rows=w.kv_block, qtype=w.k_qtype),
+                                  dict(x=v, block_rows=w.kv_block, qtype=w.v_qtype)])
+    for t, R, qt, (c, s) in zip((q, k, v), (w.q_block, w.kv_block, w.kv_block),
+                                (w.q_qtype, w.k_qtype, w.v_qtype), outs):
+        c1, s1 = qfa.block_quant(t, R, qt)
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.uint8), c1.view(torch.uint8))
+        assert torch.equal(s, s1)
