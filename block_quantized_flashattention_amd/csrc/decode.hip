@@ -7,15 +7,17 @@
 //   o_bh = sum_{j < L_b} softmax_j(softmax_scale * q_bh . (sk_j Kc_j)) * sv_j Vc_j
 //
 // Design (HBM-bound: every valid cache byte is read once):
-//   * Split-K: a workgroup of 4 wavefronts owns one (batch, query head,
-//     1024-token chunk); each wavefront owns 256 consecutive tokens. Chunks
+//   * Split-K: a workgroup of 8 wavefronts owns one (batch, query head,
+//     1024-token chunk); each wavefront owns 128 consecutive tokens (short
+//     per-wavefront score arrays keep the registers low, so more wavefronts
+//     are resident per SIMD to cover the HBM latency). Chunks
 //     past a sequence's length exit at once. A second small kernel merges the
 //     chunks' partial (max, sum, o) by log-sum-exp; a sequence that fits one
 //     chunk is written directly.
 //   * Lane geometry: a 16-byte load per lane, LPT = row_bytes/16 lanes per
 //     token, so one wavefront load covers 64/LPT consecutive tokens; loads are
 //     issued four at a time ahead of their use.
-//   * Two passes per 256 tokens: all scores first (a per-lane partial dot
+//   * Two passes per 128 tokens: all scores first (a per-lane partial dot
 //     product, then a DPP butterfly over the LPT lanes of the token), their
 //     max, then exp2 and the V accumulation; every lane accumulates o for its
 //     own channels over its own tokens and the token groups are summed once.
@@ -24,16 +26,16 @@
 //     v_dot2_f32_f16 (fp32 accumulation). V codes are converted with the
 //     unsigned-byte converter after flipping the sign bit (code + 128, or code
 //     + 8 for INT4); the offset is removed once per output channel.
-//   * When one scale block covers a wavefront's 256 tokens (block size a
-//     multiple of 256), its K and V scales are two scalar loads.
+//   * When one scale block covers a wavefront's 128 tokens (block size a
+//     multiple of 128), its K and V scales are two scalar loads.
 #include "qfa_device.h"
 #include "qfa_launch.h"
 
 namespace qfa {
 namespace {
 
-constexpr int kDecWaves = 4;
-constexpr int kWaveTokens = kDecodeChunk / kDecWaves;  // 256
+constexpr int kDecWaves = 8;
+constexpr int kWaveTokens = kDecodeChunk / kDecWaves;  // 128
 constexpr int kGroup = 4;                              // loads issued together
 
 struct DecParams {
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
   constexpr int LPT = kRowBytes / 16;        // lanes per token
   constexpr int EPL = INT4 ? 32 : 16;        // channels per lane
   constexpr int TPS = 64 / LPT;              // tokens per wavefront load
-  constexpr int NSUB = kWaveTokens / TPS;    // loads per lane per 256 tokens
+  constexpr int NSUB = kWaveTokens / TPS;    // loads per lane per wavefront chunk
   constexpr int NG = NSUB / kGroup;
   constexpr float kOff = INT4 ? 8.0f : 128.0f;
   static_assert(NSUB % kGroup == 0, "load groups");
