@@ -369,9 +369,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   };
 
   // Softmax of tile t and O^T += V_t^T . P_t^T (V and scales from V buffer t % 2).
-  auto softmax_pv = [&](const Acc* sacc, const VStage<D>& vs, int t) {
+  // The mask (causal diagonal or end of the keys) is a compile-time switch
+  // for causal attention, so its many unmasked tiles carry no per-element
+  // compare and select; without causality only a ragged last tile is masked
+  // and a runtime flag (cheaper in registers there) selects it.
+  auto softmax_pv = [&](const Acc* sacc, const VStage<D>& vs, int t, auto mask_c, bool rt_mask) {
     const int n0 = t * kBN;
-    const bool need_mask = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
+    const bool need_mask = decltype(mask_c)::value || rt_mask;
     const int lim = lim_base - n0;  // masked iff key_of(kb, r) > lim
     f16x8 pb[2][2];
     if constexpr (!TOK) {
@@ -509,7 +513,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   auto step = [&](const int t, Acc* scur, Acc* snext, auto par) {
     constexpr int PAR = decltype(par)::value;  // t % 2
     if (t + 1 < ntiles && wave_active(t + 1)) qk(snext, kst[PAR ^ 1]);
-    if (wave_active(t)) softmax_pv(scur, vst[PAR], t);
+    if (wave_active(t)) {
+      const int n0 = t * kBN;
+      const bool m = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
+      if constexpr (CAUSAL) {
+        if (m) softmax_pv(scur, vst[PAR], t, std::true_type(), false);
+        else softmax_pv(scur, vst[PAR], t, std::false_type(), false);
+      } else {
+        softmax_pv(scur, vst[PAR], t, std::false_type(), m);
+      }
+    }
     // K_{t+2} into K buffer t % 2 (K_t was last read in step t-1) and V_{t+1}
     // into V buffer (t+1) % 2 (V_{t-1} was last read in step t-1).
     store_k<D, KQT>(kst[PAR], pf);
