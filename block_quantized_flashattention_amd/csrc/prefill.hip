@@ -276,7 +276,9 @@ struct QK {
 // for the lane half `half`: MFMA 32x32 result rows 8*(r/4) + 4*half + r%4.
 __device__ __forceinline__ constexpr int key_of(int kb, int r) { return kb * 32 + 8 * (r >> 2) + (r & 3); }
 
-template <int D, int KVM, bool CAUSAL, bool TOK>
+// RAGGED (non-causal only): Sk is not a multiple of the tile, so the last tile
+// needs the end-of-keys mask; otherwise no tile does and the mask is compiled out.
+template <int D, int KVM, bool CAUSAL, bool TOK, bool RAGGED>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   constexpr bool FP8 = KVM == KV_F8_F8;
   constexpr int KQT = KVTypes<KVM>::K, VQT = KVTypes<KVM>::V;
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         if (m) softmax_pv(scur, vst[PAR], t, std::true_type(), false);
         else softmax_pv(scur, vst[PAR], t, std::false_type(), false);
       } else {
-        softmax_pv(scur, vst[PAR], t, std::false_type(), m);
+        softmax_pv(scur, vst[PAR], t, std::false_type(), RAGGED && m);
       }
     }
     // K_{t+2} into K buffer t % 2 (K_t was last read in step t-1) and V_{t+1}
@@ -563,12 +565,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
 template <int D, int KVM>
 hipError_t launch_kv(const FwdParams& p, int grid, bool causal, bool tok, hipStream_t st) {
+  const bool ragged = (p.Sk % kBN) != 0;
   if (causal) {
-    if (tok) fwd_kernel<D, KVM, true, true><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, KVM, true, false><<<grid, kThreads, 0, st>>>(p);
+    if (tok) fwd_kernel<D, KVM, true, true, false><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, true, false, false><<<grid, kThreads, 0, st>>>(p);
+  } else if (ragged) {
+    if (tok) fwd_kernel<D, KVM, false, true, true><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, false, false, true><<<grid, kThreads, 0, st>>>(p);
   } else {
-    if (tok) fwd_kernel<D, KVM, false, true><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, KVM, false, false><<<grid, kThreads, 0, st>>>(p);
+    if (tok) fwd_kernel<D, KVM, false, true, false><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, false, false, false><<<grid, kThreads, 0, st>>>(p);
   }
   return hipGetLastError();
 }
