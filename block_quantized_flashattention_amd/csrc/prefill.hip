@@ -35,9 +35,14 @@
 //     probabilities stay below 2^8 (exact softmax, fp16-safe).
 //   * Row sums add the fp16-rounded probabilities with v_dot2_f32_f16, i.e.
 //     exactly the weights the P.V product uses.
-//   * Causal: tiles past a workgroup's last row are skipped, wavefronts skip
-//     tiles entirely above their rows, and the mask is applied per element
-//     only on tiles crossing the diagonal. Work is ordered longest first.
+//   * One step per key tile: the max of tile t and the rare rescale, then, in
+//     one straight-line block, S(t+1) on the matrix unit, the exponentials of
+//     tile t, the staging of the next tiles and P(t) V(t).
+//   * Causal: tiles past a workgroup's last row are skipped and the mask is a
+//     compile-time variant used only on tiles crossing a wavefront's diagonal
+//     (with one scale per tile, a wavefront whose rows all lie above a tile
+//     runs it fully masked rather than branching around it; with per-token
+//     scales it skips it). Work is ordered longest first.
 //   * XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
 //     all query heads and row blocks of one (batch, KV head) are given ids on
 //     the same XCD and its K/V codes stay in that XCD's L2.
@@ -212,7 +217,7 @@ template <int D, int VQT>
 __device__ __forceinline__ void store_v(VStage<D>& st, const Prefetch& f, bool scale_f16) {
   const int tid = threadIdx.x;
   constexpr int kUnits = (kBN / 4) * (D / 8);
-  if (tid < kUnits) {
+  if (kUnits >= kThreads || tid < kUnits) {
     const int kg = tid % (kBN / 4), dg = tid / (kBN / 4);
     f16x2 val[4][4];  // [key][channel pair]
 #pragma unroll
@@ -241,11 +246,11 @@ __device__ __forceinline__ void store_v(VStage<D>& st, const Prefetch& f, bool s
       *(f16x4*)(st.vt + (dg * 8 + e) * VStage<D>::kStride + pos) = col;
     }
   }
-  if (tid < kBN) {
-    const uint32_t mask = scale_f16 ? 0xFFFFu : 0xFFFFFFFFu;
-    st.ksc[tid] = scale_from_bits((f.ks >> f.shift) & mask, scale_f16);
-    st.vsc[tid] = scale_from_bits((f.vs >> f.shift) & mask, scale_f16);
-  }
+  // Every thread holds the scales of key tid % kBN; the copies write equal
+  // values, which keeps this store free of a branch.
+  const uint32_t mask = scale_f16 ? 0xFFFFu : 0xFFFFFFFFu;
+  st.ksc[tid % kBN] = scale_from_bits((f.ks >> f.shift) & mask, scale_f16);
+  st.vsc[tid % kBN] = scale_from_bits((f.vs >> f.shift) & mask, scale_f16);
 }
 
 template <int D, bool FP8>
@@ -260,6 +265,17 @@ struct QK {
     } else {
       return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
     }
+  }
+  // a . b plus an accumulator that starts at 0x3E22F983 in every element,
+  // given as the inline constant 1/(2 pi) (INT8 only; the compiler does not
+  // fold a splat into that operand). The result is only read as the
+  // accumulator of the next matrix instruction of the same kind, which needs
+  // no wait states; the leading s_nop covers a vector write of a or b just
+  // before, which the hazard check cannot see through the asm.
+  static __device__ __forceinline__ Acc mma_biased(const Op& a, const Op& b) {
+    Acc r;
+    asm("s_nop 2\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, 0x3e22f983" : "=&v"(r) : "v"(a), "v"(b));
+    return r;
   }
   static __device__ __forceinline__ Op load(const uint8_t* p) {
     if constexpr (FP8) {
@@ -286,6 +302,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   using Op = typename T::Op;
   using Acc = typename T::Acc;
   constexpr int kDB = D / 32;  // 32-channel blocks of the output
+  // INT8 scores with one scale per tile: the integer accumulator starts at the
+  // bit pattern kBiasBits of the float kBiasInt * 2^-26 (the inline constant
+  // 1/(2 pi) of the matrix instruction), so 'kBiasBits + dot' is the bit
+  // pattern of the float (kBiasInt + dot) * 2^-26 exactly as long as the sum
+  // stays in that binade, i.e. -2292099 <= dot < 6096509, which any 8-bit
+  // codes with D <= 128 satisfy (|dot| <= 128 * 128 * 128). The scores then
+  // need no integer-to-float conversion, and their max is a float max.
+  constexpr bool kBiasAcc = !FP8 && !TOK;
+  constexpr uint32_t kBiasBits = 0x3E22F983u;
+  constexpr int kBiasInt = 10680707;  // 2^23 + 0x22F983
+  static_assert(D <= 128, "biased INT8 scores need |dot| < 2^21");
   __shared__ KStage<D> kst[2];
   __shared__ VStage<D> vst[2];
 
@@ -362,11 +389,115 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
   auto qk = [&](Acc* sacc, const KStage<D>& ks) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = (Acc){};
       const uint8_t* krow = ks.k + (kb * 32 + col) * KStage<D>::kStride + half * T::kSlice;
+      if constexpr (kBiasAcc) {
+        sacc[kb] = T::mma_biased(T::load(krow), qop[0]);
+      } else {
+        sacc[kb] = T::mma(T::load(krow), qop[0], (Acc){});
+      }
 #pragma unroll
-      for (int s = 0; s < T::kSteps; ++s)
+      for (int s = 1; s < T::kSteps; ++s)
         sacc[kb] = T::mma(T::load(krow + s * 2 * T::kSlice), qop[s], sacc[kb]);
+    }
+  };
+
+  // Softmax of tile t and O^T += V_t^T . P_t^T (V and scales from V buffer t % 2).
+  // The mask (causal diagonal or end of the keys) is a compile-time switch
+  // for causal attention, so its many unmasked tiles carry no per-element
+  // compare and select; without causality only a ragged last tile is masked
+  // and a runtime flag (cheaper in registers there) selects it.
+  // One-scale-per-tile softmax in two parts. tile_max converts the scores of
+  // a tile, takes their max and applies the lazy O rescale (a rare, uniform
+  // branch); tile_exp forms the fp16 probabilities in the B-operand layout of
+  // P.V and their row sums. Returns the score multiplier of the tile.
+  auto tile_max = [&](const Acc* sacc, const VStage<D>& vs, float (&x)[2][16], auto mask_c,
+                      bool rt_mask, int lim) -> float {
+    const bool need_mask = decltype(mask_c)::value || rt_mask;
+    const float ck = cq * vs.ksc[0];
+    const float sv_t = vs.vsc[0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = sacc[kb][r];
+        x[kb][r] = kBiasAcc ? __int_as_float(v) : (float)v;
+      }
+    // Tile max as four independent chains (short dependency depth).
+    float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          mc[r & 3] = fmaxf(mc[r & 3], key_of(kb, r) > lim ? -INFINITY : x[kb][r]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mc[r & 3] = fmaxf(mc[r & 3], x[kb][r]);
+    }
+    const float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+    // Max of this lane half; the row max over both halves is only formed when
+    // some row needs a rescale (or the V scale changes), which is rare.
+    // (x - kBiasInt * 2^-26) * 2^26 is the integer dot product, exactly.
+    const float mt = mx == -INFINITY ? -INFINITY
+                     : kBiasAcc ? (mx - __int_as_float(kBiasBits)) * (ck * 67108864.0f)
+                                : mx * ck;  // ck >= 0
+    const float sv_eff = sv_t > 0.0f ? sv_t : (sv_cur > 0.0f ? sv_cur : 1.0f);
+    if (__any(mt > m_run + kRescaleSlack) || sv_eff != sv_cur) {
+      const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = mrow > m_run + kRescaleSlack ? fmaxf(m_run, mrow) : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float f = sv_cur > 0.0f ? alpha * (sv_cur / sv_eff) : 0.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < kDB; ++i) o[i] *= f;
+      m_run = m_new;
+      sv_cur = sv_eff;
+    }
+    return ck;
+  };
+  auto tile_exp = [&](const float (&x)[2][16], float ck, f16x8 (&pb)[2][2], auto mask_c,
+                      bool rt_mask, int lim) {
+    const bool need_mask = decltype(mask_c)::value || rt_mask;
+    float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
+    if constexpr (kBiasAcc) {
+      // x = (kBiasInt + dot) * 2^-26: scale by ck * 2^26 and fold the offset
+      // into the subtrahend (one rounding, an error below one unit of dot).
+      msub = __builtin_fmaf(-(float)kBiasInt, ck, msub);
+      ck *= 67108864.0f;
+    }
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float a0 = __builtin_fmaf(x[kb][r], ck, msub);
+        float a1 = __builtin_fmaf(x[kb][r + 1], ck, msub);
+        if (need_mask) {
+          a0 = key_of(kb, r) > lim ? -INFINITY : a0;
+          a1 = key_of(kb, r + 1) > lim ? -INFINITY : a1;
+        }
+        const f16x2 h2 = {(_Float16)__builtin_amdgcn_exp2f(a0),
+                          (_Float16)__builtin_amdgcn_exp2f(a1)};
+        ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2(h2, one, ls[(r >> 1) & 3], false);
+        pb[kb][r >> 3][r & 7] = h2[0];
+        pb[kb][r >> 3][(r & 7) + 1] = h2[1];
+      }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  // O^T += V_t^T . P_t^T; consecutive matrix instructions update different
+  // output blocks.
+  auto tile_pv = [&](const f16x8 (&pb)[2][2], const VStage<D>& vs) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const _Float16* vrow = vs.vt + (db * 32 + col) * VStage<D>::kStride + half * 8;
+        const f16x8 a = *(const f16x8*)(vrow + g * 16);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
+      }
     }
   };
 
@@ -381,64 +512,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     const int lim = lim_base - n0;  // masked iff key_of(kb, r) > lim
     f16x8 pb[2][2];
     if constexpr (!TOK) {
-      // One K and one V scale for the whole tile, staged in slot 0.
-      const float ck = cq * vs.ksc[0];
-      const float sv_t = vs.vsc[0];
       float x[2][16];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[kb][r] = (float)sacc[kb][r];
-      // Tile max as four independent chains (short dependency depth).
-      float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            mc[r & 3] = fmaxf(mc[r & 3], key_of(kb, r) > lim ? -INFINITY : x[kb][r]);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mc[r & 3] = fmaxf(mc[r & 3], x[kb][r]);
-      }
-      const float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
-      // Max of this lane half; the row max over both halves is only formed when
-      // some row needs a rescale (or the V scale changes), which is rare.
-      const float mt = mx == -INFINITY ? -INFINITY : mx * ck;  // ck >= 0
-      const float sv_eff = sv_t > 0.0f ? sv_t : (sv_cur > 0.0f ? sv_cur : 1.0f);
-      if (__any(mt > m_run + kRescaleSlack) || sv_eff != sv_cur) {
-        const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = mrow > m_run + kRescaleSlack ? fmaxf(m_run, mrow) : m_run;
-        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float f = sv_cur > 0.0f ? alpha * (sv_cur / sv_eff) : 0.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < kDB; ++i) o[i] *= f;
-        m_run = m_new;
-        sv_cur = sv_eff;
-      }
-      const float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
-      const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float a0 = __builtin_fmaf(x[kb][r], ck, msub);
-          float a1 = __builtin_fmaf(x[kb][r + 1], ck, msub);
-          if (need_mask) {
-            a0 = key_of(kb, r) > lim ? -INFINITY : a0;
-            a1 = key_of(kb, r + 1) > lim ? -INFINITY : a1;
-          }
-          const f16x2 h2 = {(_Float16)__builtin_amdgcn_exp2f(a0),
-                            (_Float16)__builtin_amdgcn_exp2f(a1)};
-          ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2(h2, one, ls[(r >> 1) & 3], false);
-          pb[kb][r >> 3][r & 7] = h2[0];
-          pb[kb][r >> 3][(r & 7) + 1] = h2[1];
-        }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      const float ck = tile_max(sacc, vs, x, mask_c, rt_mask, lim);
+      tile_exp(x, ck, pb, mask_c, rt_mask, lim);
     } else {
       // Per-key scales (e.g. INT4 K/V with one scale per token).
       float x[2][16];
@@ -484,15 +560,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         }
       l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-      const _Float16* vrow = vs.vt + (db * 32 + col) * VStage<D>::kStride + half * 8;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f16x8 a = *(const f16x8*)(vrow + g * 16);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
-      }
-    }
+    tile_pv(pb, vs);
   };
 
   // Pipeline: K runs one tile ahead of V. Step t issues S(t+1) = K_{t+1} Q^T on
@@ -512,23 +580,61 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
   Acc sa[2], sb[2];
   if (wave_active(0)) qk(sa, kst[0]);
-  auto step = [&](const int t, Acc* scur, Acc* snext, auto par) {
+  // One step with one scale per tile. After the max and the rare rescale,
+  // S(t+1), the exponentials of tile t, the staging of the next tiles and
+  // P(t) V(t) form one straight-line block, which leaves the compiler free to
+  // interleave the matrix instructions with the vector work. S(t+1) is also
+  // formed when tile t is the last one (from the clamped tile already staged;
+  // the result is not used), and every wavefront runs every step (a step whose
+  // keys all lie beyond a wavefront's rows is fully masked and adds nothing),
+  // so the loop has no data-dependent paths besides the rescale.
+  auto steady_step = [&](const int t, Acc* scur, Acc* snext, auto par, auto mask_c, bool rt_mask) {
     constexpr int PAR = decltype(par)::value;  // t % 2
-    if (t + 1 < ntiles && wave_active(t + 1)) qk(snext, kst[PAR ^ 1]);
-    if (wave_active(t)) {
-      const int n0 = t * kBN;
-      const bool m = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
-      if constexpr (CAUSAL) {
-        if (m) softmax_pv(scur, vst[PAR], t, std::true_type(), false);
-        else softmax_pv(scur, vst[PAR], t, std::false_type(), false);
-      } else {
-        softmax_pv(scur, vst[PAR], t, std::false_type(), RAGGED && m);
-      }
-    }
-    // K_{t+2} into K buffer t % 2 (K_t was last read in step t-1) and V_{t+1}
-    // into V buffer (t+1) % 2 (V_{t-1} was last read in step t-1).
+    const int lim = lim_base - t * kBN;
+    float x[2][16];
+    f16x8 pb[2][2];
+    const float ck = tile_max(scur, vst[PAR], x, mask_c, rt_mask, lim);
+    qk(snext, kst[PAR ^ 1]);
+    tile_exp(x, ck, pb, mask_c, rt_mask, lim);
+    // K_{t+2} into K buffer t % 2 and V_{t+1} into V buffer (t+1) % 2, both
+    // last read in step t-1, while P(t) V(t) runs.
     store_k<D, KQT>(kst[PAR], pf);
     store_v<D, VQT>(vst[PAR ^ 1], pf, p.kv_scale_f16);
+    tile_pv(pb, vst[PAR]);
+  };
+  auto step = [&](const int t, Acc* scur, Acc* snext, auto par) {
+    constexpr int PAR = decltype(par)::value;  // t % 2
+    if constexpr (!TOK && !FP8) {
+      const int n0 = t * kBN;
+      // Masked: the causal diagonal, keys past the end, or a wavefront whose
+      // rows all lie above the tile (every key masked, so the tile adds
+      // nothing and the step runs the same instructions as the others).
+      const bool m = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
+      if constexpr (CAUSAL) {
+        if (m) steady_step(t, scur, snext, par, std::true_type(), false);
+        else steady_step(t, scur, snext, par, std::false_type(), false);
+      } else {
+        steady_step(t, scur, snext, par, std::false_type(), RAGGED && m);
+      }
+    } else {
+      // Per-key scales and FP8 (measured faster this way): wavefronts skip the
+      // tiles beyond their rows, and S(t+1) is a block of its own.
+      if (t + 1 < ntiles && wave_active(t + 1)) qk(snext, kst[PAR ^ 1]);
+      if (wave_active(t)) {
+        const int n0 = t * kBN;
+        const bool m = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
+        if constexpr (CAUSAL) {
+          if (m) softmax_pv(scur, vst[PAR], t, std::true_type(), false);
+          else softmax_pv(scur, vst[PAR], t, std::false_type(), false);
+        } else {
+          softmax_pv(scur, vst[PAR], t, std::false_type(), RAGGED && m);
+        }
+      }
+      // K_{t+2} into K buffer t % 2 (K_t was last read in step t-1) and
+      // V_{t+1} into V buffer (t+1) % 2 (V_{t-1} was last read in step t-1).
+      store_k<D, KQT>(kst[PAR], pf);
+      store_v<D, VQT>(vst[PAR ^ 1], pf, p.kv_scale_f16);
+    }
     __syncthreads();
     fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, tile_n0(t + 3), tile_n0(t + 2));
   };
