@@ -123,6 +123,28 @@ def _quant_outputs(x, block_rows, qtype, scale_dtype, layout, codes, scales):
     return job, codes, scales
 
 
+def prepare_block_quant_multi(jobs, stream=None):
+    """Marshal one ``block_quant_multi`` call once; returns (launch, outputs).
+
+    ``launch()`` issues the same call again (same tensors, same stream) at the
+    cost of one ctypes call, for loops that repeat a call on fixed buffers.
+    """
+    descs, outs = [], []
+    for j in jobs:
+        job, codes, scales = _quant_outputs(j["x"], j["block_rows"], j["qtype"],
+                                            j.get("scale_dtype", torch.float32),
+                                            j.get("layout", "bnsd"), j.get("codes"),
+                                            j.get("scales"))
+        descs.append(job)
+        outs.append((codes, scales))
+    arr = (QuantJob * max(len(descs), 1))(*descs)
+    n, st, f = len(descs), _stream(stream), lib().qfa_block_quant_multi
+
+    def launch():
+        _check("qfa_block_quant_multi", f(arr, n, st))
+    return launch, outs
+
+
 def block_quant_multi(jobs, stream=None):
     """Quantize several tensors in shared launches; returns [(codes, scales), ...].
 
@@ -169,10 +191,8 @@ def block_quant(x: torch.Tensor, block_rows: int, qtype: str, scale_dtype=torch.
     return codes, scales
 
 
-def fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, q_qtype: str, k_qtype: str,
-        v_qtype: str, q_block: int, kv_block: int, softmax_scale: float, causal: bool = False,
-        layout: str = "bnsd", out_dtype=torch.float16, out=None, stream=None):
-    """Attention forward on block-quantized codes; returns out [B,Hq,Sq,D] (or BSND)."""
+def _fwd_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, q_qtype, k_qtype, v_qtype,
+              q_block, kv_block, softmax_scale, causal, layout, out_dtype, out, stream):
     for t, n in ((q_codes, "q_codes"), (q_scales, "q_scales"), (k_codes, "k_codes"),
                  (k_scales, "k_scales"), (v_codes, "v_codes"), (v_scales, "v_scales")):
         _dev(t, n)
@@ -187,23 +207,50 @@ def fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, q_qtype: str
     _dev(out, "out")
     if q_scales.dtype != torch.float32 and q_scales.dtype != torch.float16:
         raise ValueError("scales must be float32 or float16")
-    _check("qfa_fwd", lib().qfa_fwd(
-        _ptr(q_codes), _ptr(q_scales), QTYPES[q_qtype], q_block, FLOATS[q_scales.dtype],
-        _ptr(k_codes), _ptr(k_scales), QTYPES[k_qtype], _ptr(v_codes), _ptr(v_scales),
-        QTYPES[v_qtype], kv_block, FLOATS[k_scales.dtype], B, Hq, Hkv, Sq, Sk, D,
-        LAYOUTS[layout], int(bool(causal)), float(softmax_scale), _ptr(out), FLOATS[out.dtype],
-        _stream(stream)))
+    args = (_ptr(q_codes), _ptr(q_scales), QTYPES[q_qtype], q_block, FLOATS[q_scales.dtype],
+            _ptr(k_codes), _ptr(k_scales), QTYPES[k_qtype], _ptr(v_codes), _ptr(v_scales),
+            QTYPES[v_qtype], kv_block, FLOATS[k_scales.dtype], B, Hq, Hkv, Sq, Sk, D,
+            LAYOUTS[layout], int(bool(causal)), float(softmax_scale), _ptr(out),
+            FLOATS[out.dtype], _stream(stream))
+    return args, out
+
+
+def fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, q_qtype: str, k_qtype: str,
+        v_qtype: str, q_block: int, kv_block: int, softmax_scale: float, causal: bool = False,
+        layout: str = "bnsd", out_dtype=torch.float16, out=None, stream=None):
+    """Attention forward on block-quantized codes; returns out [B,Hq,Sq,D] (or BSND)."""
+    args, out = _fwd_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, q_qtype,
+                          k_qtype, v_qtype, q_block, kv_block, softmax_scale, causal, layout,
+                          out_dtype, out, stream)
+    _check("qfa_fwd", lib().qfa_fwd(*args))
     return out
+
+
+def prepare_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, q_qtype: str,
+                k_qtype: str, v_qtype: str, q_block: int, kv_block: int, softmax_scale: float,
+                causal: bool = False, layout: str = "bnsd", out_dtype=torch.float16, out=None,
+                stream=None):
+    """Marshal one ``fwd`` call once; returns (launch, out).
+
+    ``launch()`` issues the same forward again (same tensors, same stream) at
+    the cost of one ctypes call, for loops that repeat a call on fixed buffers.
+    """
+    args, out = _fwd_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, q_qtype,
+                          k_qtype, v_qtype, q_block, kv_block, softmax_scale, causal, layout,
+                          out_dtype, out, stream)
+    f = lib().qfa_fwd
+
+    def launch():
+        _check("qfa_fwd", f(*args))
+    return launch, out
 
 
 def decode_workspace_bytes(B: int, Hq: int, S_max: int, D: int) -> int:
     return int(lib().qfa_decode_workspace_bytes(B, Hq, S_max, D))
 
 
-def decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtype: str, kv_block: int,
-           softmax_scale: float, layout: str = "bnsd", out_dtype=None, out=None, workspace=None,
-           stream=None):
-    """One query token per sequence against a quantized KV cache; returns out [B,Hq,1,D]."""
+def _decode_args(q, k_cache, v_cache, k_scales, v_scales, seq_lens, kv_qtype, kv_block,
+                 softmax_scale, layout, out_dtype, out, workspace, stream):
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (k_scales, "k_scales"),
                  (v_scales, "v_scales"), (seq_lens, "seq_lens")):
         _dev(t, n)
@@ -220,13 +267,42 @@ def decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtype: str, 
     need = decode_workspace_bytes(B, Hq, S_max, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check("qfa_decode", lib().qfa_decode(
-        _ptr(q), FLOATS[q.dtype], B, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
-        _ptr(v_scales), QTYPES[kv_qtype], kv_block, FLOATS[k_scales.dtype], S_max,
-        LAYOUTS[layout], _ptr(seq_lens), float(softmax_scale), _ptr(out), FLOATS[out.dtype],
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (_ptr(q), FLOATS[q.dtype], B, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+            _ptr(v_scales), QTYPES[kv_qtype], kv_block, FLOATS[k_scales.dtype], S_max,
+            LAYOUTS[layout], _ptr(seq_lens), float(softmax_scale), _ptr(out), FLOATS[out.dtype],
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    return args, out, workspace
+
+
+def decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtype: str, kv_block: int,
+           softmax_scale: float, layout: str = "bnsd", out_dtype=None, out=None, workspace=None,
+           stream=None):
+    """One query token per sequence against a quantized KV cache; returns out [B,Hq,1,D]."""
+    args, out, _ = _decode_args(q, k_cache, v_cache, k_scales, v_scales, seq_lens, kv_qtype,
+                                kv_block, softmax_scale, layout, out_dtype, out, workspace, stream)
+    _check("qfa_decode", lib().qfa_decode(*args))
     return out
 
 
-__all__ = ["block_quant", "fwd", "decode", "decode_workspace_bytes", "lib", "header_functions",
+def prepare_decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtype: str,
+                   kv_block: int, softmax_scale: float, layout: str = "bnsd", out_dtype=None,
+                   out=None, workspace=None, stream=None):
+    """Marshal one ``decode`` call once; returns (launch, out).
+
+    ``launch()`` issues the same decode again (same tensors, workspace and
+    stream) at the cost of one ctypes call.
+    """
+    args, out, workspace = _decode_args(q, k_cache, v_cache, k_scales, v_scales, seq_lens,
+                                        kv_qtype, kv_block, softmax_scale, layout, out_dtype, out,
+                                        workspace, stream)
+    f = lib().qfa_decode
+
+    def launch():
+        _check("qfa_decode", f(*args))
+    launch.workspace = workspace  # keeps a workspace allocated here alive
+    return launch, out
+
+
+__all__ = ["block_quant", "block_quant_multi", "prepare_block_quant_multi", "fwd", "prepare_fwd",
+           "decode", "prepare_decode", "decode_workspace_bytes", "lib", "header_functions",
            "QFAError", "QTYPES", "LAYOUTS", "FLOATS", "QMAX", "code_dtype"]
