@@ -219,6 +219,28 @@ __device__ __forceinline__ void store_v(VStage<D>& st, const Prefetch& f, bool s
   constexpr int kUnits = (kBN / 4) * (D / 8);
   if (kUnits >= kThreads || tid < kUnits) {
     const int kg = tid % (kBN / 4), dg = tid / (kBN / 4);
+    const int pos = vt_pos(kg * 4);
+    if constexpr (VQT == QFA_INT8) {
+      // Transpose bytes first: one permute gathers channels (c, c+1) of two
+      // keys, so each conversion yields a key pair of one channel, which is
+      // what the transposed store needs.
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        f16x2 pr[2][4];  // [key pair][channel 4d + i]
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const uint32_t wa = d ? f.v[2 * kp].y : f.v[2 * kp].x;
+          const uint32_t wb = d ? f.v[2 * kp + 1].y : f.v[2 * kp + 1].x;
+          i8x4_to_h(__builtin_amdgcn_perm(wb, wa, 0x05010400u), pr[kp][0], pr[kp][1]);
+          i8x4_to_h(__builtin_amdgcn_perm(wb, wa, 0x07030602u), pr[kp][2], pr[kp][3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x4 col = {pr[0][i][0], pr[0][i][1], pr[1][i][0], pr[1][i][1]};
+          *(f16x4*)(st.vt + (dg * 8 + 4 * d + i) * VStage<D>::kStride + pos) = col;
+        }
+      }
+    } else {
     f16x2 val[4][4];  // [key][channel pair]
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -238,12 +260,12 @@ __device__ __forceinline__ void store_v(VStage<D>& st, const Prefetch& f, bool s
         i8x4_to_h(w.y, val[r][2], val[r][3]);
       }
     }
-    const int pos = vt_pos(kg * 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = e >> 1, s = e & 1;
       f16x4 col = {val[0][j][s], val[1][j][s], val[2][j][s], val[3][j][s]};
       *(f16x4*)(st.vt + (dg * 8 + e) * VStage<D>::kStride + pos) = col;
+    }
     }
   }
   // Every thread holds the scales of key tid % kBN; the copies write equal
