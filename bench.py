@@ -93,8 +93,7 @@ def bench_prefill(torch, qfa, wl, steps, warmup):
     return w, wall, fwd_ms, quant_ms, ops
 
 
-def bench_decode(torch, qfa, wl, steps, warmup):
-    w = wl.DECODE
+def bench_decode(torch, qfa, wl, w, steps, warmup):
     q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
     sdt = torch.float16
     kc, ks = qfa.block_quant(k, w.kv_block, w.kv_qtype, sdt)
@@ -244,18 +243,20 @@ def main():
                                       "block_quantized_flashattention_amd/csrc/quant.hip")}},
     }
     if not args.no_decode:
-        log(f"decode: {wl.DECODE.name}")
-        dw, dms, nbytes = bench_decode(torch, qfa, wl, max(args.steps, 10), args.warmup)
-        gbs = nbytes / (dms * 1e-3) / 1e9
-        log(f"decode {dms:.3f} ms, {gbs:.0f} GB/s")
-        rec["decode"] = {"workload": dw.name, "value": round(gbs, 1), "unit": "GB/s",
-                         "ms": round(dms, 4), "bytes": nbytes,
-                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
-                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                      "traffic": profiled_traffic(
-                                          "decode_int8_kv_b32_h32.md",
-                                          "block_quantized_flashattention_amd/csrc/decode.hip")}}
+        # INT8 cache, then the same shape with a packed INT4 cache.
+        for key, dwl, prof in (("decode", wl.DECODE, "decode_int8_kv_b32_h32.md"),
+                               ("decode_int4", wl.DECODE_INT4, "decode_int4_kv_b32_h32.md")):
+            log(f"{key}: {dwl.name}")
+            dw, dms, nbytes = bench_decode(torch, qfa, wl, dwl, max(args.steps, 10), args.warmup)
+            gbs = nbytes / (dms * 1e-3) / 1e9
+            log(f"{key} {dms:.3f} ms, {gbs:.0f} GB/s")
+            rec[key] = {"workload": dw.name, "value": round(gbs, 1), "unit": "GB/s",
+                        "ms": round(dms, 4), "bytes": nbytes,
+                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                     "traffic": profiled_traffic(
+                                         prof, "block_quantized_flashattention_amd/csrc/decode.hip")}}
     if args.copy_probe:
         # A plain elementwise copy of known size: reads 1 GiB (fp32), writes 512 MiB (fp16).
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

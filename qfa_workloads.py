@@ -122,6 +122,10 @@ DECODE = DecodeWorkload(
     len_hi=8192, seed=4, kv_qtype="int8", kv_block=256, kv_scale_dtype="f16", q_dtype="f16",
     out_dtype="f16", softmax_scale=_f32(1.0 / math.sqrt(128)))
 
+# The decode shape above with a packed INT4 cache (two codes per byte, one
+# fp16 scale per 256-token block): half the cache bytes of INT8.
+DECODE_INT4 = dataclasses.replace(DECODE, name="int4_kv_decode_b32_h32", kv_qtype="int4")
+
 PREFILL_WORKLOADS = {w.name: w for w in (TINY, INT8_CAUSAL, FP8_ROT, GQA_INT4)}
 
 

@@ -75,10 +75,11 @@ def test_small_decode(name, B, Hq, Hkv, D, S_max, lens, qt, R, sdt, layout):
     _run(w, q, k, v, lens_t, layout=layout)
 
 
-def test_full_size_decode_sampled():
+@pytest.mark.parametrize("w", [wl.DECODE, wl.DECODE_INT4], ids=lambda w: w.name)
+def test_full_size_decode_sampled(w):
     """The full decode workload (B=32, 32 heads, S_max=8192, L in [4096, 8192]),
-    inputs drawn on the GPU; 24 (batch, head) pairs compared with the oracle."""
-    w = wl.DECODE
+    INT8 or packed INT4 cache, inputs drawn on the GPU; 24 (batch, head) pairs
+    compared with the oracle."""
     say("full-size decode: generating inputs on the GPU")
     q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
     rng = np.random.default_rng(7)
