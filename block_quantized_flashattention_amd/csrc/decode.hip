@@ -21,11 +21,18 @@
 //     product, then a DPP butterfly over the LPT lanes of the token), their
 //     max, then exp2 and the V accumulation; every lane accumulates o for its
 //     own channels over its own tokens and the token groups are summed once.
-//   * With an fp16 query, K codes are converted exactly to packed fp16 (the
-//     byte goes into the mantissa of 1024 + byte) and dotted with
-//     v_dot2_f32_f16 (fp32 accumulation). V codes are converted with the
-//     unsigned-byte converter after flipping the sign bit (code + 128, or code
-//     + 8 for INT4); the offset is removed once per output channel.
+//   * With an fp16 query, INT8 K codes are converted exactly to packed fp16
+//     (the byte goes into the mantissa of 1024 + byte) and dotted with
+//     v_dot2_f32_f16 (fp32 accumulation); V codes are converted with the
+//     unsigned-byte converter after flipping the sign bit (code + 128) and
+//     accumulated in fp32. Packed INT4, which carries twice the codes per
+//     byte, stays in fp16 pairs for both: one shift and mask put a nibble
+//     pair under the exponent of 1024 (1032 + code, exact); keys pair
+//     channels e and e + 4 of each group of 8 (the query is paired the same
+//     way) and drop 1032 * sum(q) once per token; values pair one channel of
+//     two tokens against the two fp16 weights and drop 1032 times the sum of
+//     those weights once per output channel. With an fp32/bf16 query the
+//     codes go to fp32 (offset 128 or 8, removed once per channel).
 //   * When one scale block covers a wavefront's 128 tokens (block size a
 //     multiple of 128), its K and V scales are two scalar loads.
 #include "qfa_device.h"
@@ -88,17 +95,11 @@ __device__ __forceinline__ void i8x4_to_h(uint32_t w, f16x2& lo, f16x2& hi) {
   hi = __builtin_bit_cast(f16x2, b) - bias;
 }
 
-// Eight packed two's-complement nibbles (element 2k low) as four exact fp16 pairs.
-__device__ __forceinline__ void i4x8_to_h(uint32_t w, f16x2* h) {
-  const uint32_t u = w ^ 0x88888888u;              // nibble + 8 in [0, 15]
-  const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
-  const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // e0 e1 e2 e3
-  const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // e4 e5 e6 e7
-  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  h[0] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, p0, 0x05010400u)) - bias;
-  h[1] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, p0, 0x07030602u)) - bias;
-  h[2] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, p1, 0x05010400u)) - bias;
-  h[3] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, p1, 0x07030602u)) - bias;
+// The nibbles at bits 0-3 and 16-19 of w (two's-complement codes) as an fp16
+// pair 1032 + code, exact: flip the sign bit, keep the nibbles, set the
+// exponent of 1024.
+__device__ __forceinline__ uint32_t i4_pair_h(uint32_t w) {
+  return ((w ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
 }
 
 // Offset codes (code + 128, or code + 8 for INT4) of one 16-byte chunk as floats.
@@ -164,8 +165,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
     qf[e] = load_q(p.q, qoff + d0 + e, p.q_dtype);
     qsum += qf[e];
   }
+  // Packed INT4 keys are read as channel pairs (e, e + 4) of each group of 8
+  // (the nibbles one shift-and-mask isolates); INT8 keys as (2e, 2e + 1).
+  constexpr bool kI4H = INT4 && QF16;
 #pragma unroll
-  for (int e = 0; e < EPL / 2; ++e) qh[e] = (f16x2){(_Float16)qf[2 * e], (_Float16)qf[2 * e + 1]};
+  for (int e = 0; e < EPL / 2; ++e) {
+    const int c0 = kI4H ? 8 * (e / 4) + (e % 4) : 2 * e;
+    const int c1 = kI4H ? c0 + 4 : 2 * e + 1;
+    qh[e] = (f16x2){(_Float16)qf[c0], (_Float16)qf[c1]};
+  }
 
   const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
   const uint8_t* kp = p.k + cbase + dc * 16;
@@ -210,10 +218,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
         if constexpr (QF16) {
           f16x2 kh[EPL / 2];
           if constexpr (INT4) {
-            i4x8_to_h(w.x, kh + 0);
-            i4x8_to_h(w.y, kh + 4);
-            i4x8_to_h(w.z, kh + 8);
-            i4x8_to_h(w.w, kh + 12);
+            // Channel pairs (8i + s, 8i + s + 4) as fp16 1032 + code, exact;
+            // the 1032 * sum(q) this adds is removed once per token below.
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int sft = 0; sft < 4; ++sft)
+                kh[4 * i + sft] = __builtin_bit_cast(f16x2, i4_pair_h(ww[i] >> (4 * sft)));
           } else {
             i8x4_to_h(w.x, kh[0], kh[1]);
             i8x4_to_h(w.y, kh[2], kh[3]);
@@ -227,6 +239,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
             a1 = __builtin_amdgcn_fdot2(qh[e + 1], kh[e + 1], a1, false);
           }
           acc = a0 + a1;
+          if constexpr (INT4) acc = __builtin_fmaf(-1032.0f, qsum, acc);
         } else {
           float f[EPL];
           chunk_to_f32<INT4>(w, f);
@@ -261,24 +274,71 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g + 1 < NG) vload(vw[(g + 1) & 1], g + 1);
+      if constexpr (kI4H) {
+        // Two tokens at a time: each channel's codes of tokens j and j + 1
+        // form one fp16 pair (1032 + code), dotted with the two weights in
+        // fp16; the sums of those same fp16 weights remove the offset.
+        static_assert(kGroup % 2 == 0, "token pairs");
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const int j = g * kGroup + i;
-        const float pr = __builtin_amdgcn_exp2f(sc[j] - m_blk);  // 0 for masked tokens
-        lp[i & 1] += pr;
-        float wt = pr;
-        if constexpr (!BLOCK_SCALE) {
-          const int t = min(t_begin + j * TPS + tg, t_last);
-          wt *= load_scale(p.vs, sbase + t / p.kv_block, p.kv_scale_f16);
+        for (int i = 0; i < kGroup; i += 2) {
+          const int j = g * kGroup + i;
+          const float pa = __builtin_amdgcn_exp2f(sc[j] - m_blk);  // 0 for masked tokens
+          const float pb = __builtin_amdgcn_exp2f(sc[j + 1] - m_blk);
+          float wa = pa, wb = pb;
+          if constexpr (!BLOCK_SCALE) {
+            const int ta = min(t_begin + j * TPS + tg, t_last);
+            const int tb = min(t_begin + (j + 1) * TPS + tg, t_last);
+            wa *= load_scale(p.vs, sbase + ta / p.kv_block, p.kv_scale_f16);
+            wb *= load_scale(p.vs, sbase + tb / p.kv_block, p.kv_scale_f16);
+          }
+          const f16x2 wp = {(_Float16)wa, (_Float16)wb};
+          if constexpr (BLOCK_SCALE) {
+            lp[(i >> 1) & 1] = __builtin_amdgcn_fdot2(wp, one, lp[(i >> 1) & 1], false);
+          } else {
+            lp[(i >> 1) & 1] += pa + pb;
+            wsum = __builtin_amdgcn_fdot2(wp, one, wsum, false);
+          }
+          const uint4 va = vw[g & 1][i], vb = vw[g & 1][i + 1];
+          const uint32_t wa4[4] = {va.x, va.y, va.z, va.w}, wb4[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            // Bytes 0-1 (2-3) of token j then of token j + 1: channel 8d + c
+            // (8d + 4 + c) sits in bits 0-3 (token j) and 16-19 (token j + 1)
+            // after a shift.
+            const uint32_t r0 = __builtin_amdgcn_perm(wb4[d], wa4[d], 0x05040100u);
+            const uint32_t r1 = __builtin_amdgcn_perm(wb4[d], wa4[d], 0x07060302u);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t sft = (c & 1) * 4 + (c >> 1) * 8;
+              o[8 * d + c] = __builtin_amdgcn_fdot2(
+                  wp, __builtin_bit_cast(f16x2, i4_pair_h(r0 >> sft)), o[8 * d + c], false);
+              o[8 * d + 4 + c] = __builtin_amdgcn_fdot2(
+                  wp, __builtin_bit_cast(f16x2, i4_pair_h(r1 >> sft)), o[8 * d + 4 + c], false);
+            }
+          }
         }
-        wsum += wt;
-        float f[EPL];
-        chunk_to_f32<INT4>(vw[g & 1][i], f);
+      } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = __builtin_fmaf(wt, f[e], o[e]);
+        for (int i = 0; i < kGroup; ++i) {
+          const int j = g * kGroup + i;
+          const float pr = __builtin_amdgcn_exp2f(sc[j] - m_blk);  // 0 for masked tokens
+          lp[i & 1] += pr;
+          float wt = pr;
+          if constexpr (!BLOCK_SCALE) {
+            const int t = min(t_begin + j * TPS + tg, t_last);
+            wt *= load_scale(p.vs, sbase + t / p.kv_block, p.kv_scale_f16);
+          }
+          wsum += wt;
+          float f[EPL];
+          chunk_to_f32<INT4>(vw[g & 1][i], f);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = __builtin_fmaf(wt, f[e], o[e]);
+        }
       }
     }
     l_blk = lp[0] + lp[1];
+    if constexpr (kI4H && BLOCK_SCALE) wsum = l_blk;
     // Sum the token groups: lanes with the same channel chunk.
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
@@ -287,8 +347,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], off);
     }
+    constexpr float kOffV = kI4H ? 1032.0f : kOff;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = (o[e] - kOff * wsum) * sv_blk;
+    for (int e = 0; e < EPL; ++e) o[e] = (o[e] - kOffV * wsum) * sv_blk;
   }
 
   // Merge the wavefronts of the workgroup.
