@@ -9,9 +9,10 @@
 //   * A workgroup of 4 wavefronts owns 128 query rows of one (batch, head);
 //     each wavefront owns 32 rows. Two workgroups share a CU (at most 256
 //     registers per lane), so one's softmax arithmetic overlaps the other's
-//     matrix work. Key tiles of 64 rows are double-buffered in LDS and their
-//     codes are fetched into registers two tiles ahead (two register sets),
-//     so a load has two tiles of compute to arrive; one barrier per tile.
+//     matrix work. Key tiles of 64 rows are double-buffered in LDS, K one tile
+//     ahead of V; each tile's codes are loaded into registers a step before
+//     they are staged, so a load has a step of compute to arrive; one barrier
+//     per tile.
 //   * Scores are formed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_32x32x32_i8 (INT8 Q/K; INT4 K is widened to INT8 while it is
 //     staged) or v_mfma_f32_32x32x64_f8f6f4 (FP8 e4m3 Q/K). In the MFMA result
@@ -24,8 +25,9 @@
 //     are exact in fp16 and are converted once per workgroup. Keys are
 //     permuted inside each group of 16 so that every lane reads its operand
 //     slice with one 16-byte LDS read.
-//   * Scale fold: with one K scale per tile, the row max is taken on the
-//     integer dot products and each probability costs one FMA and one exp2:
+//   * Scale fold: with one K scale per tile, the row max is taken on the raw
+//     scores (INT8: the biased accumulator read as floats, see kBiasAcc) and
+//     each probability costs one FMA and one exp2:
 //     p = exp2(dot * (sq * sk * softmax_scale * log2 e) - m). The V block
 //     scale is folded into the accumulator (O is kept in units of the current
 //     V scale and rescaled when it changes). With per-token scales (INT4 K/V)
@@ -35,14 +37,16 @@
 //     probabilities stay below 2^8 (exact softmax, fp16-safe).
 //   * Row sums add the fp16-rounded probabilities with v_dot2_f32_f16, i.e.
 //     exactly the weights the P.V product uses.
-//   * One step per key tile: the max of tile t and the rare rescale, then, in
-//     one straight-line block, S(t+1) on the matrix unit, the exponentials of
-//     tile t, the staging of the next tiles and P(t) V(t).
+//   * One step per key tile: the max of tile t and the rare rescale, then
+//     (INT8 with one scale per tile) one straight-line block holding S(t+1)
+//     on the matrix unit, the exponentials of tile t, the staging of the next
+//     tiles and P(t) V(t). FP8 and per-token scales issue S(t+1) in a block
+//     of its own before the softmax (measured faster for them).
 //   * Causal: tiles past a workgroup's last row are skipped and the mask is a
 //     compile-time variant used only on tiles crossing a wavefront's diagonal
-//     (with one scale per tile, a wavefront whose rows all lie above a tile
-//     runs it fully masked rather than branching around it; with per-token
-//     scales it skips it). Work is ordered longest first.
+//     (in the straight-line INT8 step, a wavefront whose rows all lie above a
+//     tile runs it fully masked rather than branching around it; the other
+//     paths skip it). Work is ordered longest first.
 //   * XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
 //     all query heads and row blocks of one (batch, KV head) are given ids on
 //     the same XCD and its K/V codes stay in that XCD's L2.
@@ -423,11 +427,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     }
   };
 
-  // Softmax of tile t and O^T += V_t^T . P_t^T (V and scales from V buffer t % 2).
-  // The mask (causal diagonal or end of the keys) is a compile-time switch
-  // for causal attention, so its many unmasked tiles carry no per-element
-  // compare and select; without causality only a ragged last tile is masked
-  // and a runtime flag (cheaper in registers there) selects it.
   // One-scale-per-tile softmax in two parts. tile_max converts the scores of
   // a tile, takes their max and applies the lazy O rescale (a rare, uniform
   // branch); tile_exp forms the fp16 probabilities in the B-operand layout of
