@@ -93,6 +93,32 @@ def bench_prefill(torch, qfa, wl, steps, warmup):
     return w, wall, fwd_ms, quant_ms, ops
 
 
+def bench_forward(torch, qfa, wl, w, steps, warmup):
+    """Forward alone on workload ``w`` (codes quantized once): average kernel
+    time from per-call HIP events over ``steps`` back-to-back calls."""
+    q, k, v = wl.make_prefill_inputs(w, device="cuda")
+    sdt = torch.float32
+    qc, qs = qfa.block_quant(q, w.q_block, w.q_qtype, sdt)
+    kc, ks = qfa.block_quant(k, w.kv_block, w.k_qtype, sdt)
+    vc, vs = qfa.block_quant(v, w.kv_block, w.v_qtype, sdt)
+    out = torch.empty_like(q)
+    del q, k, v
+    attn, _ = qfa.prepare_fwd(qc, qs, kc, ks, vc, vs, q_qtype=w.q_qtype, k_qtype=w.k_qtype,
+                              v_qtype=w.v_qtype, q_block=w.q_block, kv_block=w.kv_block,
+                              softmax_scale=w.softmax_scale, causal=w.causal, out=out)
+    settle(torch, attn)
+    for _ in range(warmup):
+        attn()
+    torch.cuda.synchronize()
+    evs = [_events(torch) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        attn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
 def bench_decode(torch, qfa, wl, w, steps, warmup):
     q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
     sdt = torch.float16
@@ -242,6 +268,17 @@ def main():
                                       "block_quant_qkv_int8_causal_h32_s4096.md",
                                       "block_quantized_flashattention_amd/csrc/quant.hip")}},
     }
+    # The same shape with packed INT4 V codes (INT8 Q and K): forward only.
+    mw = wl.INT8QK_INT4V
+    log(f"forward: {mw.name}")
+    mms = bench_forward(torch, qfa, wl, mw, args.steps, args.warmup)
+    mtops = mw.attention_ops() / (mms * 1e-3) / 1e12
+    log(f"forward {mw.name} {mms:.3f} ms, {mtops:.1f} TOPS")
+    rec["fwd_int8qk_int4v"] = {"workload": mw.name, "ms": round(mms, 4),
+                               "roofline": {"bound": "mfma", "achieved": round(mtops, 2),
+                                            "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                                            "frac": round(mtops / PEAK_INT8_TOPS, 4),
+                                            "traffic": None}}
     if not args.no_decode:
         # INT8 cache, then the same shape with a packed INT4 cache.
         for key, dwl, prof in (("decode", wl.DECODE, "decode_int8_kv_b32_h32.md"),

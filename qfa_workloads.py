@@ -122,6 +122,11 @@ DECODE = DecodeWorkload(
     len_hi=8192, seed=4, kv_qtype="int8", kv_block=256, kv_scale_dtype="f16", q_dtype="f16",
     out_dtype="f16", softmax_scale=_f32(1.0 / math.sqrt(128)))
 
+# The INT8 causal prefill shape with packed INT4 V codes (INT8 Q and K, one
+# scale per 256 keys): the mixed-precision variant of the pages' INT8/INT4 layers.
+INT8QK_INT4V = dataclasses.replace(INT8_CAUSAL, name="int8qk_int4v_causal_h32_s4096",
+                                   v_qtype="int4")
+
 # The decode shape above with a packed INT4 cache (two codes per byte, one
 # fp16 scale per 256-token block): half the cache bytes of INT8.
 DECODE_INT4 = dataclasses.replace(DECODE, name="int4_kv_decode_b32_h32", kv_qtype="int4")

@@ -102,6 +102,7 @@ _ROWS = lambda S: np.unique(np.concatenate([[0, 1, 127, 128, 129, S // 2, S - 2,
     (wl.INT8_CAUSAL, [0, 13, 31]),
     (wl.FP8_ROT, [0, 23]),
     (wl.GQA_INT4, [0, 9, 63]),
+    (wl.INT8QK_INT4V, [0, 17]),
 ], ids=lambda x: getattr(x, "name", None) or str(x))
 def test_full_size_sampled_rows(w, heads):
     """The full workloads in the launch configuration the benchmark times:
