@@ -9,7 +9,8 @@ What it computes is the plain definition of the method, slowly and in the
 open:
 
 * ``quant``      -- symmetric per-block amax quantization to INT8, FP8 e4m3fn or
-                    nibble-packed INT4, with the quotient formed in IEEE fp32;
+                    nibble-packed INT4, with the quotient formed in IEEE fp32,
+                    optionally after an exact rotation rounded once to 16 bits;
 * ``attention``  -- exact softmax attention in float64 on the dequantized values
                     (prefill, causal or not, grouped-query heads);
 * ``decode``     -- one query token against a quantized KV cache of per-sequence
@@ -30,11 +31,12 @@ Pages cited in docstrings (by title and section; titles shortened):
 Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages fix, hand-computed cases, library routines and closed forms.
 """
-from .quant import (QMAX, block_quant, code_values, dequantize, e4m3fn_decode,
-                    e4m3fn_encode, fp16_round, pack_int4, unpack_int4)
+from .quant import (QMAX, bf16_round, block_quant, code_values, dequantize, e4m3fn_decode,
+                    e4m3fn_encode, fp16_round, pack_int4, rotate_block_quant, unpack_int4)
 from .attention import attention, attention_rows, decode
 
 __all__ = [
-    "QMAX", "block_quant", "code_values", "dequantize", "e4m3fn_decode", "e4m3fn_encode",
-    "fp16_round", "pack_int4", "unpack_int4", "attention", "attention_rows", "decode",
+    "QMAX", "bf16_round", "block_quant", "code_values", "dequantize", "e4m3fn_decode",
+    "e4m3fn_encode", "fp16_round", "pack_int4", "rotate_block_quant", "unpack_int4", "attention",
+    "attention_rows", "decode",
 ]

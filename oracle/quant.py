@@ -185,3 +185,34 @@ def dequantize(codes, scales, block_rows: int, qtype: str, layout: str = "bnsd")
     s = np.asarray(scales).astype(np.float64)
     row_scale = np.repeat(s, block_rows, axis=2)[:, :, :S]
     return vals * row_scale[..., None]
+
+
+def bf16_round(y) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (8 significant bits,
+    ties to even, one rounding) and return them as float64. Values are assumed
+    normal in bfloat16 (no overflow or subnormal results)."""
+    y = np.asarray(y, dtype=np.float64)
+    m, e = np.frexp(y)  # y = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def rotate_block_quant(x, w, block_rows: int, qtype: str, in_dtype: str,
+                       scale_dtype: str = "f32", layout: str = "bnsd"):
+    """Rotate, then block-quantize ([MindIE-SD] FP8 attention: Q and K are
+    multiplied by an orthogonal matrix before the dynamic block quantization).
+
+    ``y[..., i] = round16(sum_k x[..., k] * w[i, k])``: the exact product of the
+    16-bit inputs (x and w hold values of ``in_dtype``, "bf16" or "f16"),
+    evaluated in float64, rounded once to ``in_dtype`` (nearest-even); then
+    ``block_quant`` on y. Returns (codes, scales) as ``block_quant`` does.
+    """
+    x64 = np.asarray(_to_f32(x), dtype=np.float64)
+    w64 = np.asarray(_to_f32(w), dtype=np.float64)
+    y = x64 @ w64.T
+    if in_dtype == "bf16":
+        y = bf16_round(y)
+    elif in_dtype == "f16":
+        y = y.astype(np.float16).astype(np.float64)
+    else:
+        raise ValueError(f"unknown input dtype {in_dtype!r}")
+    return block_quant(y.astype(np.float32), block_rows, qtype, scale_dtype, layout)

@@ -202,3 +202,78 @@ def test_dequantize_inverse_layouts():
         assert xh.shape == (1, 2, 130, 64)
         s = np.repeat(scales.astype(np.float64), 64, axis=2)[:, :, :130, None]
         assert np.all(np.abs(xh - x.double().numpy()) <= s * 16 * (1 + 1e-6))
+
+
+# ---- rotation + block quantization ----------------------------------------
+
+def test_bf16_round_matches_torch():
+    """On float32 inputs (one rounding either way) the float64 bf16 rounding
+    agrees with torch's float32 -> bfloat16 conversion (nearest-even)."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(1 << 18) * 10.0 ** rng.integers(-20, 20, 1 << 18)).astype(np.float32)
+    ref = torch.from_numpy(x).bfloat16().double().numpy()
+    np.testing.assert_array_equal(oracle.bf16_round(x.astype(np.float64)), ref)
+
+
+def test_bf16_round_is_one_rounding():
+    """A value just above (below) the midpoint of two adjacent bf16 values goes
+    up (down); the exact midpoint goes to the even neighbour. A detour through
+    float32 would round 'just above' to the midpoint first."""
+    lo = np.array([1.0, 1.5, 3.0, -7.25, 1e-3], dtype=np.float64)
+    lo = oracle.bf16_round(lo)
+    m, e = np.frexp(lo)
+    step = np.ldexp(np.ones_like(lo), e - 8)            # bf16 spacing at lo
+    mid = lo + np.sign(lo) * step / 2
+    up = lo + np.sign(lo) * step
+    eps = np.abs(mid) * 2.0 ** -40
+    np.testing.assert_array_equal(oracle.bf16_round(mid + np.sign(lo) * eps), up)
+    np.testing.assert_array_equal(oracle.bf16_round(mid - np.sign(lo) * eps), lo)
+    # ties to even: of lo and up, the one whose 8-bit significand is even
+    sig_lo = np.rint(np.ldexp(np.frexp(lo)[0], 8)).astype(np.int64)
+    np.testing.assert_array_equal(oracle.bf16_round(mid), np.where(sig_lo % 2 == 0, lo, up))
+
+
+def _rand16(shape, dt, seed):
+    t = torch.from_numpy(np.random.default_rng(seed).standard_normal(shape).astype(np.float32))
+    return t.to(torch.bfloat16 if dt == "bf16" else torch.float16)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("qtype", ["int8", "fp8"])
+def test_rotate_identity_is_block_quant(dt, qtype):
+    x = _rand16((1, 2, 70, 64), dt, 11)
+    eye = np.eye(64, dtype=np.float32)
+    c1, s1 = oracle.rotate_block_quant(x, eye, 32, qtype, dt)
+    c0, s0 = oracle.block_quant(x, 32, qtype)
+    np.testing.assert_array_equal(c1, c0)
+    np.testing.assert_array_equal(s1, s0)
+
+
+def test_rotate_permutation_permutes_channels():
+    x = _rand16((2, 1, 40, 64), "bf16", 12)
+    perm = np.random.default_rng(3).permutation(64)
+    w = np.zeros((64, 64), dtype=np.float32)
+    w[np.arange(64), perm] = 1.0                        # y[..., i] = x[..., perm[i]]
+    c1, s1 = oracle.rotate_block_quant(x, w, 64, "fp8", "bf16", layout="bnsd")
+    c0, s0 = oracle.block_quant(x[..., perm], 64, "fp8")
+    np.testing.assert_array_equal(c1, c0)
+    np.testing.assert_array_equal(s1, s0)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_rotate_rounds_sums_once(dt):
+    """w with two ones per row: y = x_a + x_b exactly, which float32 holds, so
+    torch's float32 -> 16-bit conversion is the single nearest-even rounding
+    the definition asks for; codes and scales must match block_quant of it."""
+    x = _rand16((1, 1, 96, 64), dt, 13)
+    rng = np.random.default_rng(4)
+    a, b = rng.permutation(64), rng.permutation(64)
+    w = np.zeros((64, 64), dtype=np.float32)
+    w[np.arange(64), a] += 1.0
+    w[np.arange(64), b] += 1.0
+    xf = x.float()
+    y = (xf[..., a] + xf[..., b]).to(x.dtype)
+    c1, s1 = oracle.rotate_block_quant(x, w, 32, "int8", dt, layout="bsnd")
+    c0, s0 = oracle.block_quant(y, 32, "int8", layout="bsnd")
+    np.testing.assert_array_equal(c1, c0)
+    np.testing.assert_array_equal(s1, s0)
