@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.qfa_block_quant.restype = i
     L.qfa_block_quant_multi.argtypes = [ctypes.POINTER(QuantJob), i, vp]
     L.qfa_block_quant_multi.restype = i
+    L.qfa_rotate_block_quant.argtypes = [vp, i, vp, i, i, i, i, i, i, i, vp, vp, i, vp]
+    L.qfa_rotate_block_quant.restype = i
     L.qfa_fwd.argtypes = [vp, vp, i, i, i, vp, vp, i, vp, vp, i, i, i,
                           i, i, i, i, i, i, i, i, f, vp, i, vp]
     L.qfa_fwd.restype = i
@@ -191,6 +193,32 @@ def block_quant(x: torch.Tensor, block_rows: int, qtype: str, scale_dtype=torch.
     return codes, scales
 
 
+def rotate_block_quant(x: torch.Tensor, w: torch.Tensor, block_rows: int, qtype: str,
+                       scale_dtype=torch.float32, layout: str = "bnsd", codes=None, scales=None,
+                       stream=None):
+    """y = x . w^T rounded to x's 16-bit type, block-quantized like ``block_quant``;
+    returns (codes, scales). x: [B,N,S,D] (bnsd) or [B,S,N,D] (bsnd), fp16 or
+    bf16; w: [D, D] of the same dtype (pass R^T to rotate by R)."""
+    _dev(x, "x")
+    _dev(w, "w")
+    if layout == "bnsd":
+        B, N, S, D = x.shape
+    else:
+        B, S, N, D = x.shape
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=code_dtype(qtype), device=x.device)
+    if scales is None:
+        scales = torch.empty(B, N, -(-S // block_rows), dtype=scale_dtype, device=x.device)
+    _dev(codes, "codes")
+    _dev(scales, "scales")
+    if w.dtype != x.dtype or tuple(w.shape) != (D, D):
+        raise ValueError("w must be [D, D] with the dtype of x")
+    _check("qfa_rotate_block_quant", lib().qfa_rotate_block_quant(
+        _ptr(x), FLOATS[x.dtype], _ptr(w), B, N, S, D, LAYOUTS[layout], block_rows,
+        QTYPES[qtype], _ptr(codes), _ptr(scales), FLOATS[scales.dtype], _stream(stream)))
+    return codes, scales
+
+
 def _fwd_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, q_qtype, k_qtype, v_qtype,
               q_block, kv_block, softmax_scale, causal, layout, out_dtype, out, stream):
     for t, n in ((q_codes, "q_codes"), (q_scales, "q_scales"), (k_codes, "k_codes"),
@@ -303,6 +331,7 @@ def prepare_decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtyp
     return launch, out
 
 
-__all__ = ["block_quant", "block_quant_multi", "prepare_block_quant_multi", "fwd", "prepare_fwd",
+__all__ = ["block_quant", "block_quant_multi", "prepare_block_quant_multi", "rotate_block_quant",
+           "fwd", "prepare_fwd",
            "decode", "prepare_decode", "decode_workspace_bytes", "lib", "header_functions",
            "QFAError", "QTYPES", "LAYOUTS", "FLOATS", "QMAX", "code_dtype"]

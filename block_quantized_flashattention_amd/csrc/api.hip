@@ -82,6 +82,23 @@ int qfa_block_quant_multi(const qfa_quant_job* jobs, int njobs, void* stream) {
   return from_hip(qfa::launch_block_quant_multi(a, n, (hipStream_t)stream));
 }
 
+int qfa_rotate_block_quant(const void* x, int x_dtype, const void* w, int B, int N, int S, int D,
+                           int layout, int block_rows, int qtype, void* codes, void* scales,
+                           int scale_dtype, void* stream) {
+  const int st = check_quant(x, x_dtype, B, N, S, D, layout, block_rows, qtype, codes, scales,
+                             scale_dtype);
+  if (st != QFA_OK) return st;
+  if ((x_dtype != QFA_F16 && x_dtype != QFA_BF16) || (D != 64 && D != 128) ||
+      qtype == QFA_INT4 || block_rows % 32 != 0 || block_rows > 256)
+    return QFA_ERR_UNSUPPORTED;
+  if ((long)B * N * S == 0) return QFA_OK;
+  if (!w) return QFA_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(codes, 4)) return QFA_ERR_UNSUPPORTED;
+  qfa::RotQuantArgs a{x, x_dtype, w, B, N, S, D, layout, block_rows, qtype, codes, scales,
+                      scale_dtype};
+  return from_hip(qfa::launch_rotate_block_quant(a, (hipStream_t)stream));
+}
+
 int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
             int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
             const void* v_codes, const void* v_scales, int v_qtype, int kv_block,

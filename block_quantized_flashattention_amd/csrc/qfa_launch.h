@@ -27,6 +27,22 @@ hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream);
 // Several tensors, grouped by input and code type into shared launches.
 hipError_t launch_block_quant_multi(const QuantArgs* a, int n, hipStream_t stream);
 
+// Fused rotation + block quantization (16-bit x and w, INT8 or FP8 codes).
+struct RotQuantArgs {
+  const void* x;
+  int x_dtype;
+  const void* w;
+  int B, N, S, D;
+  int layout;
+  int block_rows;
+  int qtype;
+  void* codes;
+  void* scales;
+  int scale_dtype;
+};
+
+hipError_t launch_rotate_block_quant(const RotQuantArgs& a, hipStream_t stream);
+
 struct FwdArgs {
   const void* q;
   const void* qs;

@@ -398,6 +398,182 @@ long prepare(const QuantArgs& a, QuantParams& p) {
   return p.total_blocks;
 }
 
+
+// ---- Fused rotation and block quantization -------------------------------
+// y[row][i] = round16(sum_k x[row][k] * w[i][k]) with x and w in the same
+// 16-bit type (bf16 or fp16) and round16 the nearest-even rounding back to
+// that type, then the block quantizer above on y ([MindIE-SD] FP8 attention
+// pipeline: rotate Q and K, then block-quantize; the rotation is given as
+// w = R^T so that y = x . R). The product runs on the matrix unit as
+// Y^T = W . X^T (v_mfma_f32_32x32x16_{bf16,f16}): W (D x D) is staged in LDS
+// once per workgroup, each lane feeds one row of x straight from memory as
+// the B operand, and each lane ends up holding 16 output channels of one row
+// (4 runs of 4 consecutive channels), which it scales and stores as 4-byte
+// code groups. One workgroup of 4 wavefronts owns one block of R rows
+// (R a multiple of 32, at most 256; wavefront v takes 32-row tiles v, v+4).
+
+struct RotParams {
+  const uint16_t* x;
+  const uint16_t* w;
+  char* codes;
+  void* scales;
+  int N, S, R, nblk;
+  long x_row, x_head, x_batch;  // element strides of x
+  long c_row, c_head, c_batch;  // byte strides of codes
+  int scale_f16;
+};
+
+constexpr int kRotWaves = 4;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mma16(const i32x4& a, const i32x4& b, const f32x16& c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Round to the 16-bit input type and back (the value y takes before quantization).
+template <bool BF16>
+__device__ __forceinline__ float round16(float f) {
+  if constexpr (BF16) return bf16_bits_to_f32(f32_to_bf16_bits(f));
+  return (float)(_Float16)f;
+}
+
+// Four consecutive codes as one dword.
+template <int QT>
+__device__ __forceinline__ uint32_t encode4(const float* t) {
+  if constexpr (QT == QFA_FP8_E4M3) {
+    const float c0 = __builtin_amdgcn_fmed3f(t[0], -448.0f, 448.0f);
+    const float c1 = __builtin_amdgcn_fmed3f(t[1], -448.0f, 448.0f);
+    const float c2 = __builtin_amdgcn_fmed3f(t[2], -448.0f, 448.0f);
+    const float c3 = __builtin_amdgcn_fmed3f(t[3], -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+  } else {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float n = __builtin_amdgcn_fmed3f(__builtin_rintf(t[i]), -128.0f, 127.0f);
+      acc |= ((uint32_t)(int)n & 0xFFu) << (8 * i);
+    }
+    return acc;
+  }
+}
+
+template <int D, bool BF16, int QT, int TPW>
+__global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams p) {
+  constexpr int kStride = D + 8;       // 16-bit elements per staged row of W
+  constexpr int kIB = D / 32;          // 32-channel output blocks
+  constexpr int kKS = D / 16;          // k steps of 16
+  constexpr float kQmax = QT == QFA_FP8_E4M3 ? 448.0f : 127.0f;
+  __shared__ uint16_t ws[D * kStride];
+  __shared__ uint32_t red[kRotWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;  // row of x within a 32-row tile
+  const long blk = blockIdx.x;
+  const int r = (int)(blk % p.nblk);
+  const long bn = blk / p.nblk;
+  const int n = (int)(bn % p.N);
+  const long b = bn / p.N;
+  const int row0 = r * p.R;
+  const int rows = min(p.R, p.S - row0);
+
+  // Stage W (row-major, rows padded) with 16-byte copies.
+  for (int c = threadIdx.x; c < D * D / 8; c += 64 * kRotWaves) {
+    const int i = c / (D / 8), k8 = (c % (D / 8)) * 8;
+    *(uint4*)(ws + i * kStride + k8) = *(const uint4*)(p.w + (long)i * D + k8);
+  }
+  __syncthreads();
+
+  const uint16_t* xb = p.x + b * p.x_batch + (long)n * p.x_head + (long)row0 * p.x_row;
+  f32x16 acc[TPW][kIB];
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tile = wave + kRotWaves * tt;
+    const int trow = tile * 32 + col;  // this lane's row within the block
+    const bool valid = tile * 32 < rows && trow < rows;
+    // B operands: 8 channels of this lane's row per k step (zero past the block).
+    i32x4 xo[kKS];
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+      xo[s] = (i32x4){};
+      if (valid) xo[s] = *(const i32x4*)(xb + (long)trow * p.x_row + 16 * s + 8 * half);
+    }
+#pragma unroll
+    for (int ib = 0; ib < kIB; ++ib) {
+      acc[tt][ib] = (f32x16){};
+      const uint16_t* wrow = ws + (ib * 32 + col) * kStride + 8 * half;
+#pragma unroll
+      for (int s = 0; s < kKS; ++s)
+        acc[tt][ib] = mma16<BF16>(*(const i32x4*)(wrow + 16 * s), xo[s], acc[tt][ib]);
+    }
+#pragma unroll
+    for (int ib = 0; ib < kIB; ++ib)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float y = round16<BF16>(acc[tt][ib][e]);
+        acc[tt][ib][e] = y;
+        amax_bits = max(amax_bits, __float_as_uint(y) & 0x7FFFFFFFu);
+      }
+  }
+  // Block amax: wavefront shuffles, then the four wavefronts through LDS.
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off));
+  if (lane == 0) red[wave] = amax_bits;
+  __syncthreads();
+  amax_bits = max(max(red[0], red[1]), max(red[2], red[3]));
+
+  const float amax = __uint_as_float(amax_bits);
+  float sc = amax / kQmax;
+  if (p.scale_f16) sc = (float)(_Float16)sc;
+  if (threadIdx.x == 0) {
+    const long si = bn * p.nblk + r;
+    if (p.scale_f16) ((uint16_t*)p.scales)[si] = (uint16_t)f32_to_f16_bits(sc);
+    else ((float*)p.scales)[si] = sc;
+  }
+  const bool zero = !(sc != 0.0f);
+  const bool fast = sc >= 0x1p-60f && sc <= 0x1p100f;
+  const float rcp = fast ? 1.0f / sc : 0.0f;
+  char* cb = p.codes + b * p.c_batch + (long)n * p.c_head + (long)row0 * p.c_row;
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tile = wave + kRotWaves * tt;
+    const int trow = tile * 32 + col;
+    if (tile * 32 >= rows || trow >= rows) continue;
+#pragma unroll
+    for (int ib = 0; ib < kIB; ++ib)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // Accumulator registers 4g..4g+3: channels ib*32 + 8g + 4*half + 0..3.
+        float t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = quotient<QT == QFA_FP8_E4M3>(acc[tt][ib][4 * g + i], sc, rcp, fast);
+        *(uint32_t*)(cb + (long)trow * p.c_row + ib * 32 + 8 * g + 4 * half) = zero ? 0u : encode4<QT>(t);
+      }
+  }
+}
+
+template <int D, bool BF16, int QT>
+hipError_t launch_rot_tpw(const RotParams& p, long grid, int tpw, hipStream_t st) {
+  if (tpw == 1) rot_quant_kernel<D, BF16, QT, 1><<<grid, 64 * kRotWaves, 0, st>>>(p);
+  else rot_quant_kernel<D, BF16, QT, 2><<<grid, 64 * kRotWaves, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_rot_qt(const RotParams& p, int qtype, long grid, int tpw, hipStream_t st) {
+  if (qtype == QFA_FP8_E4M3) return launch_rot_tpw<D, BF16, QFA_FP8_E4M3>(p, grid, tpw, st);
+  return launch_rot_tpw<D, BF16, QFA_INT8>(p, grid, tpw, st);
+}
 }  // namespace
 
 hipError_t launch_block_quant_multi(const QuantArgs* a, int n, hipStream_t stream) {
@@ -445,6 +621,43 @@ hipError_t launch_block_quant_multi(const QuantArgs* a, int n, hipStream_t strea
 
 hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream) {
   return launch_block_quant_multi(&a, 1, stream);
+}
+
+hipError_t launch_rotate_block_quant(const RotQuantArgs& a, hipStream_t stream) {
+  RotParams p{};
+  p.x = (const uint16_t*)a.x;
+  p.w = (const uint16_t*)a.w;
+  p.codes = (char*)a.codes;
+  p.scales = a.scales;
+  p.N = a.N;
+  p.S = a.S;
+  p.R = a.block_rows;
+  p.nblk = (a.S + a.block_rows - 1) / a.block_rows;
+  if (a.layout == QFA_BNSD) {
+    p.x_row = a.D;
+    p.x_head = (long)a.S * a.D;
+    p.c_row = a.D;
+    p.c_head = (long)a.S * a.D;
+  } else {
+    p.x_row = (long)a.N * a.D;
+    p.x_head = a.D;
+    p.c_row = (long)a.N * a.D;
+    p.c_head = a.D;
+  }
+  p.x_batch = (long)a.N * a.S * a.D;
+  p.c_batch = (long)a.N * a.S * a.D;
+  p.scale_f16 = a.scale_dtype == QFA_F16;
+  const long grid = (long)a.B * a.N * p.nblk;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  const int tpw = a.block_rows > 32 * kRotWaves ? 2 : 1;
+  const bool bf = a.x_dtype == QFA_BF16;
+  if (a.D == 64) {
+    return bf ? launch_rot_qt<64, true>(p, a.qtype, grid, tpw, stream)
+              : launch_rot_qt<64, false>(p, a.qtype, grid, tpw, stream);
+  }
+  return bf ? launch_rot_qt<128, true>(p, a.qtype, grid, tpw, stream)
+            : launch_rot_qt<128, false>(p, a.qtype, grid, tpw, stream);
 }
 
 }  // namespace qfa

@@ -122,6 +122,32 @@ typedef struct qfa_quant_job {
 QFA_API int qfa_block_quant_multi(const qfa_quant_job* jobs, int njobs, void* stream);
 
 /*
+ * qfa_rotate_block_quant -- rotate, then block-quantize, in one pass
+ * ([MindIE-SD] FP8 attention pipeline: Q and K are multiplied by an
+ * orthogonal matrix before the dynamic block quantization, which spreads
+ * channel outliers; the rotation is applied here inside the quantizer so the
+ * rotated tensor never goes to memory).
+ *
+ *   y[.., row, i] = round16(sum_k x[.., row, k] * w[i][k])
+ *
+ * i.e. y = x . w^T (pass w = R^T to apply y = x . R), with the sum in fp32 on
+ * the matrix unit and round16 the nearest-even rounding to x's 16-bit type;
+ * then y is quantized exactly as qfa_block_quant quantizes a tensor of that
+ * type (same blocks, scales and codes).
+ *
+ *   x          [B,N,S,D] or [B,S,N,D] (layout), dtype x_dtype: F16 or BF16.
+ *   w          [D][D] row-major, same dtype as x, device memory, 16-byte aligned.
+ *   codes      same layout as x, D bytes per row (INT8 or e4m3 codes).
+ *   scales     [B, N, ceil(S/block_rows)] of scale_dtype (F32 or F16).
+ * Limits: as qfa_block_quant, plus D in {64, 128}, block_rows a multiple of
+ * 32 and at most 256, qtype INT8 or FP8_E4M3 (otherwise QFA_ERR_UNSUPPORTED).
+ * Ownership and errors as qfa_block_quant; w is read only.
+ */
+QFA_API int qfa_rotate_block_quant(const void* x, int x_dtype, const void* w, int B, int N, int S,
+                                   int D, int layout, int block_rows, int qtype, void* codes,
+                                   void* scales, int scale_dtype, void* stream);
+
+/*
  * qfa_fwd -- prefill attention forward run on block-quantized codes.
  *
  * Computes, for query row i of head h and key row j of KV head

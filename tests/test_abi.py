@@ -23,8 +23,8 @@ def L():
 def test_exports_every_declared_function(L):
     names = qfa.header_functions()
     assert set(names) == {"qfa_version", "qfa_status_string", "qfa_block_quant",
-                          "qfa_block_quant_multi", "qfa_fwd", "qfa_decode_workspace_bytes",
-                          "qfa_decode"}
+                          "qfa_block_quant_multi", "qfa_rotate_block_quant", "qfa_fwd",
+                          "qfa_decode_workspace_bytes", "qfa_decode"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -80,6 +80,27 @@ def test_block_quant_multi_validation(L):
     assert multi(L, job(S=0, x=None), job(scales=None)) == NULL
     assert multi(L, job(B=0, x=None, codes=None, scales=None)) == OK
     assert multi(L, job(S=0, x=None), job(x=MIS)) == UNSUP
+
+
+def rot(L, x=P, dt=BF16, w=P, B=1, N=2, S=300, D=128, layout=BNSD, R=128, qt=F8, codes=P,
+        scales=P, sdt=F32):
+    return L.qfa_rotate_block_quant(x, dt, w, B, N, S, D, layout, R, qt, codes, scales, sdt, None)
+
+
+def test_rotate_block_quant_validation(L):
+    assert rot(L, dt=7) == ENUM
+    assert rot(L, qt=9) == ENUM
+    assert rot(L, D=12) == SHAPE
+    assert rot(L, R=0) == SHAPE
+    assert rot(L, dt=F32) == UNSUP             # 16-bit inputs only
+    assert rot(L, D=96) == UNSUP
+    assert rot(L, qt=I4) == UNSUP
+    assert rot(L, R=100) == UNSUP              # block rows: multiples of 32, at most 256
+    assert rot(L, R=288) == UNSUP
+    assert rot(L, w=None) == NULL
+    assert rot(L, x=None) == NULL
+    assert rot(L, w=MIS) == UNSUP              # misaligned
+    assert rot(L, S=0, x=None, w=None) == OK   # empty: nothing to do
 
 
 def fwd(L, q=P, qs=P, qqt=I8, qb=128, qsd=F32, k=P, ks=P, kqt=I8, v=P, vs=P, vqt=I8, kb=256,

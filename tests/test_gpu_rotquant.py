@@ -1,0 +1,119 @@
+"""GPU parity of qfa_rotate_block_quant against the oracle's rotation (exact
+product rounded once to 16 bits) followed by block quantization.
+
+The GPU sums the 16-bit products in fp32 on the matrix unit. Where the exact
+product lies within the fp32 error bound of a 16-bit rounding midpoint, either
+neighbour is a correct rounding of a correctly computed sum, so those
+elements ("ambiguous") may differ by one code step; a block whose amax such an
+element could change may get the other scale. Everything else is compared
+byte for byte."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_flashattention_amd as qfa
+import oracle
+import qfa_workloads as wl
+from gpu_util import SDT, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _round16(y, dt):
+    return oracle.bf16_round(y) if dt == "bf16" else y.astype(np.float16).astype(np.float64)
+
+
+def _inputs(B, N, S, D, dt, layout, seed):
+    gen = torch.Generator().manual_seed(seed)
+    x = torch.randn(B, N, S, D, generator=gen, dtype=torch.float64)
+    x[..., :3] *= 20.0  # a few outlier channels, which the rotation spreads
+    rot = wl.random_orthogonal(D, gen)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    x = x.to(tdt)
+    w = rot.t().contiguous().to(tdt)  # y = x . rot = x . w^T
+    if layout == "bsnd":
+        x = x.transpose(1, 2).contiguous()
+    return x, w
+
+
+def _check(x, w, R, qtype, dt, sdt, layout, heads=None):
+    say(f"rotate+quant {tuple(x.shape)} {dt} {qtype} R={R} scales={sdt} {layout} heads={heads}")
+    gc, gs = qfa.rotate_block_quant(x.cuda(), w.cuda(), R, qtype, SDT[sdt], layout)
+    torch.cuda.synchronize()
+    xb = x if layout == "bnsd" else x.transpose(1, 2)
+    gcb = gc.cpu() if layout == "bnsd" else gc.cpu().transpose(1, 2)
+    gsb = gs.cpu()
+    if heads is not None:
+        xb, gcb, gsb = xb[:, heads], gcb[:, heads], gsb[:, heads]
+    xb = xb.contiguous()
+    rc, rs = oracle.rotate_block_quant(xb, w, R, qtype, dt, sdt, "bnsd")
+    gcb = gcb.contiguous().numpy()
+    gsb = gsb.numpy()
+    # Ambiguous elements: the 16-bit rounding of the exact sum moved by a bound
+    # on the fp32 accumulation error. The matrix unit adds D/16 partial sums
+    # of 16 exact products, each rounded to fp32: at most ~(D/16 + 16) roundings
+    # of 2^-24 relative to the sum of |products|; 2^-18 leaves a 4x margin.
+    x64 = xb.double().numpy()
+    w64 = w.double().numpy()
+    y64 = x64 @ w64.T
+    bound = 2.0 ** -18 * (np.abs(x64) @ np.abs(w64).T)
+    amb = _round16(y64 - bound, dt) != _round16(y64 + bound, dt)
+    B, N, S, D = x64.shape
+    nblk = -(-S // R)
+    bad_blocks = 0
+    ok = np.ones(rc.shape, dtype=bool)
+    for b in range(B):
+        for n in range(N):
+            for r in range(nblk):
+                sl = slice(r * R, min(S, (r + 1) * R))
+                same_scale = gsb[b, n, r] == rs[b, n, r]
+                if not same_scale:
+                    # only possible when an ambiguous element can reach the amax
+                    yb = np.abs(_round16(y64[b, n, sl], dt))
+                    alt = np.maximum(np.abs(_round16(y64[b, n, sl] - bound[b, n, sl], dt)),
+                                     np.abs(_round16(y64[b, n, sl] + bound[b, n, sl], dt)))
+                    assert (amb[b, n, sl] & (alt >= yb.max())).any(), (b, n, r, gsb[b, n, r], rs[b, n, r])
+                    bad_blocks += 1
+                    continue
+                gv = oracle.code_values(gcb[b, n, sl], qtype)
+                rv = oracle.code_values(rc[b, n, sl], qtype)
+                diff = gv != rv
+                if diff.any():
+                    assert amb[b, n, sl][diff].all(), "code differs where the rounding is not ambiguous"
+                    # one code step at most
+                    step = np.maximum(np.abs(rv), np.abs(gv))[diff]
+                    tol = 1.0 if qtype == "int8" else np.maximum(step * 2.0 ** -3, 2.0 ** -9)
+                    assert (np.abs(gv - rv)[diff] <= tol).all()
+                ok[b, n, sl] = ~diff
+    nblocks = B * N * nblk
+    say(f"  ambiguous elements {int(amb.sum())} of {amb.size}; code differences {int((~ok).sum())}; "
+        f"blocks with the other scale {bad_blocks} of {nblocks}")
+    assert bad_blocks <= max(1, nblocks // 100)
+
+
+@pytest.mark.parametrize("case", [
+    # B, N, S, D, dtype, R, qtype, scale dtype, layout
+    (1, 2, 300, 128, "bf16", 128, "fp8", "f32", "bnsd"),
+    (2, 1, 200, 64, "f16", 64, "int8", "f16", "bsnd"),
+    (1, 2, 600, 128, "bf16", 256, "fp8", "f32", "bsnd"),
+    (1, 3, 70, 128, "f16", 32, "int8", "f32", "bnsd"),
+], ids=lambda c: "_".join(map(str, c)))
+def test_rotate_block_quant_small(case):
+    B, N, S, D, dt, R, qtype, sdt, layout = case
+    x, w = _inputs(B, N, S, D, dt, layout, seed=B * 1000 + S)
+    _check(x, w, R, qtype, dt, sdt, layout)
+
+
+@pytest.mark.parametrize("R", [128, 256])
+def test_rotate_block_quant_full_size_sampled(R):
+    """The FP8 workload's Q/K shape (2 x 24 heads x 4608 x 128, bf16): the
+    kernel runs on the whole tensor; two heads are checked."""
+    x, w = _inputs(2, 24, 4608, 128, "bf16", "bnsd", seed=R)
+    _check(x, w, R, "fp8", "bf16", "f32", "bnsd", heads=[0, 23])
+
+
+def test_rotate_block_quant_empty():
+    w = torch.eye(128, dtype=torch.bfloat16, device="cuda")
+    x = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device="cuda")
+    c, s = qfa.rotate_block_quant(x, w, 128, "fp8")
+    assert c.shape == (1, 2, 0, 128) and s.shape == (1, 2, 0)
