@@ -119,6 +119,38 @@ def bench_forward(torch, qfa, wl, w, steps, warmup):
     return sum(a.elapsed_time(b) for a, b in evs) / steps
 
 
+def bench_rotate_quant(torch, qfa, wl, steps, warmup):
+    """Fused rotation + FP8 block quantization of Q (128-row blocks) and K
+    (256-row blocks) of the FP8 workload's shape: average time of the pair
+    from per-call HIP events, and the algorithmic bytes (bf16 read once, e4m3
+    codes and fp32 scales written once)."""
+    w = wl.FP8_ROT
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    q = torch.randn(w.B, w.Hq, w.S, w.D, generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn(w.B, w.Hkv, w.S, w.D, generator=gen, device="cuda").to(torch.bfloat16)
+    wt = wl.random_orthogonal(w.D, gen).t().contiguous().to(torch.bfloat16)
+    lq, _, _ = qfa.prepare_rotate_block_quant(q, wt, w.q_block, "fp8")
+    lk, _, _ = qfa.prepare_rotate_block_quant(k, wt, w.kv_block, "fp8")
+
+    def pair():
+        lq()
+        lk()
+    settle(torch, pair)
+    for _ in range(warmup):
+        pair()
+    torch.cuda.synchronize()
+    evs = [_events(torch) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        pair()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nq, nk = q.numel(), k.numel()
+    nbytes = 3 * (nq + nk) + 4 * (w.B * w.Hq * -(-w.S // w.q_block) + w.B * w.Hkv * -(-w.S // w.kv_block))
+    return w, ms, nbytes
+
+
 def bench_decode(torch, qfa, wl, w, steps, warmup):
     q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
     sdt = torch.float16
@@ -279,6 +311,14 @@ def main():
                                             "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                                             "frac": round(mtops / PEAK_INT8_TOPS, 4),
                                             "traffic": None}}
+    rw, rms, rbytes = bench_rotate_quant(torch, qfa, wl, args.steps, args.warmup)
+    rgbs = rbytes / (rms * 1e-3) / 1e9
+    log(f"rotate+quantize Q/K of {rw.name}: {rms:.3f} ms, {rgbs:.0f} GB/s")
+    rec["rotate_quantize"] = {"workload": rw.name, "ms": round(rms, 4), "bytes": rbytes,
+                              "roofline": {"bound": "hbm", "achieved": round(rgbs, 1),
+                                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                           "frac": round(rgbs / PEAK_HBM_GBS, 4),
+                                           "traffic": None}}
     if not args.no_decode:
         # INT8 cache, then the same shape with a packed INT4 cache.
         for key, dwl, prof in (("decode", wl.DECODE, "decode_int8_kv_b32_h32.md"),

@@ -199,6 +199,16 @@ def rotate_block_quant(x: torch.Tensor, w: torch.Tensor, block_rows: int, qtype:
     """y = x . w^T rounded to x's 16-bit type, block-quantized like ``block_quant``;
     returns (codes, scales). x: [B,N,S,D] (bnsd) or [B,S,N,D] (bsnd), fp16 or
     bf16; w: [D, D] of the same dtype (pass R^T to rotate by R)."""
+    launch, codes, scales = prepare_rotate_block_quant(x, w, block_rows, qtype, scale_dtype,
+                                                       layout, codes, scales, stream)
+    launch()
+    return codes, scales
+
+
+def prepare_rotate_block_quant(x: torch.Tensor, w: torch.Tensor, block_rows: int, qtype: str,
+                               scale_dtype=torch.float32, layout: str = "bnsd", codes=None,
+                               scales=None, stream=None):
+    """Marshal one ``rotate_block_quant`` call once; returns (launch, codes, scales)."""
     _dev(x, "x")
     _dev(w, "w")
     if layout == "bnsd":
@@ -213,10 +223,13 @@ def rotate_block_quant(x: torch.Tensor, w: torch.Tensor, block_rows: int, qtype:
     _dev(scales, "scales")
     if w.dtype != x.dtype or tuple(w.shape) != (D, D):
         raise ValueError("w must be [D, D] with the dtype of x")
-    _check("qfa_rotate_block_quant", lib().qfa_rotate_block_quant(
-        _ptr(x), FLOATS[x.dtype], _ptr(w), B, N, S, D, LAYOUTS[layout], block_rows,
-        QTYPES[qtype], _ptr(codes), _ptr(scales), FLOATS[scales.dtype], _stream(stream)))
-    return codes, scales
+    args = (_ptr(x), FLOATS[x.dtype], _ptr(w), B, N, S, D, LAYOUTS[layout], block_rows,
+            QTYPES[qtype], _ptr(codes), _ptr(scales), FLOATS[scales.dtype], _stream(stream))
+    f = lib().qfa_rotate_block_quant
+
+    def launch():
+        _check("qfa_rotate_block_quant", f(*args))
+    return launch, codes, scales
 
 
 def _fwd_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, q_qtype, k_qtype, v_qtype,
@@ -332,6 +345,6 @@ def prepare_decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtyp
 
 
 __all__ = ["block_quant", "block_quant_multi", "prepare_block_quant_multi", "rotate_block_quant",
-           "fwd", "prepare_fwd",
+           "prepare_rotate_block_quant", "fwd", "prepare_fwd",
            "decode", "prepare_decode", "decode_workspace_bytes", "lib", "header_functions",
            "QFAError", "QTYPES", "LAYOUTS", "FLOATS", "QMAX", "code_dtype"]
