@@ -10,7 +10,8 @@ open:
 
 * ``quant``      -- symmetric per-block amax quantization to INT8, FP8 e4m3fn or
                     nibble-packed INT4, with the quotient formed in IEEE fp32,
-                    optionally after an exact rotation rounded once to 16 bits;
+                    optionally after an exact rotation rounded once to 16 bits,
+                    and the append of one token into a quantized KV cache;
 * ``attention``  -- exact softmax attention in float64 on the dequantized values
                     (prefill, causal or not, grouped-query heads);
 * ``decode``     -- one query token against a quantized KV cache of per-sequence
@@ -32,11 +33,13 @@ Every function here is pinned by ``tests/test_oracle_*.py`` against values the
 pages fix, hand-computed cases, library routines and closed forms.
 """
 from .quant import (QMAX, bf16_round, block_quant, code_values, dequantize, e4m3fn_decode,
-                    e4m3fn_encode, fp16_round, pack_int4, rotate_block_quant, unpack_int4)
+                    e4m3fn_encode, fp16_round, kv_append, pack_int4, quantize_with_scale,
+                    rotate_block_quant, unpack_int4)
 from .attention import attention, attention_rows, decode
 
 __all__ = [
     "QMAX", "bf16_round", "block_quant", "code_values", "dequantize", "e4m3fn_decode",
-    "e4m3fn_encode", "fp16_round", "pack_int4", "rotate_block_quant", "unpack_int4", "attention",
+    "e4m3fn_encode", "fp16_round", "kv_append", "pack_int4", "quantize_with_scale",
+    "rotate_block_quant", "unpack_int4", "attention",
     "attention_rows", "decode",
 ]

@@ -216,3 +216,75 @@ def rotate_block_quant(x, w, block_rows: int, qtype: str, in_dtype: str,
     else:
         raise ValueError(f"unknown input dtype {in_dtype!r}")
     return block_quant(y.astype(np.float32), block_rows, qtype, scale_dtype, layout)
+
+
+def quantize_with_scale(values, s: float, qtype: str) -> np.ndarray:
+    """Codes of float32 ``values`` for a given scale ``s``: step 5 of the
+    definition above (``t = fl32(x / s)``, round half to even, clamp, or the
+    e4m3fn encoding); all-zero codes when s is 0. INT4 codes are returned
+    unpacked (int8 values in [-8, 7])."""
+    v = np.asarray(values, dtype=np.float32)
+    if not s != 0:
+        return (np.zeros(v.shape, np.uint8) if qtype == "fp8" else np.zeros(v.shape, np.int8))
+    t = (v / np.float32(s)).astype(np.float32)
+    if qtype == "int8":
+        return np.clip(np.rint(t), -128, 127).astype(np.int8)
+    if qtype == "int4":
+        return np.clip(np.rint(t), -8, 7).astype(np.int8)
+    return e4m3fn_encode(np.clip(t, np.float32(-448.0), np.float32(448.0)))
+
+
+def kv_append(codes, scales, x, positions, kv_block: int, qtype: str, scale_dtype: str = "f16",
+              layout: str = "bnsd"):
+    """Quantize one new token per sequence into an INT8 or packed-INT4 KV cache
+    ([Ascend-INT8] section 3: the decode cache is stored quantized, so a new
+    token is quantized into it; the block-scale update is this reading).
+
+    codes [B,H,S_max,D] (INT4: D/2 packed bytes) and scales [B,H,ceil(S_max/R)]
+    are the cache; x [B,H,D] holds the new key (or value) rows; token b goes to
+    row ``positions[b]`` (a row outside [0, S_max) leaves sequence b alone).
+    For the block r = p // R holding row p, with old rows [rR, p):
+
+    * if the block has old rows, its scale s is nonzero and fl32(max|x| / s)
+      <= qmax (or x is all zero), x is quantized with s and nothing else
+      changes;
+    * otherwise the block is requantized as one block: the old rows' values
+      fl32(code * s) together with x go through ``block_quant`` (a new scale
+      from their amax, new codes for every row of the block up to p).
+
+    Returns new (codes, scales) arrays in the input layout; rows past p are
+    not touched.
+    """
+    c = _to_bnsd(np.array(codes), layout).copy()
+    sc = np.array(scales).copy()
+    xv = np.asarray(_to_f32(x), dtype=np.float32)
+    B, H, S_max = c.shape[0], c.shape[1], c.shape[2]
+    R = kv_block
+    qmax = np.float32(QMAX[qtype])
+    for b in range(B):
+        p = int(positions[b])
+        if p < 0 or p >= S_max:
+            continue
+        r, row0 = p // R, (p // R) * R
+        for h in range(H):
+            xr = xv[b, h]
+            ax = np.float32(np.abs(xr).max()) if xr.size else np.float32(0)
+            fits = False
+            s_old = np.float32(sc[b, h, r])
+            if p > row0:
+                if s_old > 0:
+                    fits = bool(np.float32(ax / s_old) <= qmax)
+                else:
+                    fits = bool(ax == 0)
+            if fits:
+                q = quantize_with_scale(xr, s_old, qtype)
+                c[b, h, p] = pack_int4(q[None])[0] if qtype == "int4" else q
+                continue
+            old = code_values(c[b, h, row0:p], qtype).astype(np.float32)
+            vals = np.concatenate([(old * s_old).astype(np.float32), xr[None]], axis=0)
+            nc, ns = block_quant(vals[None, None], p + 1 - row0, qtype, scale_dtype)
+            c[b, h, row0:p + 1] = nc[0, 0]
+            sc[b, h, r] = ns[0, 0, 0]
+    if layout == "bsnd":
+        c = np.ascontiguousarray(c.transpose(0, 2, 1, 3))
+    return c, sc

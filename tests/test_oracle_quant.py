@@ -277,3 +277,78 @@ def test_rotate_rounds_sums_once(dt):
     c0, s0 = oracle.block_quant(y, 32, "int8", layout="bsnd")
     np.testing.assert_array_equal(c1, c0)
     np.testing.assert_array_equal(s1, s0)
+
+
+# ---- quantizing into an existing scale; KV-cache append --------------------
+
+@pytest.mark.parametrize("qtype", ["int8", "int4", "fp8"])
+def test_quantize_with_scale_matches_block_quant(qtype):
+    x = np.random.default_rng(21).standard_normal((1, 1, 40, 32)).astype(np.float32) * 3
+    c, s = oracle.block_quant(x, 40, qtype)
+    q = oracle.quantize_with_scale(x, s[0, 0, 0], qtype)
+    if qtype == "int4":
+        q = pack_int4(q)
+    np.testing.assert_array_equal(q, c)
+
+
+def _cache(B, H, S, D, R, qtype, sdt="f16"):
+    codes = np.zeros((B, H, S, D // 2 if qtype == "int4" else D),
+                     dtype=np.int8 if qtype == "int8" else np.uint8)
+    scales = np.zeros((B, H, -(-S // R)), dtype=np.float16 if sdt == "f16" else np.float32)
+    return codes, scales
+
+
+@pytest.mark.parametrize("qtype,R", [("int8", 16), ("int4", 1), ("int4", 8)])
+def test_kv_append_first_row_of_a_block_is_block_quant(qtype, R):
+    rng = np.random.default_rng(22)
+    codes, scales = _cache(2, 3, 40, 16, R, qtype)
+    x = rng.standard_normal((2, 3, 16)).astype(np.float32)
+    pos = np.array([R * 2, 0])
+    c, s = oracle.kv_append(codes, scales, x, pos, R, qtype)
+    for b in range(2):
+        ref_c, ref_s = oracle.block_quant(x[b][:, None, :][None], 1, qtype, "f16")
+        np.testing.assert_array_equal(c[b, :, pos[b]], ref_c[0, :, 0])
+        np.testing.assert_array_equal(s[b, :, pos[b] // R], ref_s[0, :, 0])
+
+
+@pytest.mark.parametrize("qtype", ["int8", "int4"])
+def test_kv_append_rows_that_fit_equal_block_quant(qtype):
+    """Row 0 holds the block's largest value, so every later row fits its scale
+    and the appended block equals block_quant of the rows at once."""
+    rng = np.random.default_rng(23)
+    R, D = 8, 16
+    rows = rng.standard_normal((R, D)).astype(np.float32)
+    rows[0, 3] = 10.0
+    codes, scales = _cache(1, 1, R, D, R, qtype)
+    for p in range(R):
+        codes, scales = oracle.kv_append(codes, scales, rows[p][None, None], [p], R, qtype)
+    ref_c, ref_s = oracle.block_quant(rows[None, None], R, qtype, "f16")
+    np.testing.assert_array_equal(codes, ref_c)
+    np.testing.assert_array_equal(scales, ref_s)
+
+
+def test_kv_append_raising_the_amax_requantizes_the_block():
+    rng = np.random.default_rng(24)
+    R, D = 8, 16
+    rows = rng.standard_normal((4, D)).astype(np.float32)
+    codes, scales = _cache(1, 1, R, D, R, "int8", "f32")
+    for p in range(3):
+        codes, scales = oracle.kv_append(codes, scales, rows[p][None, None], [p], R, "int8", "f32")
+    big = rows[3] * 0 + 0.5
+    big[5] = 50.0                                        # far above the block's amax
+    c, s = oracle.kv_append(codes, scales, big[None, None], [3], R, "int8", "f32")
+    assert s[0, 0, 0] == np.float32(np.float32(50.0) / np.float32(127.0))
+    assert c[0, 0, 3, 5] == 127                          # the new maximum reaches qmax
+    # old rows: block_quant of their dequantized fp32 values together with the new row
+    old = (codes[0, 0, :3].astype(np.float32) * scales[0, 0, 0]).astype(np.float32)
+    ref_c, ref_s = oracle.block_quant(np.concatenate([old, big[None]])[None, None], 4, "int8")
+    np.testing.assert_array_equal(c[0, 0, :4], ref_c[0, 0])
+    np.testing.assert_array_equal(c[0, 0, 4:], 0)        # rows past the new one untouched
+
+
+def test_kv_append_out_of_range_position_changes_nothing():
+    codes, scales = _cache(2, 1, 16, 16, 8, "int8")
+    x = np.ones((2, 1, 16), np.float32)
+    c, s = oracle.kv_append(codes, scales, x, [16, -1], 8, "int8")
+    np.testing.assert_array_equal(c, codes)
+    np.testing.assert_array_equal(s, scales)
