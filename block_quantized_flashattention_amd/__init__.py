@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.qfa_block_quant.restype = i
     L.qfa_block_quant_multi.argtypes = [ctypes.POINTER(QuantJob), i, vp]
     L.qfa_block_quant_multi.restype = i
+    L.qfa_kv_append.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    L.qfa_kv_append.restype = i
     L.qfa_rotate_block_quant.argtypes = [vp, i, vp, i, i, i, i, i, i, i, vp, vp, i, vp]
     L.qfa_rotate_block_quant.restype = i
     L.qfa_fwd.argtypes = [vp, vp, i, i, i, vp, vp, i, vp, vp, i, i, i,
@@ -190,6 +192,23 @@ def block_quant(x: torch.Tensor, block_rows: int, qtype: str, scale_dtype=torch.
     _check("qfa_block_quant", lib().qfa_block_quant(
         _ptr(x), FLOATS[x.dtype], B, N, S, D, LAYOUTS[layout], block_rows, QTYPES[qtype],
         _ptr(codes), _ptr(scales), FLOATS[scales.dtype], _stream(stream)))
+    return codes, scales
+
+
+def kv_append(x: torch.Tensor, positions: torch.Tensor, codes: torch.Tensor,
+              scales: torch.Tensor, kv_block: int, qtype: str, layout: str = "bnsd",
+              stream=None):
+    """Quantize x [B, H, D] into the cache (codes, scales) at row positions[b]
+    of each sequence, in place (see qfa_kv_append); returns (codes, scales)."""
+    for t, n in ((x, "x"), (positions, "positions"), (codes, "codes"), (scales, "scales")):
+        _dev(t, n)
+    if positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    B, H, D = x.shape
+    S_max = codes.shape[2] if layout == "bnsd" else codes.shape[1]
+    _check("qfa_kv_append", lib().qfa_kv_append(
+        _ptr(x), FLOATS[x.dtype], _ptr(positions), _ptr(codes), _ptr(scales), B, H, S_max, D,
+        LAYOUTS[layout], kv_block, QTYPES[qtype], FLOATS[scales.dtype], _stream(stream)))
     return codes, scales
 
 
@@ -345,6 +364,6 @@ def prepare_decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtyp
 
 
 __all__ = ["block_quant", "block_quant_multi", "prepare_block_quant_multi", "rotate_block_quant",
-           "prepare_rotate_block_quant", "fwd", "prepare_fwd",
+           "prepare_rotate_block_quant", "kv_append", "fwd", "prepare_fwd",
            "decode", "prepare_decode", "decode_workspace_bytes", "lib", "header_functions",
            "QFAError", "QTYPES", "LAYOUTS", "FLOATS", "QMAX", "code_dtype"]

@@ -99,6 +99,24 @@ int qfa_rotate_block_quant(const void* x, int x_dtype, const void* w, int B, int
   return from_hip(qfa::launch_rotate_block_quant(a, (hipStream_t)stream));
 }
 
+int qfa_kv_append(const void* x, int x_dtype, const int32_t* positions, void* codes, void* scales,
+                  int B, int H, int S_max, int D, int layout, int kv_block, int qtype,
+                  int scale_dtype, void* stream) {
+  if (!valid_float(x_dtype) || !valid_layout(layout) || !valid_qtype(qtype) ||
+      (scale_dtype != QFA_F32 && scale_dtype != QFA_F16))
+    return QFA_ERR_ENUM;
+  if (B < 0 || H < 0 || S_max < 1 || D < 8 || D % 8 != 0 || kv_block < 1) return QFA_ERR_SHAPE;
+  if (qtype == QFA_FP8_E4M3 || D > (qtype == QFA_INT4 ? 512 : 256)) return QFA_ERR_UNSUPPORTED;
+  if ((long)B * H == 0) return QFA_OK;
+  if (!x || !positions || !codes || !scales) return QFA_ERR_NULL;
+  if (!aligned(x, x_dtype == QFA_F32 ? 4 : 2) || !aligned(positions, 4) ||
+      !aligned(scales, scale_dtype == QFA_F16 ? 2 : 4))
+    return QFA_ERR_UNSUPPORTED;
+  qfa::AppendArgs a{x, x_dtype, positions, codes, scales, B, H, S_max, D, layout, kv_block, qtype,
+                    scale_dtype};
+  return from_hip(qfa::launch_kv_append(a, (hipStream_t)stream));
+}
+
 int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
             int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
             const void* v_codes, const void* v_scales, int v_qtype, int kv_block,

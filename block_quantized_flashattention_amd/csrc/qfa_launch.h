@@ -43,6 +43,22 @@ struct RotQuantArgs {
 
 hipError_t launch_rotate_block_quant(const RotQuantArgs& a, hipStream_t stream);
 
+// One new row per sequence into a quantized KV cache (INT8 or packed INT4).
+struct AppendArgs {
+  const void* x;
+  int x_dtype;
+  const int32_t* positions;
+  void* codes;
+  void* scales;
+  int B, H, S_max, D;
+  int layout;
+  int kv_block;
+  int qtype;
+  int scale_dtype;
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+
 struct FwdArgs {
   const void* q;
   const void* qs;

@@ -574,6 +574,132 @@ hipError_t launch_rot_qt(const RotParams& p, int qtype, long grid, int tpw, hipS
   if (qtype == QFA_FP8_E4M3) return launch_rot_tpw<D, BF16, QFA_FP8_E4M3>(p, grid, tpw, st);
   return launch_rot_tpw<D, BF16, QFA_INT8>(p, grid, tpw, st);
 }
+
+// ---- Appending one token to a quantized KV cache -------------------------
+// One workgroup per (batch, KV head) puts the new row at position p of the
+// sequence into block r = p / R. When the block already has rows, a nonzero
+// scale s and fl32(max|x| / s) <= qmax (or x is all zero), only the new row is
+// quantized, with s. Otherwise the block is requantized as a whole: its old
+// rows' values fl32(code * s) and the new row get a new scale from their
+// amax and new codes (rows past p are not touched).
+
+struct AppendParams {
+  const void* x;  // [B, H, D]
+  const int32_t* pos;
+  char* codes;
+  void* scales;
+  int H, S_max, D, R, nblk;
+  long c_row, c_head, c_batch;  // byte strides of codes
+  int x_dtype, scale_f16;
+};
+
+constexpr int kAppendThreads = 256;
+
+__device__ __forceinline__ float load_value(const void* x, long i, int dt) {
+  if (dt == QFA_F32) return ((const float*)x)[i];
+  const uint32_t h = ((const uint16_t*)x)[i];
+  return dt == QFA_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+}
+
+// Workgroup max of an unsigned value (every thread calls it; one barrier pair).
+__device__ __forceinline__ uint32_t wg_max(uint32_t m, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __syncthreads();  // red may still be read from a previous call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int w = 0; w < kAppendThreads / 64; ++w) r = max(r, red[w]);
+  return r;
+}
+
+template <int QT>
+__device__ __forceinline__ uint32_t code_bits(float t) {
+  constexpr float lo = QT == QFA_INT4 ? -8.0f : -128.0f, hi = QT == QFA_INT4 ? 7.0f : 127.0f;
+  return (uint32_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(t), lo, hi) & (QT == QFA_INT4 ? 0xFu : 0xFFu);
+}
+
+template <int QT>
+__device__ __forceinline__ int code_value(uint32_t bits) {
+  return QT == QFA_INT4 ? (int)(bits << 28) >> 28 : (int)(bits << 24) >> 24;
+}
+
+template <int QT>
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams p) {
+  constexpr int kPer = QT == QFA_INT4 ? 2 : 1;  // channels per code byte
+  constexpr float kQmax = QT == QFA_INT4 ? 7.0f : 127.0f;
+  __shared__ uint32_t red[kAppendThreads / 64];
+  const int bh = blockIdx.x;
+  const int b = bh / p.H, h = bh % p.H;
+  const int pp = p.pos[b];
+  if (pp < 0 || pp >= p.S_max) return;  // the whole workgroup leaves
+  const int r = pp / p.R, row0 = r * p.R, nold = pp - row0;
+  const int tid = threadIdx.x;
+  const int nbytes = p.D / kPer;  // code bytes per row
+
+  // The new row: this thread's code byte holds channels kPer*tid .. + kPer-1.
+  float xv[kPer];
+  uint32_t ax = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    xv[j] = 0.0f;
+    if (tid < nbytes) xv[j] = load_value(p.x, ((long)b * p.H + h) * p.D + kPer * tid + j, p.x_dtype);
+    ax = max(ax, __float_as_uint(xv[j]) & 0x7FFFFFFFu);
+  }
+  ax = wg_max(ax, red);
+  const float amax_x = __uint_as_float(ax);
+  const long si = (long)bh * p.nblk + r;
+  const float s_old = nold == 0 ? 0.0f
+                      : p.scale_f16 ? f16_bits_to_f32(((const uint16_t*)p.scales)[si])
+                                    : ((const float*)p.scales)[si];
+  bool fits = false;
+  if (nold > 0) fits = s_old > 0.0f ? amax_x / s_old <= kQmax : amax_x == 0.0f;
+  char* cb = p.codes + (long)b * p.c_batch + (long)h * p.c_head;
+
+  float s = s_old;
+  if (!fits) {
+    // amax of the old rows' values: fl32(max|code| * s_old), fl32 being monotonic
+    uint32_t mc = 0;
+    for (int e = tid; e < nold * nbytes; e += kAppendThreads) {
+      const uint32_t byte = (uint8_t)cb[(long)(row0 + e / nbytes) * p.c_row + e % nbytes];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) mc = max(mc, (uint32_t)abs(code_value<QT>(byte >> (4 * j))));
+    }
+    mc = wg_max(mc, red);
+    const float amax = fmaxf(amax_x, nold > 0 ? (float)mc * s_old : 0.0f);
+    s = amax / kQmax;
+    if (p.scale_f16) s = (float)(_Float16)s;
+    if (tid == 0) {
+      if (p.scale_f16) ((uint16_t*)p.scales)[si] = (uint16_t)f32_to_f16_bits(s);
+      else ((float*)p.scales)[si] = s;
+    }
+  }
+  const bool zero = !(s != 0.0f);
+  const bool fast = s >= 0x1p-60f && s <= 0x1p100f;
+  const float rcp = fast ? 1.0f / s : 0.0f;
+  if (!fits) {
+    // Requantize the old rows in place (each byte read and written by one thread).
+    for (int e = tid; e < nold * nbytes; e += kAppendThreads) {
+      char* cp = cb + (long)(row0 + e / nbytes) * p.c_row + e % nbytes;
+      const uint32_t byte = (uint8_t)*cp;
+      uint32_t out = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const float v = (float)code_value<QT>(byte >> (4 * j)) * s_old;
+        out |= (zero ? 0u : code_bits<QT>(quotient<false>(v, s, rcp, fast))) << (4 * j);
+      }
+      *cp = (char)out;
+    }
+  }
+  if (tid < nbytes) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      out |= (zero ? 0u : code_bits<QT>(quotient<false>(xv[j], s, rcp, fast))) << (4 * j);
+    cb[(long)pp * p.c_row + tid] = (char)out;
+  }
+}
 }  // namespace
 
 hipError_t launch_block_quant_multi(const QuantArgs* a, int n, hipStream_t stream) {
@@ -621,6 +747,37 @@ hipError_t launch_block_quant_multi(const QuantArgs* a, int n, hipStream_t strea
 
 hipError_t launch_block_quant(const QuantArgs& a, hipStream_t stream) {
   return launch_block_quant_multi(&a, 1, stream);
+}
+
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
+  AppendParams p{};
+  p.x = a.x;
+  p.pos = a.positions;
+  p.codes = (char*)a.codes;
+  p.scales = a.scales;
+  p.H = a.H;
+  p.S_max = a.S_max;
+  p.D = a.D;
+  p.R = a.kv_block;
+  p.nblk = (a.S_max + a.kv_block - 1) / a.kv_block;
+  const long cD = a.qtype == QFA_INT4 ? a.D / 2 : a.D;
+  if (a.layout == QFA_BNSD) {
+    p.c_row = cD;
+    p.c_head = (long)a.S_max * cD;
+  } else {
+    p.c_row = (long)a.H * cD;
+    p.c_head = cD;
+  }
+  p.c_batch = (long)a.H * a.S_max * cD;
+  p.x_dtype = a.x_dtype;
+  p.scale_f16 = a.scale_dtype == QFA_F16;
+  const long grid = (long)a.B * a.H;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  if (a.qtype == QFA_INT4) kv_append_kernel<QFA_INT4><<<grid, kAppendThreads, 0, stream>>>(p);
+  else kv_append_kernel<QFA_INT8><<<grid, kAppendThreads, 0, stream>>>(p);
+  return hipGetLastError();
 }
 
 hipError_t launch_rotate_block_quant(const RotQuantArgs& a, hipStream_t stream) {

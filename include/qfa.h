@@ -143,6 +143,36 @@ QFA_API int qfa_block_quant_multi(const qfa_quant_job* jobs, int njobs, void* st
  * 32 and at most 256, qtype INT8 or FP8_E4M3 (otherwise QFA_ERR_UNSUPPORTED).
  * Ownership and errors as qfa_block_quant; w is read only.
  */
+/*
+ * qfa_kv_append -- quantize one new row per sequence into an INT8 or packed
+ * INT4 KV cache ([Ascend-INT8] section 3: decode keeps the KV cache
+ * quantized, so each new key and value row is quantized into it).
+ *
+ * Row positions[b] of sequence b (for every KV head) receives x[b, h, :].
+ * In its block r = positions[b] / kv_block, with old rows r*kv_block ..
+ * positions[b]-1:
+ *   - if the block has old rows, a nonzero scale s and fl32(max|x| / s) <=
+ *     qmax (or x is all zero), x is quantized with s (as qfa_block_quant
+ *     quantizes with a given scale) and nothing else changes;
+ *   - otherwise the block is requantized: the old rows' values fl32(code * s)
+ *     and x get a new scale fl32(amax / qmax) (rounded to fp16 for fp16
+ *     scales) and new codes, written in place. Rows after positions[b] are
+ *     never touched.
+ *
+ *   x          [B, H, D] of x_dtype (F32/F16/BF16), device memory.
+ *   positions  [B] int32, device memory; a position outside [0, S_max)
+ *              leaves that sequence unchanged.
+ *   codes      cache [B,H,S_max,D] or [B,S_max,H,D] (layout), INT8 bytes or
+ *              packed INT4 (D/2 bytes per row), updated in place.
+ *   scales     [B, H, ceil(S_max/kv_block)] of scale_dtype, updated in place.
+ * Limits: B,H >= 0; S_max >= 1; D % 8 == 0, 8 <= D <= 256 (INT8) or 512
+ * (INT4); kv_block >= 1; qtype INT8 or INT4 (FP8: QFA_ERR_UNSUPPORTED).
+ * Two calls that touch the same block must be ordered on one stream.
+ */
+QFA_API int qfa_kv_append(const void* x, int x_dtype, const int32_t* positions, void* codes,
+                          void* scales, int B, int H, int S_max, int D, int layout, int kv_block,
+                          int qtype, int scale_dtype, void* stream);
+
 QFA_API int qfa_rotate_block_quant(const void* x, int x_dtype, const void* w, int B, int N, int S,
                                    int D, int layout, int block_rows, int qtype, void* codes,
                                    void* scales, int scale_dtype, void* stream);

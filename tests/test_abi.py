@@ -23,7 +23,8 @@ def L():
 def test_exports_every_declared_function(L):
     names = qfa.header_functions()
     assert set(names) == {"qfa_version", "qfa_status_string", "qfa_block_quant",
-                          "qfa_block_quant_multi", "qfa_rotate_block_quant", "qfa_fwd",
+                          "qfa_block_quant_multi", "qfa_rotate_block_quant", "qfa_kv_append",
+                          "qfa_fwd",
                           "qfa_decode_workspace_bytes", "qfa_decode"}
     for n in names:
         assert hasattr(L, n), n
@@ -101,6 +102,27 @@ def test_rotate_block_quant_validation(L):
     assert rot(L, x=None) == NULL
     assert rot(L, w=MIS) == UNSUP              # misaligned
     assert rot(L, S=0, x=None, w=None) == OK   # empty: nothing to do
+
+
+def app(L, x=P, dt=F16, pos=P, codes=P, scales=P, B=2, H=4, S=512, D=128, layout=BNSD, R=256,
+        qt=I8, sdt=F16):
+    return L.qfa_kv_append(x, dt, pos, codes, scales, B, H, S, D, layout, R, qt, sdt, None)
+
+
+def test_kv_append_validation(L):
+    assert app(L, dt=7) == ENUM
+    assert app(L, qt=9) == ENUM
+    assert app(L, sdt=BF16) == ENUM
+    assert app(L, S=0) == SHAPE
+    assert app(L, D=12) == SHAPE
+    assert app(L, R=0) == SHAPE
+    assert app(L, qt=F8) == UNSUP
+    assert app(L, D=264) == UNSUP
+    assert app(L, D=520, qt=I4) == UNSUP
+    assert app(L, pos=None) == NULL
+    assert app(L, scales=None) == NULL
+    assert app(L, scales=ctypes.c_void_p(257)) == UNSUP
+    assert app(L, B=0, x=None, pos=None, codes=None, scales=None) == OK
 
 
 def fwd(L, q=P, qs=P, qqt=I8, qb=128, qsd=F32, k=P, ks=P, kqt=I8, v=P, vs=P, vqt=I8, kb=256,
