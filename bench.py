@@ -151,6 +151,41 @@ def bench_rotate_quant(torch, qfa, wl, steps, warmup):
     return w, ms, nbytes
 
 
+def bench_kv_append(torch, qfa, wl, steps, warmup):
+    """One decode step's cache update on the decode workload's shape: the new K
+    and V rows of every sequence quantized into INT8 caches (fp16 scales per
+    256 rows), at positions inside existing blocks. Average time of the pair
+    from per-call HIP events."""
+    w = wl.DECODE
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    kc = torch.randint(-127, 128, (w.B, w.Hkv, w.S_max, w.D), generator=gen, device="cuda",
+                       dtype=torch.int8)
+    vc = kc.clone()
+    nblk = -(-w.S_max // w.kv_block)
+    ks = torch.full((w.B, w.Hkv, nblk), 0.05, dtype=torch.float16, device="cuda")
+    vs = ks.clone()
+    pos = torch.randint(w.len_lo, w.len_hi, (w.B,), generator=gen, device="cuda",
+                        dtype=torch.int32)
+    xk = torch.randn(w.B, w.Hkv, w.D, generator=gen, device="cuda").to(torch.float16)
+    xv = torch.randn(w.B, w.Hkv, w.D, generator=gen, device="cuda").to(torch.float16)
+    ak = qfa.kv_append(xk, pos, kc, ks, w.kv_block, "int8", prepare=True)
+    av = qfa.kv_append(xv, pos, vc, vs, w.kv_block, "int8", prepare=True)
+
+    def pair():
+        ak()
+        av()
+    for _ in range(warmup + 5):
+        pair()
+    torch.cuda.synchronize()
+    evs = [_events(torch) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        pair()
+        b.record()
+    torch.cuda.synchronize()
+    return w, sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
 def bench_decode(torch, qfa, wl, w, steps, warmup):
     q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
     sdt = torch.float16
@@ -319,6 +354,11 @@ def main():
                                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                            "frac": round(rgbs / PEAK_HBM_GBS, 4),
                                            "traffic": None}}
+    aw, ams = bench_kv_append(torch, qfa, wl, args.steps, args.warmup)
+    log(f"kv append (K and V of {aw.B} x {aw.Hkv} heads): {ams * 1e3:.1f} us")
+    rec["kv_append"] = {"workload": aw.name, "ms": round(ams, 4),
+                        "note": "latency of one decode step's K and V row appends (two launches); "
+                                "no roofline: a few KB per call"}
     if not args.no_decode:
         # INT8 cache, then the same shape with a packed INT4 cache.
         for key, dwl, prof in (("decode", wl.DECODE, "decode_int8_kv_b32_h32.md"),

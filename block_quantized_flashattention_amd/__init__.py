@@ -197,18 +197,24 @@ def block_quant(x: torch.Tensor, block_rows: int, qtype: str, scale_dtype=torch.
 
 def kv_append(x: torch.Tensor, positions: torch.Tensor, codes: torch.Tensor,
               scales: torch.Tensor, kv_block: int, qtype: str, layout: str = "bnsd",
-              stream=None):
+              stream=None, prepare: bool = False):
     """Quantize x [B, H, D] into the cache (codes, scales) at row positions[b]
-    of each sequence, in place (see qfa_kv_append); returns (codes, scales)."""
+    of each sequence, in place (see qfa_kv_append); returns (codes, scales), or
+    with ``prepare=True`` a launcher that repeats the marshalled call."""
     for t, n in ((x, "x"), (positions, "positions"), (codes, "codes"), (scales, "scales")):
         _dev(t, n)
     if positions.dtype != torch.int32:
         raise ValueError("positions must be int32")
     B, H, D = x.shape
     S_max = codes.shape[2] if layout == "bnsd" else codes.shape[1]
-    _check("qfa_kv_append", lib().qfa_kv_append(
-        _ptr(x), FLOATS[x.dtype], _ptr(positions), _ptr(codes), _ptr(scales), B, H, S_max, D,
-        LAYOUTS[layout], kv_block, QTYPES[qtype], FLOATS[scales.dtype], _stream(stream)))
+    args = (_ptr(x), FLOATS[x.dtype], _ptr(positions), _ptr(codes), _ptr(scales), B, H, S_max, D,
+            LAYOUTS[layout], kv_block, QTYPES[qtype], FLOATS[scales.dtype], _stream(stream))
+    f = lib().qfa_kv_append
+    if prepare:
+        def launch():
+            _check("qfa_kv_append", f(*args))
+        return launch
+    _check("qfa_kv_append", f(*args))
     return codes, scales
 
 
