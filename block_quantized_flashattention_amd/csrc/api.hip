@@ -175,6 +175,9 @@ int qfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D, const 
   if (D != 64 && D != 128) return QFA_ERR_UNSUPPORTED;
   if (kv_qtype == QFA_FP8_E4M3) return QFA_ERR_UNSUPPORTED;
   if (Hq / Hkv > 16) return QFA_ERR_UNSUPPORTED;
+  // The kernel addresses the rows of one (batch, KV head) with 32-bit offsets.
+  const long row_stride = (layout == QFA_BNSD ? 1L : (long)Hkv) * (kv_qtype == QFA_INT4 ? D / 2 : D);
+  if (((long)S_max + qfa::kDecodeChunk) * row_stride > INT32_MAX) return QFA_ERR_UNSUPPORTED;
   if (B == 0) return QFA_OK;
   if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f || softmax_scale > 3.0e38f)
     return QFA_ERR_SHAPE;

@@ -19,8 +19,12 @@
 //     issued four at a time ahead of their use.
 //   * Two passes per 128 tokens: all scores first (a per-lane partial dot
 //     product, then a DPP butterfly over the LPT lanes of the token), their
-//     max, then exp2 and the V accumulation; every lane accumulates o for its
-//     own channels over its own tokens and the token groups are summed once.
+//     max, then exp2 and the V accumulation. The first V loads are issued
+//     while the last keys are scored, so their latency overlaps that work.
+//     Every lane accumulates o for its own channels over its own tokens; the
+//     token groups are then summed by a reduce-scatter across the lanes (each
+//     exchange halves what a lane holds), which leaves every lane a slice of
+//     the channel sums to write.
 //   * With an fp16 query, INT8 K codes are converted exactly to packed fp16
 //     (the byte goes into the mantissa of 1024 + byte) and dotted with
 //     v_dot2_f32_f16 (fp32 accumulation); V codes are converted with the
@@ -129,8 +133,46 @@ __device__ __forceinline__ void chunk_to_f32(const uint4& w, float* f) {
   }
 }
 
+// Sums v[0..N) over the lanes that differ only in the lane bits OFF, 2*OFF,
+// ..., 32, leaving each lane one slice of the sums: every step halves the
+// values a lane holds, sending one half to its partner and adding the half it
+// receives (a reduce-scatter; log2(64/OFF) steps, N - N*OFF/64 exchanges).
+// The lane then holds the sums of channels scatter_base(lane) + [0, N*OFF/64).
+template <int OFF, int N>
+__device__ __forceinline__ void sum_scatter(float* v, int lane) {
+  if constexpr (OFF < 64) {
+    constexpr int H = N / 2;
+    const bool up = (lane & OFF) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float send = up ? v[i] : v[i + H];
+      const float keep = up ? v[i + H] : v[i];
+      v[i] = keep + __shfl_xor(send, OFF);
+    }
+    sum_scatter<OFF * 2, H>(v, lane);
+  }
+}
+template <int OFF, int N>
+__device__ __forceinline__ int scatter_base(int lane) {
+  if constexpr (OFF < 64) {
+    return ((lane & OFF) ? N / 2 : 0) + scatter_base<OFF * 2, N / 2>(lane);
+  } else {
+    return 0;
+  }
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero. The last word is the gfx9 default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
+}
+
 template <int D, bool INT4, bool QF16, bool BLOCK_SCALE>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams p) {
+// Packed INT4 with an fp16 query and block scales asks for six wavefronts per
+// SIMD, i.e. three workgroups per CU (at most 80 VGPRs): its rows are half as
+// long, so more of them must be in flight to cover the HBM latency.
+__global__ __launch_bounds__(64 * kDecWaves, INT4 && QF16 && BLOCK_SCALE ? 6 : 2)
+void decode_split_kernel(DecParams p) {
   constexpr int kRowBytes = INT4 ? D / 2 : D;
   constexpr int LPT = kRowBytes / 16;        // lanes per token
   constexpr int EPL = INT4 ? 32 : 16;        // channels per lane
@@ -139,6 +181,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
   constexpr int NG = NSUB / kGroup;
   constexpr float kOff = INT4 ? 8.0f : 128.0f;
   static_assert(NSUB % kGroup == 0, "load groups");
+  constexpr int NF = EPL / (64 / LPT);  // channels per lane after the token-group reduction
+  static_assert(NF >= 1 && EPL % (64 / LPT) == 0, "reduce-scatter");
   __shared__ float red_m[kDecWaves], red_l[kDecWaves];
   __shared__ float red_o[kDecWaves][D];
 
@@ -176,8 +220,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
   }
 
   const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
-  const uint8_t* kp = p.k + cbase + dc * 16;
-  const uint8_t* vp = p.v + cbase + dc * 16;
   const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
 
   const int t_begin = split * kDecodeChunk + wave * kWaveTokens;
@@ -199,17 +241,32 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
     // ---- scores: sc[j] for token t_begin + j*TPS + tg (log2 units) ----
     float sc[NSUB];
     uint4 kw[2][kGroup];
+    // Rows [0, L) of this (batch, KV head) through buffer resources: one
+    // 32-bit offset per lane (the host keeps every offset below 2^31), and
+    // rows at or past L read as zero, so no clamp is needed (their scores
+    // are masked).
+    const int span = (L - 1) * (int)p.c_row + kRowBytes;
+    const auto krs = rows_rsrc(p.k + cbase, span);
+    const auto vrs = rows_rsrc(p.v + cbase, span);
+    const int loff = (t_begin + tg) * (int)p.c_row + dc * 16;
+    auto bload = [&](__amdgpu_buffer_rsrc_t rs, int j) {
+      const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, loff + j * TPS * (int)p.c_row, 0, 0);
+      return make_uint4(r[0], r[1], r[2], r[3]);
+    };
     auto kload = [&](uint4* dst, int g) {
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const int t = min(t_begin + (g * kGroup + i) * TPS + tg, t_last);
-        dst[i] = *(const uint4*)(kp + (long)t * p.c_row);
-      }
+      for (int i = 0; i < kGroup; ++i) dst[i] = bload(krs, g * kGroup + i);
+    };
+    uint4 vw[2][kGroup];
+    auto vload = [&](uint4* dst, int g) {
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) dst[i] = bload(vrs, g * kGroup + i);
     };
     kload(kw[0], 0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g + 1 < NG) kload(kw[(g + 1) & 1], g + 1);
+      else vload(vw[0], 0);  // first V group, in flight while the last keys are scored
 #pragma unroll
       for (int i = 0; i < kGroup; ++i) {
         const int j = g * kGroup + i;
@@ -261,15 +318,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
     for (int off = LPT; off < 64; off <<= 1) m_blk = fmaxf(m_blk, __shfl_xor(m_blk, off));
 
     // ---- values ----
-    uint4 vw[2][kGroup];
-    auto vload = [&](uint4* dst, int g) {
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const int t = min(t_begin + (g * kGroup + i) * TPS + tg, t_last);
-        dst[i] = *(const uint4*)(vp + (long)t * p.c_row);
-      }
-    };
-    vload(vw[0], 0);
     float lp[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -344,12 +392,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
     for (int off = LPT; off < 64; off <<= 1) {
       l_blk += __shfl_xor(l_blk, off);
       wsum += __shfl_xor(wsum, off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], off);
     }
+    sum_scatter<LPT, EPL>(o, lane);
     constexpr float kOffV = kI4H ? 1032.0f : kOff;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = (o[e] - kOffV * wsum) * sv_blk;
+    for (int e = 0; e < NF; ++e) o[e] = (o[e] - kOffV * wsum) * sv_blk;
   }
 
   // Merge the wavefronts of the workgroup.
@@ -357,9 +404,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecParams 
     red_m[wave] = m_blk;
     red_l[wave] = l_blk;
   }
-  if (lane < LPT) {
+  {
+    const int base = scatter_base<LPT, EPL>(lane);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) red_o[wave][d0 + e] = o[e];
+    for (int e = 0; e < NF; ++e) red_o[wave][d0 + base + e] = o[e];
   }
   __syncthreads();
   if (wave != 0) return;

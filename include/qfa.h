@@ -238,7 +238,10 @@ QFA_API size_t qfa_decode_workspace_bytes(int B, int Hq, int S_max, int D);
  *   workspace  device buffer of at least qfa_decode_workspace_bytes(B,Hq,S_max,D)
  *              bytes; its contents on entry do not matter. Calls that share a
  *              workspace must be ordered on one stream.
- * Limits: D in {64, 128}; Hq % Hkv == 0; 1 <= Hq/Hkv <= 16.
+ * Limits: D in {64, 128}; Hq % Hkv == 0; 1 <= Hq/Hkv <= 16;
+ * (S_max + 1024) * row_stride < 2^31, where row_stride is the bytes between
+ * consecutive tokens of one head (D, or D/2 for INT4; times Hkv in BSND).
+ * Outside these limits the call returns QFA_ERR_UNSUPPORTED.
  */
 QFA_API int qfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D, const void* k_cache,
                const void* v_cache, const void* k_scales, const void* v_scales, int kv_qtype,

@@ -170,6 +170,11 @@ def test_decode_validation(L):
     assert dec(L, D=32) == UNSUP
     assert dec(L, qt=F8) == UNSUP
     assert dec(L, Hq=64, Hkv=2) == UNSUP
+    # Rows of one (batch, KV head) must stay within 32-bit byte offsets:
+    # (S_max + 1024) * row_stride < 2^31 (row_stride = Hkv * D in BSND).
+    assert dec(L, B=0, layout=BSND, Hq=16, Hkv=16, S_max=(1 << 20) - 1024) == UNSUP
+    assert dec(L, B=0, layout=BSND, Hq=16, Hkv=16, S_max=(1 << 20) - 1025) == OK
+    assert dec(L, B=0, layout=BSND, Hq=16, Hkv=16, S_max=(1 << 20) - 1024, qt=I4) == OK
     assert dec(L, lens=None) == NULL
     assert dec(L, ws=None) == WS
     assert dec(L, wsb=need - 1) == WS
