@@ -408,9 +408,11 @@ long prepare(const QuantArgs& a, QuantParams& p) {
 // Y^T = W . X^T (v_mfma_f32_32x32x16_{bf16,f16}): W (D x D) is staged in LDS
 // once per workgroup, each lane feeds one row of x straight from memory as
 // the B operand, and each lane ends up holding 16 output channels of one row
-// (4 runs of 4 consecutive channels), which it scales and stores as 4-byte
-// code groups. One workgroup of 4 wavefronts owns one block of R rows
-// (R a multiple of 32, at most 256; wavefront v takes 32-row tiles v, v+4).
+// (4 runs of 4 consecutive channels), which it scales and writes as 4-byte
+// code groups into LDS (over W, once every wavefront is done with it); the
+// block's rows then leave with coalesced 16-byte stores. One workgroup of 4
+// wavefronts owns one block of R rows (R a multiple of 32, at most 256;
+// wavefront v takes 32-row tiles v, v+4).
 
 struct RotParams {
   const uint16_t* x;
@@ -421,6 +423,7 @@ struct RotParams {
   long x_row, x_head, x_batch;  // element strides of x
   long c_row, c_head, c_batch;  // byte strides of codes
   int scale_f16;
+  int c16;  // codes and row stride 16-byte aligned
 };
 
 constexpr int kRotWaves = 4;
@@ -471,7 +474,9 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
   constexpr int kIB = D / 32;          // 32-channel output blocks
   constexpr int kKS = D / 16;          // k steps of 16
   constexpr float kQmax = QT == QFA_FP8_E4M3 ? 448.0f : 127.0f;
-  __shared__ uint16_t ws[D * kStride];
+  constexpr int kCS = D + 4;            // bytes per row of the staged codes
+  constexpr int kWsElems = D * kStride > 256 * kCS / 2 ? D * kStride : 256 * kCS / 2;
+  __shared__ __align__(16) uint16_t ws[kWsElems];
   __shared__ uint32_t red[kRotWaves];
 
   const int lane = threadIdx.x & 63;
@@ -544,11 +549,15 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
   const bool fast = sc >= 0x1p-60f && sc <= 0x1p100f;
   const float rcp = fast ? 1.0f / sc : 0.0f;
   char* cb = p.codes + b * p.c_batch + (long)n * p.c_head + (long)row0 * p.c_row;
+  // The codes go through LDS (W is no longer read: every wavefront passed the
+  // barrier above after its last matrix instruction), rows padded to D + 4
+  // bytes so that the 32 rows of a wavefront's 4-byte writes hit distinct
+  // banks; then each row is written with 16-byte (or 4-byte) coalesced stores.
+  uint8_t* cs = (uint8_t*)ws;
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    const int tile = wave + kRotWaves * tt;
-    const int trow = tile * 32 + col;
-    if (tile * 32 >= rows || trow >= rows) continue;
+    const int trow = (wave + kRotWaves * tt) * 32 + col;
+    if (trow >= rows) continue;
 #pragma unroll
     for (int ib = 0; ib < kIB; ++ib)
 #pragma unroll
@@ -557,8 +566,21 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
         float t[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) t[i] = quotient<QT == QFA_FP8_E4M3>(acc[tt][ib][4 * g + i], sc, rcp, fast);
-        *(uint32_t*)(cb + (long)trow * p.c_row + ib * 32 + 8 * g + 4 * half) = zero ? 0u : encode4<QT>(t);
+        *(uint32_t*)(cs + trow * kCS + ib * 32 + 8 * g + 4 * half) = zero ? 0u : encode4<QT>(t);
       }
+  }
+  __syncthreads();
+  if (p.c16) {
+    for (int q = threadIdx.x; q < rows * (D / 16); q += 64 * kRotWaves) {
+      const int row = q / (D / 16), c = q % (D / 16);
+      const uint32_t* src = (const uint32_t*)(cs + row * kCS + c * 16);
+      *(uint4*)(cb + (long)row * p.c_row + c * 16) = make_uint4(src[0], src[1], src[2], src[3]);
+    }
+  } else {
+    for (int q = threadIdx.x; q < rows * (D / 4); q += 64 * kRotWaves) {
+      const int row = q / (D / 4), c = q % (D / 4);
+      *(uint32_t*)(cb + (long)row * p.c_row + c * 4) = *(const uint32_t*)(cs + row * kCS + c * 4);
+    }
   }
 }
 
@@ -804,6 +826,7 @@ hipError_t launch_rotate_block_quant(const RotQuantArgs& a, hipStream_t stream) 
   p.x_batch = (long)a.N * a.S * a.D;
   p.c_batch = (long)a.N * a.S * a.D;
   p.scale_f16 = a.scale_dtype == QFA_F16;
+  p.c16 = ((uintptr_t)a.codes % 16 == 0) && (p.c_row % 16 == 0) && (p.c_head % 16 == 0) && (p.c_batch % 16 == 0);
   const long grid = (long)a.B * a.N * p.nblk;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
