@@ -50,6 +50,9 @@
 //   * XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
 //     all query heads and row blocks of one (batch, KV head) are given ids on
 //     the same XCD and its K/V codes stay in that XCD's L2.
+//   * Epilogue: a lane holds 64 channels of one row, so direct stores would
+//     touch 32 rows per instruction; fp16/bf16 output is staged in LDS per
+//     wavefront and written with 16-byte stores along the rows.
 #include <type_traits>
 
 #include "qfa_device.h"
@@ -666,8 +669,44 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
 
   // Epilogue: lane holds row qrow, channels 32*db + 8*(r/4) + 4*half + (r%4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!qvalid) return;
   const float inv = (TOK ? 1.0f : sv_cur) / l_tot;
+  if (p.out_dtype != QFA_F32) {
+    // 16-bit output goes through LDS (the V buffers: every wavefront passed
+    // the last step's barrier after its last read of them), one 32-row region
+    // per wavefront, and leaves with 16-byte stores along the rows.
+    constexpr int kOS = D + 8;  // 16-bit elements per staged row
+    uint16_t* so = reinterpret_cast<uint16_t*>(&vst[0]) + wave * 32 * kOS;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = db * 32 + 8 * rg + 4 * half;
+        const float v0 = o[db][4 * rg] * inv, v1 = o[db][4 * rg + 1] * inv;
+        const float v2 = o[db][4 * rg + 2] * inv, v3 = o[db][4 * rg + 3] * inv;
+        uint32_t w0, w1;
+        if (p.out_dtype == QFA_F16) {
+          w0 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)v0, (_Float16)v1});
+          w1 = __builtin_bit_cast(uint32_t, (f16x2){(_Float16)v2, (_Float16)v3});
+        } else {
+          w0 = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+          w1 = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+        }
+        *(uint2*)(so + col * kOS + d0) = make_uint2(w0, w1);
+      }
+    }
+    __syncthreads();
+    const long hbase = (long)b * p.o_batch + (long)h * p.o_head;
+    constexpr int kCPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int q = lane; q < 32 * kCPR; q += 64) {
+      const int row = q / kCPR, c = q % kCPR;
+      if (wrow0 + row < p.Sq)
+        *(uint4*)((uint16_t*)p.out + hbase + (long)(wrow0 + row) * p.o_row + c * 8) =
+            *(const uint4*)(so + row * kOS + c * 8);
+    }
+    return;
+  }
+  if (!qvalid) return;
   const long obase = (long)b * p.o_batch + (long)h * p.o_head + (long)qrow * p.o_row;
 #pragma unroll
   for (int db = 0; db < kDB; ++db) {
