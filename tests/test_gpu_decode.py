@@ -87,3 +87,54 @@ def test_full_size_decode_sampled(w):
     sample[0] = (int(torch.argmax(lens)), 0)
     sample[1] = (int(torch.argmin(lens)), w.Hkv - 1)
     _run(w, q.cpu(), k, v, lens.cpu(), sample=sample)
+
+
+@pytest.mark.parametrize("qt,R", [("int8", 256), ("int4", 256), ("int4", 1)])
+@pytest.mark.parametrize("layout", ["bnsd", "bsnd"])
+def test_rows_past_length_are_ignored(qt, R, layout):
+    """Cache rows at and past each sequence's length hold stale codes (random
+    bytes) and the scales of blocks that start past it are NaN: the output
+    must depend on the rows before the length only."""
+    w = wl.DecodeWorkload(name=f"stale_{qt}_r{R}", B=3, Hq=4, Hkv=2, D=128, S_max=2600,
+                          len_lo=2600, len_hi=2600, seed=77, kv_qtype=qt, kv_block=R,
+                          kv_scale_dtype="f16", q_dtype="f16", out_dtype="f16",
+                          softmax_scale=float(np.float32(1 / np.sqrt(128))))
+    lens = [1, 1100, 2583]
+    say(f"decode stale rows {w.name} {layout} lens={lens}")
+    q, k, v, _ = wl.make_decode_inputs(w)
+    kd, vd = k.cuda(), v.cuda()
+    if layout == "bsnd":
+        kd, vd = kd.transpose(1, 2).contiguous(), vd.transpose(1, 2).contiguous()
+    kc, ks = qfa.block_quant(kd, R, qt, torch.float16, layout)
+    vc, vs = qfa.block_quant(vd, R, qt, torch.float16, layout)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for b, L in enumerate(lens):
+        for c in (kc, vc):
+            rows = c[b, :, L:] if layout == "bnsd" else c[b, L:]
+            rows.copy_(torch.randint(-128, 128, rows.shape, generator=g, device="cuda",
+                                     dtype=torch.int16).to(torch.int8))
+        nb = -(-L // R)
+        ks[b, :, nb:] = float("nan")
+        vs[b, :, nb:] = float("nan")
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    out = qfa.decode(q.cuda(), kc, vc, ks, vs, lens_t.cuda(), kv_qtype=qt, kv_block=R,
+                     softmax_scale=w.softmax_scale, layout=layout, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for b, L in enumerate(lens):
+        nb = -(-L // R)
+        for kvh in range(w.Hkv):
+            if layout == "bnsd":
+                kcs = kc[b:b + 1, kvh:kvh + 1, :L].cpu().numpy()
+                vcs = vc[b:b + 1, kvh:kvh + 1, :L].cpu().numpy()
+            else:
+                kcs = kc[b:b + 1, :L, kvh:kvh + 1].cpu().numpy()
+                vcs = vc[b:b + 1, :L, kvh:kvh + 1].cpu().numpy()
+            kss = ks[b:b + 1, kvh:kvh + 1, :nb].cpu().numpy()
+            vss = vs[b:b + 1, kvh:kvh + 1, :nb].cpu().numpy()
+            kh = oracle.dequantize(kcs, kss, R, qt, layout)
+            vh = oracle.dequantize(vcs, vss, R, qt, layout)
+            grp = slice(kvh * 2, kvh * 2 + 2)
+            ref.append(oracle.decode(q[b:b + 1, grp].double().numpy(), kh, vh, [L], w.softmax_scale))
+            got.append(out[b:b + 1, grp].double().cpu().numpy())
+    assert_close(np.concatenate(got), np.concatenate(ref), f"{w.name} stale rows")
