@@ -65,12 +65,6 @@ struct DecParams {
   float scale_log2;
 };
 
-__device__ __forceinline__ float load_q(const void* q, long i, int dt) {
-  if (dt == QFA_F32) return ((const float*)q)[i];
-  const uint32_t hb = ((const uint16_t*)q)[i];
-  return dt == QFA_F16 ? f16_bits_to_f32(hb) : bf16_bits_to_f32(hb);
-}
-
 __device__ __forceinline__ void store_out(void* out, long i, float v, int dt) {
   if (dt == QFA_F32) ((float*)out)[i] = v;
   else if (dt == QFA_F16) ((uint16_t*)out)[i] = (uint16_t)f32_to_f16_bits(v);
@@ -200,23 +194,48 @@ void decode_split_kernel(DecParams p) {
   const int d0 = dc * EPL;
 
   // This lane's query channels: fp16 pairs for the dot2 path, else floats.
+  // The dtype is decided once, outside the loads: a per-element dtype switch
+  // between dependent conversions serialized the loads' latencies.
   const long qoff = (long)b * p.q_batch + (long)h * p.q_head;
   f16x2 qh[EPL / 2];
   float qf[EPL];
   float qsum = 0.0f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    qf[e] = load_q(p.q, qoff + d0 + e, p.q_dtype);
-    qsum += qf[e];
-  }
   // Packed INT4 keys are read as channel pairs (e, e + 4) of each group of 8
   // (the nibbles one shift-and-mask isolates); INT8 keys as (2e, 2e + 1).
   constexpr bool kI4H = INT4 && QF16;
+  if constexpr (QF16) {
+    // fp16 query: the pairs straight from its dwords (channels 2i, 2i + 1).
+    uint32_t qw[EPL / 2];
+    const uint32_t* qp = (const uint32_t*)((const uint16_t*)p.q + qoff + d0);
 #pragma unroll
-  for (int e = 0; e < EPL / 2; ++e) {
-    const int c0 = kI4H ? 8 * (e / 4) + (e % 4) : 2 * e;
-    const int c1 = kI4H ? c0 + 4 : 2 * e + 1;
-    qh[e] = (f16x2){(_Float16)qf[c0], (_Float16)qf[c1]};
+    for (int i = 0; i < EPL / 2; ++i) {
+      qw[i] = qp[i];
+      qsum += f16_bits_to_f32(qw[i] & 0xFFFFu);
+      qsum += f16_bits_to_f32(qw[i] >> 16);
+    }
+#pragma unroll
+    for (int e = 0; e < EPL / 2; ++e) {
+      if constexpr (kI4H) {
+        // Channels c and c + 4 (c = 8(e/4) + e%4) share the half of dwords c/2 and c/2 + 2.
+        const int c0 = 8 * (e / 4) + (e % 4);
+        const uint32_t sel = (c0 & 1) ? 0x07060302u : 0x05040100u;
+        qh[e] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(qw[c0 / 2 + 2], qw[c0 / 2], sel));
+      } else {
+        qh[e] = __builtin_bit_cast(f16x2, qw[e]);
+      }
+    }
+  } else if (p.q_dtype == QFA_F32) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      qf[e] = ((const float*)p.q)[qoff + d0 + e];
+      qsum += qf[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      qf[e] = bf16_bits_to_f32(((const uint16_t*)p.q)[qoff + d0 + e]);
+      qsum += qf[e];
+    }
   }
 
   const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
