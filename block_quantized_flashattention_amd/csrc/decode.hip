@@ -194,49 +194,52 @@ void decode_split_kernel(DecParams p) {
   const int d0 = dc * EPL;
 
   // This lane's query channels: fp16 pairs for the dot2 path, else floats.
-  // The dtype is decided once, outside the loads: a per-element dtype switch
-  // between dependent conversions serialized the loads' latencies.
+  // The loads are issued here and used only after the first keys are
+  // requested, and the dtype is decided once, outside the loads (a
+  // per-element switch between dependent conversions serialized the loads'
+  // latencies).
   const long qoff = (long)b * p.q_batch + (long)h * p.q_head;
   f16x2 qh[EPL / 2];
   float qf[EPL];
   float qsum = 0.0f;
+  uint32_t qw[QF16 ? EPL / 2 : 1];
+  if constexpr (QF16) {
+    const uint32_t* qp = (const uint32_t*)((const uint16_t*)p.q + qoff + d0);
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) qw[i] = qp[i];
+  } else if (p.q_dtype == QFA_F32) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] = ((const float*)p.q)[qoff + d0 + e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] = bf16_bits_to_f32(((const uint16_t*)p.q)[qoff + d0 + e]);
+  }
   // Packed INT4 keys are read as channel pairs (e, e + 4) of each group of 8
   // (the nibbles one shift-and-mask isolates); INT8 keys as (2e, 2e + 1).
   constexpr bool kI4H = INT4 && QF16;
-  if constexpr (QF16) {
-    // fp16 query: the pairs straight from its dwords (channels 2i, 2i + 1).
-    uint32_t qw[EPL / 2];
-    const uint32_t* qp = (const uint32_t*)((const uint16_t*)p.q + qoff + d0);
+  auto prep_q = [&]() {
+    if constexpr (QF16) {
 #pragma unroll
-    for (int i = 0; i < EPL / 2; ++i) {
-      qw[i] = qp[i];
-      qsum += f16_bits_to_f32(qw[i] & 0xFFFFu);
-      qsum += f16_bits_to_f32(qw[i] >> 16);
-    }
-#pragma unroll
-    for (int e = 0; e < EPL / 2; ++e) {
-      if constexpr (kI4H) {
-        // Channels c and c + 4 (c = 8(e/4) + e%4) share the half of dwords c/2 and c/2 + 2.
-        const int c0 = 8 * (e / 4) + (e % 4);
-        const uint32_t sel = (c0 & 1) ? 0x07060302u : 0x05040100u;
-        qh[e] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(qw[c0 / 2 + 2], qw[c0 / 2], sel));
-      } else {
-        qh[e] = __builtin_bit_cast(f16x2, qw[e]);
+      for (int i = 0; i < EPL / 2; ++i) {
+        qsum += f16_bits_to_f32(qw[i] & 0xFFFFu);
+        qsum += f16_bits_to_f32(qw[i] >> 16);
       }
-    }
-  } else if (p.q_dtype == QFA_F32) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      qf[e] = ((const float*)p.q)[qoff + d0 + e];
-      qsum += qf[e];
-    }
-  } else {
+      for (int e = 0; e < EPL / 2; ++e) {
+        if constexpr (kI4H) {
+          // Channels c and c + 4 (c = 8(e/4) + e%4) share the half of dwords c/2 and c/2 + 2.
+          const int c0 = 8 * (e / 4) + (e % 4);
+          const uint32_t sel = (c0 & 1) ? 0x07060302u : 0x05040100u;
+          qh[e] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(qw[c0 / 2 + 2], qw[c0 / 2], sel));
+        } else {
+          qh[e] = __builtin_bit_cast(f16x2, qw[e]);
+        }
+      }
+    } else {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      qf[e] = bf16_bits_to_f32(((const uint16_t*)p.q)[qoff + d0 + e]);
-      qsum += qf[e];
+      for (int e = 0; e < EPL; ++e) qsum += qf[e];
     }
-  }
+  };
 
   const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
   const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
@@ -252,11 +255,6 @@ void decode_split_kernel(DecParams p) {
   float sk_blk = 1.0f, sv_blk = 1.0f;
 
   if (t_begin < t_end) {
-    if constexpr (BLOCK_SCALE) {
-      sk_blk = load_scale(p.ks, sbase + t_begin / p.kv_block, p.kv_scale_f16);
-      sv_blk = load_scale(p.vs, sbase + t_begin / p.kv_block, p.kv_scale_f16);
-    }
-    const float csk = p.scale_log2 * sk_blk;
     // ---- scores: sc[j] for token t_begin + j*TPS + tg (log2 units) ----
     float sc[NSUB];
     uint4 kw[2][kGroup];
@@ -282,6 +280,12 @@ void decode_split_kernel(DecParams p) {
       for (int i = 0; i < kGroup; ++i) dst[i] = bload(vrs, g * kGroup + i);
     };
     kload(kw[0], 0);
+    if constexpr (BLOCK_SCALE) {
+      sk_blk = load_scale(p.ks, sbase + t_begin / p.kv_block, p.kv_scale_f16);
+      sv_blk = load_scale(p.vs, sbase + t_begin / p.kv_block, p.kv_scale_f16);
+    }
+    prep_q();
+    const float csk = p.scale_log2 * sk_blk;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g + 1 < NG) kload(kw[(g + 1) & 1], g + 1);

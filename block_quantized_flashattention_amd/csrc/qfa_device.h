@@ -42,10 +42,16 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
-// Load a scale stored as fp32 or fp16.
+// Load a scale stored as fp32 or fp16: one dword load (for fp16, the aligned
+// dword that holds it) and a select, no branch. A branch around the load
+// makes the compiler wait for it, and for every load issued before it, at
+// the merge point.
 __device__ __forceinline__ float load_scale(const void* p, long idx, bool f16) {
-  if (f16) return f16_bits_to_f32(((const uint16_t*)p)[idx]);
-  return ((const float*)p)[idx];
+  const long off = f16 ? idx * 2 : idx * 4;
+  const int mis = f16 ? (int)(((uintptr_t)p + (uintptr_t)off) & 2u) : 0;
+  const uint32_t w = *(const uint32_t*)((const char*)p + (off - mis));
+  const float h = f16_bits_to_f32((w >> (8 * mis)) & 0xFFFFu);
+  return f16 ? h : __uint_as_float(w);
 }
 
 }  // namespace qfa
