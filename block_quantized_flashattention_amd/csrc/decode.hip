@@ -469,32 +469,60 @@ void decode_split_kernel(DecParams p) {
 }
 
 // Log-sum-exp merge of the chunk partials of one (batch, head) per wavefront.
+// Lane s reads chunk s's (max, sum) for up to 64 chunks at a time, so those
+// loads are issued together; the weighted sums then read each chunk's o with
+// its weight taken from the lane that holds it.
 template <int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(DecParams p) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
+  const int lane = threadIdx.x;
   const int L = min(max(p.lens[b], 1), p.S_max);
   const int nsplit = (L + kDecodeChunk - 1) / kDecodeChunk;
   if (nsplit <= 1) return;
   const float* part = p.ws + ((long)b * p.Hq + h) * p.max_splits * (D + 2);
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  for (int s0 = 0; s0 < nsplit; s0 += 64)
+    if (s0 + lane < nsplit) M = fmaxf(M, part[(s0 + lane) * (D + 2) + D]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float Lsum = 0.0f;
   float acc[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) acc[i] = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* ps = part + s * (D + 2);
-    const float ms = ps[D];
-    const float c = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-    Lsum += ps[D + 1] * c;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    float c = 0.0f, lw = 0.0f;
+    if (s0 + lane < nsplit) {
+      const float* ps = part + (s0 + lane) * (D + 2);
+      const float ms = ps[D];
+      c = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+      lw = ps[D + 1] * c;
+    }
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] += ps[threadIdx.x + 64 * i] * c;
+    for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
+    Lsum += lw;
+    // Four chunks per step, their loads issued together; past the last chunk
+    // the index is clamped and the weight is zero (lanes >= n hold c = 0).
+    const int n = min(64, nsplit - s0);
+    for (int j = 0; j < n; j += 4) {
+      float v[4][D / 64], cj[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* ps = part + min(s0 + j + u, nsplit - 1) * (D + 2);
+        cj[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), min(j + u, 63)));
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) v[u][i] = ps[lane + 64 * i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) acc[i] += v[u][i] * cj[u];
+    }
   }
   const float inv = 1.0f / Lsum;
   const long obase = (long)b * p.q_batch + (long)h * p.q_head;
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) store_out(p.out, obase + threadIdx.x + 64 * i, acc[i] * inv, p.out_dtype);
+  for (int i = 0; i < D / 64; ++i) store_out(p.out, obase + lane + 64 * i, acc[i] * inv, p.out_dtype);
 }
 
 template <int D, bool INT4, bool QF16, bool BS>
