@@ -410,9 +410,9 @@ long prepare(const QuantArgs& a, QuantParams& p) {
 // the B operand, and each lane ends up holding 16 output channels of one row
 // (4 runs of 4 consecutive channels), which it scales and writes as 4-byte
 // code groups into LDS (over W, once every wavefront is done with it); the
-// block's rows then leave with coalesced 16-byte stores. One workgroup of 4
-// wavefronts owns one block of R rows (R a multiple of 32, at most 256;
-// wavefront v takes 32-row tiles v, v+4).
+// block's rows then leave with coalesced 16-byte stores. One workgroup owns
+// one block of R rows (R a multiple of 32, at most 256): 4 wavefronts for
+// R <= 128, else 8, each with one 32-row tile.
 
 struct RotParams {
   const uint16_t* x;
@@ -468,8 +468,11 @@ __device__ __forceinline__ uint32_t encode4(const float* t) {
   }
 }
 
-template <int D, bool BF16, int QT, int TPW>
-__global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams p) {
+// W = 1 or 2 groups of 4 wavefronts; with 8, at most 128 VGPRs (two
+// workgroups per CU).
+template <int D, bool BF16, int QT, int W>
+__global__ __launch_bounds__(64 * kRotWaves * W, 2 * W) void rot_quant_kernel(RotParams p) {
+  constexpr int NW = kRotWaves * W;  // wavefronts: one 32-row tile each
   constexpr int kStride = D + 8;       // 16-bit elements per staged row of W
   constexpr int kIB = D / 32;          // 32-channel output blocks
   constexpr int kKS = D / 16;          // k steps of 16
@@ -477,7 +480,7 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
   constexpr int kCS = D + 4;            // bytes per row of the staged codes
   constexpr int kWsElems = D * kStride > 256 * kCS / 2 ? D * kStride : 256 * kCS / 2;
   __shared__ __align__(16) uint16_t ws[kWsElems];
-  __shared__ uint32_t red[kRotWaves];
+  __shared__ uint32_t red[NW];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -492,18 +495,18 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
   const int rows = min(p.R, p.S - row0);
 
   // Stage W (row-major, rows padded) with 16-byte copies.
-  for (int c = threadIdx.x; c < D * D / 8; c += 64 * kRotWaves) {
+  for (int c = threadIdx.x; c < D * D / 8; c += 64 * NW) {
     const int i = c / (D / 8), k8 = (c % (D / 8)) * 8;
     *(uint4*)(ws + i * kStride + k8) = *(const uint4*)(p.w + (long)i * D + k8);
   }
   __syncthreads();
 
   const uint16_t* xb = p.x + b * p.x_batch + (long)n * p.x_head + (long)row0 * p.x_row;
-  f32x16 acc[TPW][kIB];
+  f32x16 acc[1][kIB];
   uint32_t amax_bits = 0;
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int tile = wave + kRotWaves * tt;
+  for (int tt = 0; tt < 1; ++tt) {
+    const int tile = wave + NW * tt;
     const int trow = tile * 32 + col;  // this lane's row within the block
     const bool valid = tile * 32 < rows && trow < rows;
     // B operands: 8 channels of this lane's row per k step (zero past the block).
@@ -535,7 +538,9 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
   for (int off = 32; off >= 1; off >>= 1) amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, off));
   if (lane == 0) red[wave] = amax_bits;
   __syncthreads();
-  amax_bits = max(max(red[0], red[1]), max(red[2], red[3]));
+  amax_bits = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) amax_bits = max(amax_bits, red[w]);
 
   const float amax = __uint_as_float(amax_bits);
   float sc = amax / kQmax;
@@ -555,8 +560,8 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
   // banks; then each row is written with 16-byte (or 4-byte) coalesced stores.
   uint8_t* cs = (uint8_t*)ws;
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int trow = (wave + kRotWaves * tt) * 32 + col;
+  for (int tt = 0; tt < 1; ++tt) {
+    const int trow = (wave + NW * tt) * 32 + col;
     if (trow >= rows) continue;
 #pragma unroll
     for (int ib = 0; ib < kIB; ++ib)
@@ -571,13 +576,13 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
   }
   __syncthreads();
   if (p.c16) {
-    for (int q = threadIdx.x; q < rows * (D / 16); q += 64 * kRotWaves) {
+    for (int q = threadIdx.x; q < rows * (D / 16); q += 64 * NW) {
       const int row = q / (D / 16), c = q % (D / 16);
       const uint32_t* src = (const uint32_t*)(cs + row * kCS + c * 16);
       *(uint4*)(cb + (long)row * p.c_row + c * 16) = make_uint4(src[0], src[1], src[2], src[3]);
     }
   } else {
-    for (int q = threadIdx.x; q < rows * (D / 4); q += 64 * kRotWaves) {
+    for (int q = threadIdx.x; q < rows * (D / 4); q += 64 * NW) {
       const int row = q / (D / 4), c = q % (D / 4);
       *(uint32_t*)(cb + (long)row * p.c_row + c * 4) = *(const uint32_t*)(cs + row * kCS + c * 4);
     }
@@ -585,16 +590,16 @@ __global__ __launch_bounds__(64 * kRotWaves, 2) void rot_quant_kernel(RotParams 
 }
 
 template <int D, bool BF16, int QT>
-hipError_t launch_rot_tpw(const RotParams& p, long grid, int tpw, hipStream_t st) {
-  if (tpw == 1) rot_quant_kernel<D, BF16, QT, 1><<<grid, 64 * kRotWaves, 0, st>>>(p);
-  else rot_quant_kernel<D, BF16, QT, 2><<<grid, 64 * kRotWaves, 0, st>>>(p);
+hipError_t launch_rot_w(const RotParams& p, long grid, int w, hipStream_t st) {
+  if (w == 1) rot_quant_kernel<D, BF16, QT, 1><<<grid, 64 * kRotWaves, 0, st>>>(p);
+  else rot_quant_kernel<D, BF16, QT, 2><<<grid, 128 * kRotWaves, 0, st>>>(p);
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
-hipError_t launch_rot_qt(const RotParams& p, int qtype, long grid, int tpw, hipStream_t st) {
-  if (qtype == QFA_FP8_E4M3) return launch_rot_tpw<D, BF16, QFA_FP8_E4M3>(p, grid, tpw, st);
-  return launch_rot_tpw<D, BF16, QFA_INT8>(p, grid, tpw, st);
+hipError_t launch_rot_qt(const RotParams& p, int qtype, long grid, int w, hipStream_t st) {
+  if (qtype == QFA_FP8_E4M3) return launch_rot_w<D, BF16, QFA_FP8_E4M3>(p, grid, w, st);
+  return launch_rot_w<D, BF16, QFA_INT8>(p, grid, w, st);
 }
 
 // ---- Appending one token to a quantized KV cache -------------------------
@@ -830,14 +835,14 @@ hipError_t launch_rotate_block_quant(const RotQuantArgs& a, hipStream_t stream) 
   const long grid = (long)a.B * a.N * p.nblk;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
-  const int tpw = a.block_rows > 32 * kRotWaves ? 2 : 1;
+  const int w = a.block_rows > 32 * kRotWaves ? 2 : 1;  // groups of 4 wavefronts
   const bool bf = a.x_dtype == QFA_BF16;
   if (a.D == 64) {
-    return bf ? launch_rot_qt<64, true>(p, a.qtype, grid, tpw, stream)
-              : launch_rot_qt<64, false>(p, a.qtype, grid, tpw, stream);
+    return bf ? launch_rot_qt<64, true>(p, a.qtype, grid, w, stream)
+              : launch_rot_qt<64, false>(p, a.qtype, grid, w, stream);
   }
-  return bf ? launch_rot_qt<128, true>(p, a.qtype, grid, tpw, stream)
-            : launch_rot_qt<128, false>(p, a.qtype, grid, tpw, stream);
+  return bf ? launch_rot_qt<128, true>(p, a.qtype, grid, w, stream)
+            : launch_rot_qt<128, false>(p, a.qtype, grid, w, stream);
 }
 
 }  // namespace qfa
