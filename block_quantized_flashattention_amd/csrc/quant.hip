@@ -621,11 +621,18 @@ struct AppendParams {
 };
 
 constexpr int kAppendThreads = 256;
+constexpr int kAppendUnroll = 8;   // old code bytes per thread requested together
 
 __device__ __forceinline__ float load_value(const void* x, long i, int dt) {
-  if (dt == QFA_F32) return ((const float*)x)[i];
-  const uint32_t h = ((const uint16_t*)x)[i];
-  return dt == QFA_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+  // One dword load (for 16-bit types, the aligned dword that holds the
+  // element) and selects: no branch around the load, so the compiler need
+  // not wait for it where the paths merge.
+  const long off = dt == QFA_F32 ? i * 4 : i * 2;
+  const int mis = dt == QFA_F32 ? 0 : (int)(((uintptr_t)x + (uintptr_t)off) & 2u);
+  const uint32_t w = *(const uint32_t*)((const char*)x + (off - mis));
+  const uint32_t h = (w >> (8 * mis)) & 0xFFFFu;
+  const float f16 = f16_bits_to_f32(h), b16 = bf16_bits_to_f32(h);
+  return dt == QFA_F32 ? __uint_as_float(w) : dt == QFA_F16 ? f16 : b16;
 }
 
 // Workgroup max of an unsigned value (every thread calls it; one barrier pair).
@@ -665,6 +672,10 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
   const int tid = threadIdx.x;
   const int nbytes = p.D / kPer;  // code bytes per row
 
+  // The block's stored scale, requested with the new row (used only when the
+  // block already has rows).
+  const long si = (long)bh * p.nblk + r;
+  const float s_stored = load_scale(p.scales, si, p.scale_f16);
   // The new row: this thread's code byte holds channels kPer*tid .. + kPer-1.
   float xv[kPer];
   uint32_t ax = 0;
@@ -676,22 +687,29 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
   }
   ax = wg_max(ax, red);
   const float amax_x = __uint_as_float(ax);
-  const long si = (long)bh * p.nblk + r;
-  const float s_old = nold == 0 ? 0.0f
-                      : p.scale_f16 ? f16_bits_to_f32(((const uint16_t*)p.scales)[si])
-                                    : ((const float*)p.scales)[si];
+  const float s_old = nold == 0 ? 0.0f : s_stored;
   bool fits = false;
   if (nold > 0) fits = s_old > 0.0f ? amax_x / s_old <= kQmax : amax_x == 0.0f;
   char* cb = p.codes + (long)b * p.c_batch + (long)h * p.c_head;
 
   float s = s_old;
   if (!fits) {
-    // amax of the old rows' values: fl32(max|code| * s_old), fl32 being monotonic
+    // amax of the old rows' values: fl32(max|code| * s_old), fl32 being monotonic.
+    // kAppendUnroll bytes per thread and step are requested together; past
+    // the last byte the index is clamped (a repeated byte leaves the max).
     uint32_t mc = 0;
-    for (int e = tid; e < nold * nbytes; e += kAppendThreads) {
-      const uint32_t byte = (uint8_t)cb[(long)(row0 + e / nbytes) * p.c_row + e % nbytes];
+    const int total = nold * nbytes;
+    for (int e0 = tid; e0 < total; e0 += kAppendUnroll * kAppendThreads) {
+      uint32_t by[kAppendUnroll];
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) mc = max(mc, (uint32_t)abs(code_value<QT>(byte >> (4 * j))));
+      for (int u = 0; u < kAppendUnroll; ++u) {
+        const int e = min(e0 + u * kAppendThreads, total - 1);
+        by[u] = (uint8_t)cb[(long)(row0 + e / nbytes) * p.c_row + e % nbytes];
+      }
+#pragma unroll
+      for (int u = 0; u < kAppendUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) mc = max(mc, (uint32_t)abs(code_value<QT>(by[u] >> (4 * j))));
     }
     mc = wg_max(mc, red);
     const float amax = fmaxf(amax_x, nold > 0 ? (float)mc * s_old : 0.0f);
@@ -706,17 +724,28 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
   const bool fast = s >= 0x1p-60f && s <= 0x1p100f;
   const float rcp = fast ? 1.0f / s : 0.0f;
   if (!fits) {
-    // Requantize the old rows in place (each byte read and written by one thread).
-    for (int e = tid; e < nold * nbytes; e += kAppendThreads) {
-      char* cp = cb + (long)(row0 + e / nbytes) * p.c_row + e % nbytes;
-      const uint32_t byte = (uint8_t)*cp;
-      uint32_t out = 0;
+    // Requantize the old rows in place (each byte read and written by one
+    // thread; kAppendUnroll bytes per thread and step requested together).
+    const int total = nold * nbytes;
+    for (int e0 = tid; e0 < total; e0 += kAppendUnroll * kAppendThreads) {
+      uint32_t by[kAppendUnroll];
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const float v = (float)code_value<QT>(byte >> (4 * j)) * s_old;
-        out |= (zero ? 0u : code_bits<QT>(quotient<false>(v, s, rcp, fast))) << (4 * j);
+      for (int u = 0; u < kAppendUnroll; ++u) {
+        const int e = min(e0 + u * kAppendThreads, total - 1);
+        by[u] = (uint8_t)cb[(long)(row0 + e / nbytes) * p.c_row + e % nbytes];
       }
-      *cp = (char)out;
+#pragma unroll
+      for (int u = 0; u < kAppendUnroll; ++u) {
+        const int e = e0 + u * kAppendThreads;
+        if (e >= total) break;
+        uint32_t out = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const float v = (float)code_value<QT>(by[u] >> (4 * j)) * s_old;
+          out |= (zero ? 0u : code_bits<QT>(quotient<false>(v, s, rcp, fast))) << (4 * j);
+        }
+        cb[(long)(row0 + e / nbytes) * p.c_row + e % nbytes] = (char)out;
+      }
     }
   }
   if (tid < nbytes) {
