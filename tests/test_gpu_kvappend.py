@@ -65,3 +65,16 @@ def test_kv_append_sequence_of_steps():
     for step in range(6):
         x = torch.randn(B, H, D, generator=gen).to(torch.float16) * (1.0 + 3 * (step % 3 == 2))
         _append_and_check(codes, scales, x, [L + step for L in lens], R, "int8", "bnsd")
+
+
+@pytest.mark.parametrize("qtype,layout", [("int4", "bnsd"), ("int8", "bsnd"), ("int4", "bsnd")])
+def test_kv_append_requantizes_nearly_full_blocks(qtype, layout):
+    """Rows 251 and 254 of 256-row blocks with a large new row: the whole
+    block (hundreds of old rows) is requantized, past one pass of the
+    threads' unrolled reads."""
+    B, H, S, D, R = 2, 3, 600, 128, 256
+    say(f"kv append requantizing nearly full blocks {qtype} {layout}")
+    codes, scales = _cache(B, H, S, D, R, qtype, "f16", layout, seed=23)
+    gen = torch.Generator().manual_seed(9)
+    x = torch.randn(B, H, D, generator=gen).to(torch.float16) * 30.0
+    _append_and_check(codes, scales, x, [251, R + 254], R, qtype, layout)
