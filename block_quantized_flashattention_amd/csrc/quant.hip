@@ -226,17 +226,23 @@ __device__ __forceinline__ void quant_blocks(const QuantParams& p, long wg, uint
   uint32_t amax_bits = 0;
   typename I::Raw raw[TWO_PASS ? 1 : CH];
   if constexpr (!TWO_PASS) {
+    // All CH loads are issued before any is used: a chunk past the block
+    // reads the block's first chunk instead (always in range) and is left
+    // out of the max. Loads inside a branch that also used them made the
+    // compiler wait for each one before issuing the next.
     int row = row0_t, col = col0_t;
+    bool ok[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      if (k < p.chunks && row < rows) {
-        raw[k] = I::load(xb + ((long)row * p.x_row + col) * I::kBytes);
-        amax_bits = max(amax_bits, I::absmax(raw[k]));
-      }
+      ok[k] = k < p.chunks && row < rows;
+      const long off = ok[k] ? (long)row * p.x_row + col : 0L;
+      raw[k] = I::load(xb + off * I::kBytes);
       row += p.step_rows;
       col += p.step_cols;
       if (col >= p.D) { col -= p.D; ++row; }
     }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) amax_bits = max(amax_bits, ok[k] ? I::absmax(raw[k]) : 0u);
   } else {
     int row = row0_t, col = col0_t;
     for (int k = 0; k < p.chunks && row < rows; ++k) {
