@@ -474,10 +474,10 @@ __device__ __forceinline__ uint32_t encode4(const float* t) {
   }
 }
 
-// W = 1 or 2 groups of 4 wavefronts; with 8, at most 128 VGPRs (two
-// workgroups per CU).
+// W = 1 or 2 groups of 4 wavefronts, at most 128 VGPRs (four waves per SIMD:
+// four 4-wave or two 8-wave workgroups per CU).
 template <int D, bool BF16, int QT, int W>
-__global__ __launch_bounds__(64 * kRotWaves * W, 2 * W) void rot_quant_kernel(RotParams p) {
+__global__ __launch_bounds__(64 * kRotWaves * W, 4) void rot_quant_kernel(RotParams p) {
   constexpr int NW = kRotWaves * W;  // wavefronts: one 32-row tile each
   constexpr int kStride = D + 8;       // 16-bit elements per staged row of W
   constexpr int kIB = D / 32;          // 32-channel output blocks
@@ -500,8 +500,12 @@ __global__ __launch_bounds__(64 * kRotWaves * W, 2 * W) void rot_quant_kernel(Ro
   const int row0 = r * p.R;
   const int rows = min(p.R, p.S - row0);
 
-  // Stage W (row-major, rows padded) with 16-byte copies.
-  for (int c = threadIdx.x; c < D * D / 8; c += 64 * NW) {
+  // Stage W (row-major, rows padded) with 16-byte copies, all requested
+  // before the first is written.
+  static_assert(D * D / 8 % (64 * NW) == 0, "W chunks per thread");
+#pragma unroll
+  for (int n = 0; n < D * D / 8 / (64 * NW); ++n) {
+    const int c = threadIdx.x + n * 64 * NW;
     const int i = c / (D / 8), k8 = (c % (D / 8)) * 8;
     *(uint4*)(ws + i * kStride + k8) = *(const uint4*)(p.w + (long)i * D + k8);
   }
@@ -516,12 +520,14 @@ __global__ __launch_bounds__(64 * kRotWaves * W, 2 * W) void rot_quant_kernel(Ro
     const int trow = tile * 32 + col;  // this lane's row within the block
     const bool valid = tile * 32 < rows && trow < rows;
     // B operands: 8 channels of this lane's row per k step (zero past the block).
+    // Rows past the block load row 0 (always in range) and are zeroed after
+    // the load, so no branch holds the loads back.
     i32x4 xo[kKS];
+    const long xrow = valid ? (long)trow * p.x_row : 0L;
 #pragma unroll
-    for (int s = 0; s < kKS; ++s) {
-      xo[s] = (i32x4){};
-      if (valid) xo[s] = *(const i32x4*)(xb + (long)trow * p.x_row + 16 * s + 8 * half);
-    }
+    for (int s = 0; s < kKS; ++s) xo[s] = *(const i32x4*)(xb + xrow + 16 * s + 8 * half);
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) xo[s] = valid ? xo[s] : (i32x4){};
 #pragma unroll
     for (int ib = 0; ib < kIB; ++ib) {
       acc[tt][ib] = (f32x16){};
