@@ -75,6 +75,24 @@ def test_small_decode(name, B, Hq, Hkv, D, S_max, lens, qt, R, sdt, layout):
     _run(w, q, k, v, lens_t, layout=layout)
 
 
+
+@pytest.mark.parametrize("qdt,odt", [("f32", "f32"), ("bf16", "bf16")])
+@pytest.mark.parametrize("qt,R", [("int8", 256), ("int4", 256), ("int4", 1)])
+def test_decode_query_dtypes(qdt, odt, qt, R):
+    """fp32 and bf16 queries (the codes go to fp32 on that path) with fp32 and
+    bf16 outputs, over several chunks and a ragged length."""
+    w = wl.DecodeWorkload(name=f"q{qdt}_{qt}_r{R}", B=2, Hq=4, Hkv=2, D=128, S_max=2200,
+                          len_lo=2200, len_hi=2200, seed=91, kv_qtype=qt, kv_block=R,
+                          kv_scale_dtype="f16", q_dtype=qdt, out_dtype=odt,
+                          softmax_scale=float(np.float32(1 / np.sqrt(128))))
+    q, k, v, _ = wl.make_decode_inputs(w)
+    lens = [2200, 777]
+    for b, L in enumerate(lens):
+        k[b, :, L:] = 0
+        v[b, :, L:] = 0
+    _run(w, q, k, v, torch.tensor(lens, dtype=torch.int32))
+
+
 @pytest.mark.parametrize("w", [wl.DECODE, wl.DECODE_INT4], ids=lambda w: w.name)
 def test_full_size_decode_sampled(w):
     """The full decode workload (B=32, 32 heads, S_max=8192, L in [4096, 8192]),
