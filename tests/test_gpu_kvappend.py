@@ -78,3 +78,18 @@ def test_kv_append_requantizes_nearly_full_blocks(qtype, layout):
     gen = torch.Generator().manual_seed(9)
     x = torch.randn(B, H, D, generator=gen).to(torch.float16) * 30.0
     _append_and_check(codes, scales, x, [251, R + 254], R, qtype, layout)
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("qtype", ["int8", "int4"])
+def test_kv_append_row_dtypes(xdt, qtype):
+    """fp32 and bf16 new rows (each element read from the dword that holds
+    it), one that fits its block and one that forces a requantization."""
+    B, H, S, D, R = 3, 2, 600, 128, 256
+    say(f"kv append row dtype {xdt} {qtype}")
+    codes, scales = _cache(B, H, S, D, R, qtype, "f16", "bnsd", seed=31)
+    gen = torch.Generator().manual_seed(10)
+    x = torch.randn(B, H, D, generator=gen)
+    x[0] *= 0.25
+    x[1] *= 40.0
+    _append_and_check(codes, scales, x.to(xdt), [200, R + 100, 599], R, qtype, "bnsd")
