@@ -181,6 +181,8 @@ __device__ __forceinline__ void store_codes(char* p, const float* t, bool zero) 
   }
 }
 
+constexpr int kPassGroup = 4;  // chunk loads issued together in the two-pass path
+
 // Team-wide max of an unsigned value. Teams wider than a wavefront go through
 // LDS; every thread of the workgroup must call this (it may hold a barrier).
 __device__ __forceinline__ uint32_t team_max(uint32_t m, int team_log2, uint32_t* lds) {
@@ -244,12 +246,23 @@ __device__ __forceinline__ void quant_blocks(const QuantParams& p, long wg, uint
 #pragma unroll
     for (int k = 0; k < CH; ++k) amax_bits = max(amax_bits, ok[k] ? I::absmax(raw[k]) : 0u);
   } else {
+    // Blocks too large for registers: two passes over x, each issuing
+    // kPassGroup chunk loads together (past the block: the first chunk,
+    // left out).
     int row = row0_t, col = col0_t;
-    for (int k = 0; k < p.chunks && row < rows; ++k) {
-      amax_bits = max(amax_bits, I::absmax(I::load(xb + ((long)row * p.x_row + col) * I::kBytes)));
-      row += p.step_rows;
-      col += p.step_cols;
-      if (col >= p.D) { col -= p.D; ++row; }
+    for (int k0 = 0; k0 < p.chunks && row < rows; k0 += kPassGroup) {
+      typename I::Raw rg[kPassGroup];
+      bool ok[kPassGroup];
+#pragma unroll
+      for (int u = 0; u < kPassGroup; ++u) {
+        ok[u] = k0 + u < p.chunks && row < rows;
+        rg[u] = I::load(xb + (ok[u] ? (long)row * p.x_row + col : 0L) * I::kBytes);
+        row += p.step_rows;
+        col += p.step_cols;
+        if (col >= p.D) { col -= p.D; ++row; }
+      }
+#pragma unroll
+      for (int u = 0; u < kPassGroup; ++u) amax_bits = max(amax_bits, ok[u] ? I::absmax(rg[u]) : 0u);
     }
   }
   amax_bits = team_max(amax_bits, p.team_log2, lds);
@@ -284,15 +297,29 @@ __device__ __forceinline__ void quant_blocks(const QuantParams& p, long wg, uint
     }
   } else {
     int row = row0_t, col = col0_t;
-    for (int k = 0; k < p.chunks && row < rows; ++k) {
-      float f[8], t[8];
-      I::to_f32(I::load(xb + ((long)row * p.x_row + col) * I::kBytes), f);
+    for (int k0 = 0; k0 < p.chunks && row < rows; k0 += kPassGroup) {
+      typename I::Raw rg[kPassGroup];
+      int rr[kPassGroup], cc[kPassGroup];
+      bool ok[kPassGroup];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = quotient<QT == QFA_FP8_E4M3>(f[i], s, rcp, fast);
-      store_codes<QT>(cb + (long)row * p.c_row + col / code_div, t, zero);
-      row += p.step_rows;
-      col += p.step_cols;
-      if (col >= p.D) { col -= p.D; ++row; }
+      for (int u = 0; u < kPassGroup; ++u) {
+        ok[u] = k0 + u < p.chunks && row < rows;
+        rr[u] = row;
+        cc[u] = col;
+        rg[u] = I::load(xb + (ok[u] ? (long)row * p.x_row + col : 0L) * I::kBytes);
+        row += p.step_rows;
+        col += p.step_cols;
+        if (col >= p.D) { col -= p.D; ++row; }
+      }
+#pragma unroll
+      for (int u = 0; u < kPassGroup; ++u) {
+        if (!ok[u]) continue;
+        float f[8], t[8];
+        I::to_f32(rg[u], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = quotient<QT == QFA_FP8_E4M3>(f[i], s, rcp, fast);
+        store_codes<QT>(cb + (long)rr[u] * p.c_row + cc[u] / code_div, t, zero);
+      }
     }
   }
 }
