@@ -161,10 +161,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t* base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
 }
 
-template <int D, bool INT4, bool QF16, bool BLOCK_SCALE>
 // Packed INT4 with an fp16 query and block scales asks for six wavefronts per
 // SIMD, i.e. three workgroups per CU (at most 80 VGPRs): its rows are half as
 // long, so more of them must be in flight to cover the HBM latency.
+template <int D, bool INT4, bool QF16, bool BLOCK_SCALE>
 __global__ __launch_bounds__(64 * kDecWaves, INT4 && QF16 && BLOCK_SCALE ? 6 : 2)
 void decode_split_kernel(DecParams p) {
   constexpr int kRowBytes = INT4 ? D / 2 : D;
