@@ -97,6 +97,10 @@ def _check(x, w, R, qtype, dt, sdt, layout, heads=None):
     (2, 1, 200, 64, "f16", 64, "int8", "f16", "bsnd"),
     (1, 2, 600, 128, "bf16", 256, "fp8", "f32", "bsnd"),
     (1, 3, 70, 128, "f16", 32, "int8", "f32", "bnsd"),
+    # 8-wavefront workgroups (R > 128) with empty tiles and ragged tails
+    (1, 2, 500, 128, "f16", 160, "int8", "f16", "bnsd"),
+    (2, 1, 530, 64, "bf16", 224, "fp8", "f32", "bsnd"),
+    (1, 1, 513, 128, "f16", 256, "fp8", "f16", "bnsd"),
 ], ids=lambda c: "_".join(map(str, c)))
 def test_rotate_block_quant_small(case):
     B, N, S, D, dt, R, qtype, sdt, layout = case
@@ -117,3 +121,21 @@ def test_rotate_block_quant_empty():
     x = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device="cuda")
     c, s = qfa.rotate_block_quant(x, w, 128, "fp8")
     assert c.shape == (1, 2, 0, 128) and s.shape == (1, 2, 0)
+
+
+@pytest.mark.parametrize("R", [128, 256])
+def test_rotate_block_quant_unaligned_codes(R):
+    """Codes 8 bytes past a 16-byte boundary take the 4-byte store path; its
+    bytes must equal those of the 16-byte path (checked against the oracle
+    by the other tests)."""
+    x, w = _inputs(1, 2, 400, 128, "bf16", "bnsd", seed=5 + R)
+    x, w = x.cuda(), w.cuda()
+    ref_c, ref_s = qfa.rotate_block_quant(x, w, R, "fp8")
+    buf = torch.zeros(ref_c.numel() + 16, dtype=torch.uint8, device="cuda")
+    codes = buf[8:8 + ref_c.numel()].view(ref_c.dtype).view(ref_c.shape)
+    assert codes.data_ptr() % 16 == 8
+    c, s = qfa.rotate_block_quant(x, w, R, "fp8", codes=codes)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.uint8), ref_c.view(torch.uint8))
+    assert torch.equal(s, ref_s)
+    assert int(buf[:8].sum()) == 0 and int(buf[8 + ref_c.numel():].sum()) == 0
