@@ -33,9 +33,10 @@
 //     V scale and rescaled when it changes). With per-token scales (INT4 K/V)
 //     each score and probability takes one more multiply.
 //   * The running row max is only raised when a tile's max exceeds it by more
-//     than 12 (log2 units), so the O rescale is skipped on most tiles; the
-//     probabilities stay below 2^12 (exact softmax; fp16 holds them with its
-//     full 11-bit precision, far below its 65504 limit).
+//     than 12 (log2 units; 8 with per-key scales, whose fp16 weights carry the
+//     V scale), so the O rescale is skipped on most tiles; the probabilities
+//     stay below 2^12 (exact softmax; fp16 holds them with its full 11-bit
+//     precision, far below its 65504 limit).
 //   * Row sums add the fp16-rounded probabilities with v_dot2_f32_f16, i.e.
 //     exactly the weights the P.V product uses.
 //   * One step per key tile: the max of tile t and the rare rescale, then
@@ -68,6 +69,9 @@ constexpr int kBM = 32 * kNW;     // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 12.0f;
+// With per-key V scales the fp16 weight is p * sv; the smaller slack keeps it
+// below 2^8 * sv, far from the fp16 limit for any plausible V scale.
+constexpr float kRescaleSlackTok = 8.0f;
 
 struct FwdParams {
   const uint8_t* q;
@@ -559,9 +563,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
           }
         }
       const float mt = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
-      if (__any(mt > m_run + kRescaleSlack)) {
+      if (__any(mt > m_run + kRescaleSlackTok)) {
         const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = mrow > m_run + kRescaleSlack ? fmaxf(m_run, mrow) : m_run;
+        const float m_new = mrow > m_run + kRescaleSlackTok ? fmaxf(m_run, mrow) : m_run;
         const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
