@@ -100,6 +100,25 @@ def code_dtype(qtype: str) -> torch.dtype:
     return torch.int8 if qtype == "int8" else torch.uint8
 
 
+def _expect(t: torch.Tensor, shape, dtypes, name: str):
+    """Raise ValueError unless ``t`` has exactly ``shape`` and one of ``dtypes``.
+    The library trusts the sizes it is given, so a mismatched tensor would be
+    read or written out of bounds on the GPU."""
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+
+
+def _code_shape(shape_bnsd_like, qtype: str):
+    """Shape of the codes of a tensor of this shape: the last dim halves for INT4."""
+    d = shape_bnsd_like[-1]
+    return tuple(shape_bnsd_like[:-1]) + (d // 2 if qtype == "int4" else d,)
+
+
+_SCALE_DTYPES = (torch.float32, torch.float16)
+
+
 class QuantJob(ctypes.Structure):
     """Mirror of qfa_quant_job (include/qfa.h)."""
     _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int), ("B", ctypes.c_int),
@@ -115,13 +134,17 @@ def _quant_outputs(x, block_rows, qtype, scale_dtype, layout, codes, scales):
         B, N, S, D = x.shape
     else:
         B, S, N, D = x.shape
-    cshape = list(x.shape[:-1]) + [D // 2 if qtype == "int4" else D]
+    if qtype not in QTYPES or x.dtype not in FLOATS or block_rows < 1:
+        raise ValueError("unknown qtype or input dtype, or block_rows < 1")
+    cshape = _code_shape(x.shape, qtype)
     if codes is None:
         codes = torch.empty(cshape, dtype=code_dtype(qtype), device=x.device)
     if scales is None:
         scales = torch.empty(B, N, -(-S // block_rows), dtype=scale_dtype, device=x.device)
     _dev(codes, "codes")
     _dev(scales, "scales")
+    _expect(codes, cshape, (code_dtype(qtype),), "codes")
+    _expect(scales, (B, N, -(-S // block_rows)), _SCALE_DTYPES, "scales")
     job = QuantJob(_ptr(x), FLOATS[x.dtype], B, N, S, D, LAYOUTS[layout], block_rows,
                    QTYPES[qtype], _ptr(codes), _ptr(scales), FLOATS[scales.dtype])
     return job, codes, scales
@@ -182,13 +205,17 @@ def block_quant(x: torch.Tensor, block_rows: int, qtype: str, scale_dtype=torch.
         B, N, S, D = x.shape
     else:
         B, S, N, D = x.shape
-    cshape = list(x.shape[:-1]) + [D // 2 if qtype == "int4" else D]
+    if qtype not in QTYPES or x.dtype not in FLOATS or block_rows < 1:
+        raise ValueError("unknown qtype or input dtype, or block_rows < 1")
+    cshape = _code_shape(x.shape, qtype)
     if codes is None:
         codes = torch.empty(cshape, dtype=code_dtype(qtype), device=x.device)
     if scales is None:
         scales = torch.empty(B, N, -(-S // block_rows), dtype=scale_dtype, device=x.device)
     _dev(codes, "codes")
     _dev(scales, "scales")
+    _expect(codes, cshape, (code_dtype(qtype),), "codes")
+    _expect(scales, (B, N, -(-S // block_rows)), _SCALE_DTYPES, "scales")
     _check("qfa_block_quant", lib().qfa_block_quant(
         _ptr(x), FLOATS[x.dtype], B, N, S, D, LAYOUTS[layout], block_rows, QTYPES[qtype],
         _ptr(codes), _ptr(scales), FLOATS[scales.dtype], _stream(stream)))
@@ -207,6 +234,12 @@ def kv_append(x: torch.Tensor, positions: torch.Tensor, codes: torch.Tensor,
         raise ValueError("positions must be int32")
     B, H, D = x.shape
     S_max = codes.shape[2] if layout == "bnsd" else codes.shape[1]
+    cs = (B, H, S_max, D) if layout == "bnsd" else (B, S_max, H, D)
+    _expect(codes, _code_shape(cs, qtype), (code_dtype(qtype),), "codes")
+    _expect(scales, (B, H, -(-S_max // kv_block)), _SCALE_DTYPES, "scales")
+    _expect(positions, (B,), (torch.int32,), "positions")
+    if x.dtype not in FLOATS:
+        raise ValueError(f"x has dtype {x.dtype}")
     args = (_ptr(x), FLOATS[x.dtype], _ptr(positions), _ptr(codes), _ptr(scales), B, H, S_max, D,
             LAYOUTS[layout], kv_block, QTYPES[qtype], FLOATS[scales.dtype], _stream(stream))
     f = lib().qfa_kv_append
@@ -248,6 +281,8 @@ def prepare_rotate_block_quant(x: torch.Tensor, w: torch.Tensor, block_rows: int
     _dev(scales, "scales")
     if w.dtype != x.dtype or tuple(w.shape) != (D, D):
         raise ValueError("w must be [D, D] with the dtype of x")
+    _expect(codes, x.shape, (code_dtype(qtype),), "codes")
+    _expect(scales, (B, N, -(-S // block_rows)), _SCALE_DTYPES, "scales")
     args = (_ptr(x), FLOATS[x.dtype], _ptr(w), B, N, S, D, LAYOUTS[layout], block_rows,
             QTYPES[qtype], _ptr(codes), _ptr(scales), FLOATS[scales.dtype], _stream(stream))
     f = lib().qfa_rotate_block_quant
@@ -268,11 +303,25 @@ def _fwd_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, q_qtype, 
     else:
         B, Sq, Hq, D = q_codes.shape
         Sk, Hkv = k_codes.shape[1], k_codes.shape[2]
+    for qt in (q_qtype, k_qtype, v_qtype):
+        if qt not in QTYPES:
+            raise ValueError(f"unknown code type {qt!r}")
+    if q_qtype == "int4":
+        raise ValueError("Q codes cannot be INT4")
+    if q_block < 1 or kv_block < 1:
+        raise ValueError("block sizes must be >= 1")
     if out is None:
         out = torch.empty(q_codes.shape, dtype=out_dtype, device=q_codes.device)
     _dev(out, "out")
-    if q_scales.dtype != torch.float32 and q_scales.dtype != torch.float16:
-        raise ValueError("scales must be float32 or float16")
+    qshape = (B, Hq, Sq, D) if layout == "bnsd" else (B, Sq, Hq, D)
+    kvshape = (B, Hkv, Sk, D) if layout == "bnsd" else (B, Sk, Hkv, D)
+    _expect(q_codes, qshape, (code_dtype(q_qtype),), "q_codes")
+    _expect(k_codes, _code_shape(kvshape, k_qtype), (code_dtype(k_qtype),), "k_codes")
+    _expect(v_codes, _code_shape(kvshape, v_qtype), (code_dtype(v_qtype),), "v_codes")
+    _expect(q_scales, (B, Hq, -(-Sq // q_block)), _SCALE_DTYPES, "q_scales")
+    _expect(k_scales, (B, Hkv, -(-Sk // kv_block)), _SCALE_DTYPES, "k_scales")
+    _expect(v_scales, (B, Hkv, -(-Sk // kv_block)), (k_scales.dtype,), "v_scales")
+    _expect(out, qshape, tuple(FLOATS), "out")
     args = (_ptr(q_codes), _ptr(q_scales), QTYPES[q_qtype], q_block, FLOATS[q_scales.dtype],
             _ptr(k_codes), _ptr(k_scales), QTYPES[k_qtype], _ptr(v_codes), _ptr(v_scales),
             QTYPES[v_qtype], kv_block, FLOATS[k_scales.dtype], B, Hq, Hkv, Sq, Sk, D,
@@ -322,21 +371,34 @@ def _decode_args(q, k_cache, v_cache, k_scales, v_scales, seq_lens, kv_qtype, kv
         _dev(t, n)
     if seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32")
-    B, Hq, D = q.shape[0], q.numel() // (q.shape[0] * q.shape[-1]), q.shape[-1]
+    B, D = q.shape[0], q.shape[-1]
+    Hq = q.numel() // (B * D) if B * D else 0
     if layout == "bnsd":
         Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
     else:
         S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if kv_qtype not in QTYPES or kv_block < 1:
+        raise ValueError("unknown kv_qtype or kv_block < 1")
+    if q.dim() != 4 or q.numel() != B * Hq * D or q.dtype not in FLOATS:
+        raise ValueError(f"q must be [B, Hq, 1, D] (or [B, 1, Hq, D]) float, got {tuple(q.shape)}")
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     _dev(out, "out")
+    cshape = (B, Hkv, S_max, D) if layout == "bnsd" else (B, S_max, Hkv, D)
+    _expect(k_cache, _code_shape(cshape, kv_qtype), (code_dtype(kv_qtype),), "k_cache")
+    _expect(v_cache, _code_shape(cshape, kv_qtype), (code_dtype(kv_qtype),), "v_cache")
+    _expect(k_scales, (B, Hkv, -(-S_max // kv_block)), _SCALE_DTYPES, "k_scales")
+    _expect(v_scales, (B, Hkv, -(-S_max // kv_block)), (k_scales.dtype,), "v_scales")
+    _expect(seq_lens, (B,), (torch.int32,), "seq_lens")
+    _expect(out, q.shape, tuple(FLOATS), "out")
+    head = (_ptr(q), FLOATS[q.dtype], B, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+            _ptr(v_scales), QTYPES[kv_qtype], kv_block, FLOATS[k_scales.dtype], S_max,
+            LAYOUTS[layout], _ptr(seq_lens), float(softmax_scale), _ptr(out), FLOATS[out.dtype])
     need = decode_workspace_bytes(B, Hq, S_max, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    args = (_ptr(q), FLOATS[q.dtype], B, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
-            _ptr(v_scales), QTYPES[kv_qtype], kv_block, FLOATS[k_scales.dtype], S_max,
-            LAYOUTS[layout], _ptr(seq_lens), float(softmax_scale), _ptr(out), FLOATS[out.dtype],
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _dev(workspace, "workspace")
+    args = head + (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     return args, out, workspace
 
 
