@@ -65,6 +65,11 @@ def lib() -> ctypes.CDLL:
     L.qfa_decode.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, i, i, vp, f, vp, i,
                              vp, sz, vp]
     L.qfa_decode.restype = i
+    L.qfa_decode_noalloc_max_bytes.argtypes = []
+    L.qfa_decode_noalloc_max_bytes.restype = sz
+    L.qfa_decode_noalloc.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, i, i, vp, f, vp, i,
+                                     vp]
+    L.qfa_decode_noalloc.restype = i
     _lib = L
     return L
 
@@ -394,6 +399,8 @@ def _decode_args(q, k_cache, v_cache, k_scales, v_scales, seq_lens, kv_qtype, kv
     head = (_ptr(q), FLOATS[q.dtype], B, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
             _ptr(v_scales), QTYPES[kv_qtype], kv_block, FLOATS[k_scales.dtype], S_max,
             LAYOUTS[layout], _ptr(seq_lens), float(softmax_scale), _ptr(out), FLOATS[out.dtype])
+    if workspace is False:  # the no-alloc entry point takes no workspace
+        return head + (_stream(stream),), out, None
     need = decode_workspace_bytes(B, Hq, S_max, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -409,6 +416,22 @@ def decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtype: str, 
     args, out, _ = _decode_args(q, k_cache, v_cache, k_scales, v_scales, seq_lens, kv_qtype,
                                 kv_block, softmax_scale, layout, out_dtype, out, workspace, stream)
     _check("qfa_decode", lib().qfa_decode(*args))
+    return out
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(lib().qfa_decode_noalloc_max_bytes())
+
+
+def decode_noalloc(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtype: str,
+                   kv_block: int, softmax_scale: float, layout: str = "bnsd", out=None,
+                   out_dtype=None, stream=None):
+    """``decode`` without a workspace: the split-K partials go to the library's
+    static per-device scratch (qfa_decode_noalloc). ``out`` may be given so
+    that the call allocates nothing at all; calls that overlap on one GPU race."""
+    args, out, _ = _decode_args(q, k_cache, v_cache, k_scales, v_scales, seq_lens, kv_qtype,
+                                kv_block, softmax_scale, layout, out_dtype, out, False, stream)
+    _check("qfa_decode_noalloc", lib().qfa_decode_noalloc(*args))
     return out
 
 
@@ -433,5 +456,6 @@ def prepare_decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtyp
 
 __all__ = ["block_quant", "block_quant_multi", "prepare_block_quant_multi", "rotate_block_quant",
            "prepare_rotate_block_quant", "kv_append", "fwd", "prepare_fwd",
-           "decode", "prepare_decode", "decode_workspace_bytes", "lib", "header_functions",
+           "decode", "prepare_decode", "decode_workspace_bytes", "decode_noalloc",
+           "decode_noalloc_max_bytes", "lib", "header_functions",
            "QFAError", "QTYPES", "LAYOUTS", "FLOATS", "QMAX", "code_dtype"]

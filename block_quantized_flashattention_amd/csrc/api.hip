@@ -48,6 +48,7 @@ const char* qfa_status_string(int status) {
     case QFA_ERR_UNSUPPORTED: return "valid combination not implemented by this build";
     case QFA_ERR_WORKSPACE: return "decode workspace missing or too small";
     case QFA_ERR_HIP: return "HIP runtime error at launch";
+    case QFA_ERR_SCRATCH: return "request exceeds the library's static decode scratch";
     default: return "unknown status";
   }
 }
@@ -162,11 +163,14 @@ size_t qfa_decode_workspace_bytes(int B, int Hq, int S_max, int D) {
   return qfa::decode_workspace_bytes(B, Hq, S_max, D);
 }
 
-int qfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D, const void* k_cache,
-               const void* v_cache, const void* k_scales, const void* v_scales, int kv_qtype,
-               int kv_block, int kv_scale_dtype, int S_max, int layout, const int32_t* seq_lens,
-               float softmax_scale, void* out, int out_dtype, void* workspace,
-               size_t workspace_bytes, void* stream) {
+// Validation shared by the two decode entry points; on QFA_OK, *need holds the
+// bytes of split-K partials the call will write.
+static int check_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
+                        const void* k_cache, const void* v_cache, const void* k_scales,
+                        const void* v_scales, int kv_qtype, int kv_block, int kv_scale_dtype,
+                        int S_max, int layout, const int32_t* seq_lens, float softmax_scale,
+                        const void* out, int out_dtype, size_t* need) {
+  *need = 0;
   if (!valid_float(q_dtype) || !valid_float(out_dtype) || !valid_qtype(kv_qtype) ||
       !valid_layout(layout) || (kv_scale_dtype != QFA_F32 && kv_scale_dtype != QFA_F16))
     return QFA_ERR_ENUM;
@@ -183,15 +187,51 @@ int qfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D, const 
     return QFA_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !k_scales || !v_scales || !seq_lens || !out)
     return QFA_ERR_NULL;
-  const size_t need = qfa::decode_workspace_bytes(B, Hq, S_max, D);
-  if (S_max > qfa::kDecodeChunk && (!workspace || workspace_bytes < need))
-    return QFA_ERR_WORKSPACE;
-  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 16) ||
-      !aligned(q, 4) || !aligned(out, 4) || !aligned(seq_lens, 4))
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(q, 4) || !aligned(out, 4) ||
+      !aligned(seq_lens, 4))
     return QFA_ERR_UNSUPPORTED;
+  // Partials are written only when a sequence spans more than one chunk.
+  *need = S_max > qfa::kDecodeChunk ? qfa::decode_workspace_bytes(B, Hq, S_max, D) : 0;
+  return QFA_OK;
+}
+
+int qfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D, const void* k_cache,
+               const void* v_cache, const void* k_scales, const void* v_scales, int kv_qtype,
+               int kv_block, int kv_scale_dtype, int S_max, int layout, const int32_t* seq_lens,
+               float softmax_scale, void* out, int out_dtype, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  const int st = check_decode(q, q_dtype, B, Hq, Hkv, D, k_cache, v_cache, k_scales, v_scales,
+                              kv_qtype, kv_block, kv_scale_dtype, S_max, layout, seq_lens,
+                              softmax_scale, out, out_dtype, &need);
+  if (st != QFA_OK || B == 0) return st;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QFA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return QFA_ERR_UNSUPPORTED;
   qfa::DecodeArgs a{q, q_dtype, B, Hq, Hkv, D, k_cache, v_cache, k_scales, v_scales, kv_qtype,
                     kv_block, kv_scale_dtype, S_max, layout, seq_lens, softmax_scale, out,
                     out_dtype, workspace};
+  return from_hip(qfa::launch_decode(a, (hipStream_t)stream));
+}
+
+size_t qfa_decode_noalloc_max_bytes(void) { return qfa::kDecodeScratchBytes; }
+
+int qfa_decode_noalloc(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
+                       const void* k_cache, const void* v_cache, const void* k_scales,
+                       const void* v_scales, int kv_qtype, int kv_block, int kv_scale_dtype,
+                       int S_max, int layout, const int32_t* seq_lens, float softmax_scale,
+                       void* out, int out_dtype, void* stream) {
+  size_t need = 0;
+  const int st = check_decode(q, q_dtype, B, Hq, Hkv, D, k_cache, v_cache, k_scales, v_scales,
+                              kv_qtype, kv_block, kv_scale_dtype, S_max, layout, seq_lens,
+                              softmax_scale, out, out_dtype, &need);
+  if (st != QFA_OK || B == 0) return st;
+  if (need > qfa::kDecodeScratchBytes) return QFA_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = qfa::decode_scratch((hipStream_t)stream, &ws);
+  if (e != hipSuccess) return QFA_ERR_HIP;
+  qfa::DecodeArgs a{q, q_dtype, B, Hq, Hkv, D, k_cache, v_cache, k_scales, v_scales, kv_qtype,
+                    kv_block, kv_scale_dtype, S_max, layout, seq_lens, softmax_scale, out,
+                    out_dtype, ws};
   return from_hip(qfa::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -39,11 +39,19 @@
 //     codes go to fp32 (offset 128 or 8, removed once per channel).
 //   * When one scale block covers a wavefront's 128 tokens (block size a
 //     multiple of 128), its K and V scales are two scalar loads.
+#include <mutex>
+
 #include "qfa_device.h"
 #include "qfa_launch.h"
 
 namespace qfa {
 namespace {
+
+// Split-K partials of qfa_decode_noalloc, for callers that cannot allocate.
+// Each device holds its own copy from library load until the process ends.
+// Host code must never pass this name to a kernel (on the host it is only a
+// stand-in): decode_scratch() looks up each device's address once.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
 
 constexpr int kDecWaves = 8;
 constexpr int kWaveTokens = kDecodeChunk / kDecWaves;  // 128
@@ -546,6 +554,35 @@ hipError_t launch_dec(const DecParams& p, int B, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // The symbol's address is per device: look it up with that device current.
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int B, int Hq, int S_max, int D) {
   const long splits = (S_max + kDecodeChunk - 1) / kDecodeChunk;

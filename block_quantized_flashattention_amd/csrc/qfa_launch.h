@@ -101,4 +101,10 @@ constexpr int kDecodeChunk = 1024;
 size_t decode_workspace_bytes(int B, int Hq, int S_max, int D);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Size of the library's static decode scratch (qfa_decode_noalloc).
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+// Device address of that scratch on the device `stream` runs on (looked up
+// once per device, then cached); never allocates.
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 }  // namespace qfa

@@ -26,7 +26,9 @@
  *     codes per byte, so their innermost extent is dim/2 bytes.
  *   - A "block" is `block_rows` consecutive sequence rows times all `dim`
  *     channels of one (batch, head); the last block of a sequence may be short.
- *   - The library holds no mutable global state; calls are reentrant.
+ *   - The library holds no mutable global state and calls are reentrant,
+ *     with one exception: qfa_decode_noalloc works in a static per-device
+ *     scratch array (see there).
  */
 #ifndef QFA_H
 #define QFA_H
@@ -49,7 +51,8 @@ typedef enum {
   QFA_ERR_ENUM = 3,         /* an enumeration value is unknown */
   QFA_ERR_UNSUPPORTED = 4,  /* a valid combination this build does not implement */
   QFA_ERR_WORKSPACE = 5,    /* decode workspace missing or too small */
-  QFA_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
+  QFA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
+  QFA_ERR_SCRATCH = 7       /* qfa_decode_noalloc: the call needs more than the static scratch */
 } qfa_status;
 
 typedef enum { QFA_F32 = 0, QFA_F16 = 1, QFA_BF16 = 2 } qfa_float;
@@ -248,6 +251,33 @@ QFA_API int qfa_decode(const void* q, int q_dtype, int B, int Hq, int Hkv, int D
                int kv_block, int kv_scale_dtype, int S_max, int layout, const int32_t* seq_lens,
                float softmax_scale, void* out, int out_dtype, void* workspace,
                size_t workspace_bytes, void* stream);
+
+/*
+ * qfa_decode_noalloc -- qfa_decode without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, arithmetic, kernels and results as qfa_decode (bit for bit),
+ * except that the split-K partials go to a static device array of
+ * qfa_decode_noalloc_max_bytes() bytes (8 MiB) that the library holds on each
+ * GPU it runs on until the process ends. The call allocates nothing: on its
+ * first use on a device it only looks up that device's copy of the array.
+ * A call that needs more partial space than the array holds
+ * (qfa_decode_workspace_bytes(B, Hq, S_max, D) > the maximum, when S_max >
+ * 1024) returns QFA_ERR_SCRATCH and launches nothing; with D = 128 the limit
+ * is B * Hq * ceil(S_max / 1024) <= 16131 (e.g. B=32, Hq=32, S_max up to
+ * 15360). The array's contents on entry do not matter (every partial read is
+ * written first by the same call). All calls on one GPU share the array:
+ * calls that may overlap on one GPU (different streams, or host threads
+ * without ordering) race and must be serialized by the caller.
+ */
+QFA_API size_t qfa_decode_noalloc_max_bytes(void);
+QFA_API int qfa_decode_noalloc(const void* q, int q_dtype, int B, int Hq, int Hkv, int D,
+                               const void* k_cache, const void* v_cache, const void* k_scales,
+                               const void* v_scales, int kv_qtype, int kv_block,
+                               int kv_scale_dtype, int S_max, int layout,
+                               const int32_t* seq_lens, float softmax_scale, void* out,
+                               int out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,14 +25,15 @@ def test_exports_every_declared_function(L):
     assert set(names) == {"qfa_version", "qfa_status_string", "qfa_block_quant",
                           "qfa_block_quant_multi", "qfa_rotate_block_quant", "qfa_kv_append",
                           "qfa_fwd",
-                          "qfa_decode_workspace_bytes", "qfa_decode"}
+                          "qfa_decode_workspace_bytes", "qfa_decode",
+                          "qfa_decode_noalloc_max_bytes", "qfa_decode_noalloc"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_status_strings(L):
-    for s in range(7):
-        assert L.qfa_status_string(s)
+    for s in range(8):
+        assert L.qfa_status_string(s) != b"unknown status"
     assert L.qfa_status_string(99) == b"unknown status"
     assert L.qfa_version() >= 100
 
@@ -180,3 +181,29 @@ def test_decode_validation(L):
     assert dec(L, wsb=need - 1) == WS
     assert dec(L, k=MIS, wsb=need) == UNSUP
     assert dec(L, B=0, q=None, k=None, v=None) == OK
+
+
+def dec_na(L, q=P, qdt=F16, B=2, Hq=4, Hkv=2, D=128, k=P, v=P, ks=P, vs=P, qt=I8, kb=256,
+           sdt=F16, S_max=4096, layout=BNSD, lens=P, scale=0.1, out=P, odt=F16):
+    return L.qfa_decode_noalloc(q, qdt, B, Hq, Hkv, D, k, v, ks, vs, qt, kb, sdt, S_max, layout,
+                                lens, ctypes.c_float(scale), out, odt, None)
+
+
+def test_decode_noalloc_validation(L):
+    """The allocation-free decode validates as qfa_decode does and refuses a
+    call whose split-K partials would not fit the static scratch, before any
+    device call (these return during host-side validation)."""
+    SCRATCH = 7
+    cap = L.qfa_decode_noalloc_max_bytes()
+    assert cap == 8 << 20
+    assert dec_na(L, qdt=9) == ENUM
+    assert dec_na(L, Hq=5) == SHAPE
+    assert dec_na(L, D=32) == UNSUP
+    assert dec_na(L, lens=None) == NULL
+    assert dec_na(L, k=MIS) == UNSUP
+    assert dec_na(L, B=0, q=None, k=None, v=None) == OK
+    # D=128: B * Hq * ceil(S_max/1024) * 130 floats must fit 8 MiB.
+    assert L.qfa_decode_workspace_bytes(32, 32, 16384, 128) > cap
+    assert dec_na(L, B=32, Hq=32, Hkv=32, S_max=16384) == SCRATCH
+    assert dec_na(L, B=32, Hq=32, Hkv=32, S_max=16384, lens=None) == NULL  # validation first
+    assert L.qfa_status_string(SCRATCH) != b"unknown status"
