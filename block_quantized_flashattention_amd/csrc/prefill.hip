@@ -6,55 +6,53 @@
 //   o_i  = sum_j softmax_j(x_ij) * sv_j * Vc_j             online softmax, P.V on MFMA
 //
 // Design:
-//   * A workgroup of 4 wavefronts owns 128 query rows of one (batch, head);
-//     each wavefront owns 32 rows. Two workgroups share a CU (at most 256
-//     registers per lane), so one's softmax arithmetic overlaps the other's
-//     matrix work. Key tiles of 64 rows are double-buffered in LDS, K one tile
-//     ahead of V; each tile's codes are loaded into registers a step before
-//     they are staged, so a load has a step of compute to arrive; one barrier
-//     per tile.
+//   * A workgroup of 8 wavefronts (one per CU; 2 per SIMD) owns 256
+//     (query row, query head) pairs of one (batch, KV head): hpw query heads
+//     of the KV head (hpw = the largest power of two <= 8 dividing the GQA
+//     group) times 256/hpw consecutive rows. Each wavefront owns 32 rows of
+//     one head, and one staged K/V tile feeds all of them: under GQA every
+//     K/V tile is loaded, unpacked and converted once for up to 8 heads.
+//   * Two groups of four wavefronts, A (waves 0-3) and B (waves 4-7), run in
+//     anti-phase, one of each on every SIMD: in each phase one group issues
+//     the matrix work of a tile (S(t+1) = K Q^T and O += P(t) V(t)) while the
+//     other computes a tile's softmax on the vector unit; a barrier ends each
+//     phase and the groups swap. Matrix instructions of one wavefront run
+//     concurrently with vector instructions of the other, so the matrix unit
+//     and the vector unit are both kept busy rather than idling whenever the
+//     two wavefronts of a SIMD happen to be in the same kind of work.
+//   * The matrix-phase group also stages the next K and V tiles: codes are
+//     loaded into registers two phases ahead and written to LDS (K as bytes,
+//     INT4 widened to INT8; V transposed and converted exactly to fp16), and
+//     the next tiles' loads are issued; its vector instructions fill the
+//     issue slots between its matrix instructions.
 //   * Scores are formed transposed, S^T = K . Q^T, with
-//     v_mfma_i32_32x32x32_i8 (INT8 Q/K; INT4 K is widened to INT8 while it is
-//     staged) or v_mfma_f32_32x32x64_f8f6f4 (FP8 e4m3 Q/K). In the MFMA result
-//     layout each lane then holds one query row and 16 of every 32 keys, so
-//     row max and row sum are register reductions plus one exchange between
-//     the lane halves, and the probabilities are already in the register
-//     layout of the B operand of O^T += V^T . P^T on v_mfma_f32_32x32x16_f16:
-//     P never goes through LDS.
-//   * V is staged transposed ([channel][key], fp16): INT8, INT4 and e4m3 codes
-//     are exact in fp16 and are converted once per workgroup. Keys are
-//     permuted inside each group of 16 so that every lane reads its operand
-//     slice with one 16-byte LDS read.
-//   * Scale fold: with one K scale per tile, the row max is taken on the raw
-//     scores (INT8: the biased accumulator read as floats, see kBiasAcc) and
-//     each probability costs one FMA and one exp2:
-//     p = exp2(dot * (sq * sk * softmax_scale * log2 e) - m). The V block
-//     scale is folded into the accumulator (O is kept in units of the current
-//     V scale and rescaled when it changes). With per-token scales (INT4 K/V)
-//     each score and probability takes one more multiply.
-//   * The running row max is only raised when a tile's max exceeds it by more
-//     than 12 (log2 units; 8 with per-key scales, whose fp16 weights carry the
-//     V scale), so the O rescale is skipped on most tiles; the probabilities
-//     stay below 2^12 (exact softmax; fp16 holds them with its full 11-bit
-//     precision, far below its 65504 limit).
+//     v_mfma_i32_32x32x32_i8 (INT8 Q/K; INT4 K widened) or
+//     v_mfma_f32_32x32x64_f8f6f4 (FP8 e4m3 Q/K). Each lane then holds one
+//     query row and 16 of every 32 keys, so row max and row sum are register
+//     reductions plus one exchange between the lane halves, and the fp16
+//     probabilities land directly in the B-operand layout of
+//     O^T += V^T . P^T on v_mfma_f32_32x32x16_f16: P never goes through LDS.
+//   * Scale fold: with one K/V scale per tile, INT8 scores are read from an
+//     integer accumulator started at a bit pattern that makes the sum a float
+//     (see kBiasBits), and each probability costs one FMA and one exp2. O is
+//     kept in units of the current V block scale and rescaled when it
+//     changes. With per-key scales (INT4 K/V, one scale per token) each score
+//     takes one more multiply, the fp16 weights are p * sv_j / sv_ref with
+//     sv_ref the running maximum V scale (so every weight stays <= 2^slack
+//     whatever the scales' magnitude), and O is kept in units of sv_ref.
+//   * The running row max is raised only when a tile's max exceeds it by more
+//     than the slack (log2 units), so the O rescale is skipped on most tiles;
+//     the probabilities stay below 2^slack (exact softmax; fp16 holds them
+//     with its full precision).
 //   * Row sums add the fp16-rounded probabilities with v_dot2_f32_f16, i.e.
 //     exactly the weights the P.V product uses.
-//   * One step per key tile: the max of tile t and the rare rescale, then
-//     (INT8 with one scale per tile) one straight-line block holding S(t+1)
-//     on the matrix unit, the exponentials of tile t, the staging of the next
-//     tiles and P(t) V(t). FP8 and per-token scales issue S(t+1) in a block
-//     of its own before the softmax (measured faster for them).
-//   * Causal: tiles past a workgroup's last row are skipped and the mask is a
-//     compile-time variant used only on tiles crossing a wavefront's diagonal
-//     (in the straight-line INT8 step, a wavefront whose rows all lie above a
-//     tile runs it fully masked rather than branching around it; the other
-//     paths skip it). Work is ordered longest first.
+//   * Causal: tiles past the workgroup's last row are never loaded; a
+//     wavefront skips tiles above its rows; the mask is a compile-time
+//     variant used only on tiles that cross a wavefront's diagonal or the
+//     end of the keys. Work is ordered longest first.
 //   * XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
-//     all query heads and row blocks of one (batch, KV head) are given ids on
-//     the same XCD and its K/V codes stay in that XCD's L2.
-//   * Epilogue: a lane holds 64 channels of one row, so direct stores would
-//     touch 32 rows per instruction; fp16/bf16 output is staged in LDS per
-//     wavefront and written with 16-byte stores along the rows.
+//     all work of one (batch, KV head) runs on one XCD and its K/V codes stay
+//     in that XCD's L2.
 #include <type_traits>
 
 #include "qfa_device.h"
@@ -63,14 +61,15 @@
 namespace qfa {
 namespace {
 
-constexpr int kNW = 4;            // wavefronts per workgroup
-constexpr int kThreads = 64 * kNW;
-constexpr int kBM = 32 * kNW;     // query rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPairs = 256;       // (row, head) pairs per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kXcds = 8;
+constexpr int kScaleRing = 3;     // tiles of scales in flight
 constexpr float kRescaleSlack = 12.0f;
-// With per-key V scales the fp16 weight is p * sv; the smaller slack keeps it
-// below 2^8 * sv, far from the fp16 limit for any plausible V scale.
+// With per-key scales the fp16 weight is p * sv_j / sv_ref <= p; the smaller
+// slack keeps the weights and their row sums well inside fp16.
 constexpr float kRescaleSlackTok = 8.0f;
 
 struct FwdParams {
@@ -82,29 +81,38 @@ struct FwdParams {
   const void* vs;
   void* out;
   int B, Hq, Hkv, Sq, Sk, group;
+  int hpw, rph, n_rb, n_hg;     // heads per workgroup, rows per head, row blocks, head groups
   long q_row, q_head, q_batch;  // byte strides of Q codes
   long k_row, k_head, k_batch;  // byte strides of K codes
   long v_row, v_head, v_batch;  // byte strides of V codes
   long o_row, o_head, o_batch;  // element strides of out
   int q_block, kv_block, nqblk, nkblk;
   int q_scale_f16, kv_scale_f16;
-  int k_qtype, v_qtype, out_dtype;
+  int out_dtype;
   float scale_log2;  // softmax_scale * log2(e)
-  int n_mblocks;
   int xcd_order;     // 1: XCD-grouped workgroup order
 };
 
+// LDS of one workgroup, as separate arrays so that the compiler can tell the
+// buffers apart (a tile's operand reads and the next tile's staging writes
+// then need no ordering): K tiles [64 keys][D + 16 pad] bytes; V tiles held
+// transposed, [D][64 + 8 pad] fp16, keys permuted in groups of 16 (see vt_pos)
+// so that each lane's MFMA operand is one 16-byte read; a ring of per-tile
+// scales (K and V scale per key with per-key scales, else slot 0, and the V
+// scale O is expressed in while the tile is processed); the fp16/bf16 output
+// staged per wavefront for coalesced row stores.
 template <int D>
-struct KStage {
-  static constexpr int kStride = D + 16;    // bytes per staged K row
-  uint8_t k[kBN * kStride];
+struct Geo {
+  static constexpr int kKStride = D + 16;
+  static constexpr int kVStride = kBN + 8;
+  static constexpr int kKBytes = kBN * kKStride;
+  static constexpr int kVElems = D * kVStride;
+  static constexpr int kOutStride = D + 8;
 };
-template <int D>
-struct VStage {
-  static constexpr int kStride = kBN + 8;   // fp16 elements per staged V^T row
-  _Float16 vt[D * kStride];
-  float ksc[kBN];                           // K and V scales of the same tile's keys
-  float vsc[kBN];
+struct ScaleRing {
+  float ks[kScaleRing][kBN];
+  float vs[kScaleRing][kBN];
+  float vref[kScaleRing];
 };
 
 // Position of key `key` (0..kBN-1) inside a staged V^T row: groups of 4 keys
@@ -126,15 +134,19 @@ __device__ __forceinline__ uint2 unpack_int4x8(uint32_t w) {
   return make_uint2(o0, o1);
 }
 
-// Four signed bytes of `w` as two packed fp16 pairs (exact): the byte is
-// placed in the mantissa of 1024 + (byte ^ 0x80) and 1152 is subtracted.
-__device__ __forceinline__ void i8x4_to_h(uint32_t w, f16x2& lo, f16x2& hi) {
-  const uint32_t u = w ^ 0x80808080u;
-  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);  // bytes 0,1
-  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u);  // bytes 2,3
+// Bytes 0 and 1 of `u` (signed codes) as an exact fp16 pair: the byte with
+// its sign bit flipped goes into the mantissa of 1024, and 1152 is subtracted.
+__device__ __forceinline__ f16x2 i8pair_to_h(uint32_t u, uint32_t sel) {
   const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  lo = __builtin_bit_cast(f16x2, a) - bias;
-  hi = __builtin_bit_cast(f16x2, b) - bias;
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u ^ 0x80808080u, sel)) - bias;
+}
+
+// The nibbles at bits 0-3 and 16-19 of w (two's-complement codes) as an exact
+// fp16 pair: flip the sign bit, place the nibbles under the exponent of 1024
+// (1032 + code), subtract 1032.
+__device__ __forceinline__ f16x2 i4pair_to_h(uint32_t w) {
+  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  return __builtin_bit_cast(f16x2, ((w ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u) - bias;
 }
 
 // Code types of K and V handled by one kernel instance.
@@ -145,146 +157,177 @@ template <> struct KVTypes<KV_I4_I4> { static constexpr int K = QFA_INT4, V = QF
 template <> struct KVTypes<KV_I8_I4> { static constexpr int K = QFA_INT8, V = QFA_INT4; };
 template <> struct KVTypes<KV_F8_F8> { static constexpr int K = QFA_FP8_E4M3, V = QFA_FP8_E4M3; };
 
-// Registers holding one prefetched tile of K and V codes (and scales) for this thread.
-struct Prefetch {
-  uint4 k[kBN * 128 / 16 / kThreads];
-  uint2 v[4];
-  uint32_t ks, vs;  // raw dwords holding this thread's key's scales
-  uint32_t shift;   // bit offset of an fp16 scale inside its dword
+// Staging geometry (one unit per thread and tile):
+//   K: key tid / 8, eighth tid % 8 of its row: D/8 staged bytes (D/16 source
+//      bytes for INT4).
+//   V: keys 2 (tid % 32) and 2 (tid % 32) + 1, channels (tid / 32) * D/16 +
+//      [0, D/16): D/16 source bytes (D/32 for INT4) per key.
+// Threads of group A (tid < 256) hold keys 0-31 of K and channels 0..D/2-1 of
+// V; group B the rest, so each group stages half of every tile.
+template <int D, int KQT, int VQT>
+struct Stage {
+  static constexpr int kKSrc = KQT == QFA_INT4 ? D / 16 : D / 8;   // bytes
+  static constexpr int kVCh = D / 16;                              // channels per key
+  static constexpr int kVSrc = VQT == QFA_INT4 ? kVCh / 2 : kVCh;  // bytes per key
+  uint32_t k[kKSrc / 4];
+  uint32_t v[2][kVSrc / 4 > 0 ? kVSrc / 4 : 1];
 };
 
-__device__ __forceinline__ float scale_from_bits(uint32_t bits, bool f16) {
-  return f16 ? f16_bits_to_f32(bits) : __uint_as_float(bits);
+template <int N>
+__device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
+  if constexpr (N == 4) {
+    const uint4 x = *(const uint4*)p;
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+  } else if constexpr (N == 2) {
+    const uint2 x = *(const uint2*)p;
+    w[0] = x.x; w[1] = x.y;
+  } else {
+    w[0] = *(const uint32_t*)p;
+  }
 }
 
-// Issue the loads of one tile's codes and scales into registers. Every load is
-// unconditional (keys past the end are clamped to the last key, whose codes
-// are finite and whose scores are masked) and nothing reads the loaded values
-// before store_tile, so the loads stay in flight across the compute of the
-// tiles in between. In-head offsets are 32-bit (checked on the host).
+// Issue the loads of this thread's K and V units of a tile. Keys past the end
+// are clamped to the last key (finite codes, masked scores). Nothing reads the
+// registers before the matching stage_tile, two phases later.
 template <int D, int KQT, int VQT>
-__device__ __forceinline__ void fetch_tile(Prefetch& f, const FwdParams& p, const uint8_t* kbase,
-                                           const uint8_t* vbase, long sbase, int kn0, int vn0) {
+__device__ __forceinline__ void fetch_tile(Stage<D, KQT, VQT>& f, const FwdParams& p,
+                                           const uint8_t* kbase, const uint8_t* vbase, int kn0,
+                                           int vn0) {
+  using S = Stage<D, KQT, VQT>;
   const int tid = threadIdx.x;
   const int last = p.Sk - 1;
-  int n0 = kn0;
-  const uint32_t krow = (uint32_t)p.k_row, vrow = (uint32_t)p.v_row;
-  constexpr int kChunks = kBN * D / 16;  // 16 codes per chunk
-  static_assert(kChunks % kThreads == 0, "K chunks per thread");
-#pragma unroll
-  for (int i = 0; i < kChunks / kThreads; ++i) {
-    const int c = tid + i * kThreads;
-    const uint32_t key = (uint32_t)min(n0 + c / (D / 16), last);
-    const uint32_t col = (uint32_t)(c % (D / 16)) * 16u;
-    if constexpr (KQT == QFA_INT4) {
-      const uint2 w = *(const uint2*)(kbase + (key * krow + col / 2u));
-      f.k[i] = make_uint4(w.x, w.y, 0u, 0u);
-    } else {
-      f.k[i] = *(const uint4*)(kbase + (key * krow + col));
-    }
+  {
+    const uint32_t key = (uint32_t)min(kn0 + tid / 8, last);
+    load_words(f.k, kbase + (key * (uint32_t)p.k_row + (uint32_t)(tid % 8) * S::kKSrc));
   }
-  // V: 4 keys x 8 channels per thread (threads past the last unit repeat a unit).
-  n0 = vn0;
-  constexpr int kUnits = (kBN / 4) * (D / 8);
-  const int u = tid % kUnits;
-  const int kg = u % (kBN / 4), dg = u / (kBN / 4);
+  const int kp = tid % 32, cg = tid / 32;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t key = (uint32_t)min(n0 + kg * 4 + r, last);
-    if constexpr (VQT == QFA_INT4) {
-      f.v[r] = make_uint2(*(const uint32_t*)(vbase + (key * vrow + (uint32_t)dg * 4u)), 0u);
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t key = (uint32_t)min(vn0 + 2 * kp + r, last);
+    const uint8_t* src = vbase + (key * (uint32_t)p.v_row + (uint32_t)cg * S::kVSrc);
+    if constexpr (S::kVSrc >= 4) {
+      load_words(f.v[r], src);
     } else {
-      f.v[r] = *(const uint2*)(vbase + (key * vrow + (uint32_t)dg * 8u));
+      f.v[r][0] = *(const uint16_t*)src;  // D = 64 INT4: 2 bytes per key
     }
-  }
-  // Scale of this thread's key (slot 0 alone is read when one scale covers the
-  // tile), as the aligned dword holding it, for either scale type.
-  const int key = min(n0 + (tid % kBN), last);
-  const long g = sbase + (p.kv_block == 1 ? key : key / p.kv_block);
-  const long widx = p.kv_scale_f16 ? (g >> 1) : g;
-  f.shift = p.kv_scale_f16 ? (uint32_t)(g & 1) * 16u : 0u;
-  f.ks = ((const uint32_t*)p.ks)[widx];
-  f.vs = ((const uint32_t*)p.vs)[widx];
-}
-
-template <int D, int KQT>
-__device__ __forceinline__ void store_k(KStage<D>& st, const Prefetch& f) {
-  const int tid = threadIdx.x;
-  constexpr int kChunks = kBN * D / 16;
-#pragma unroll
-  for (int i = 0; i < kChunks / kThreads; ++i) {
-    const int c = tid + i * kThreads;
-    const int key = c / (D / 16);
-    const int col = (c % (D / 16)) * 16;
-    uint4 w = f.k[i];
-    if constexpr (KQT == QFA_INT4) {
-      const uint2 a = unpack_int4x8(w.x), b = unpack_int4x8(w.y);
-      w = make_uint4(a.x, a.y, b.x, b.y);
-    }
-    *(uint4*)(st.k + key * KStage<D>::kStride + col) = w;
   }
 }
 
-template <int D, int VQT>
-__device__ __forceinline__ void store_v(VStage<D>& st, const Prefetch& f, bool scale_f16) {
+template <int D, int KQT, int VQT>
+__device__ __forceinline__ void stage_k(uint8_t* kbuf, const Stage<D, KQT, VQT>& f) {
   const int tid = threadIdx.x;
-  constexpr int kUnits = (kBN / 4) * (D / 8);
-  if (kUnits >= kThreads || tid < kUnits) {
-    const int kg = tid % (kBN / 4), dg = tid / (kBN / 4);
-    const int pos = vt_pos(kg * 4);
-    if constexpr (VQT == QFA_INT8) {
-      // Transpose bytes first: one permute gathers channels (c, c+1) of two
-      // keys, so each conversion yields a key pair of one channel, which is
-      // what the transposed store needs.
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        f16x2 pr[2][4];  // [key pair][channel 4d + i]
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-          const uint32_t wa = d ? f.v[2 * kp].y : f.v[2 * kp].x;
-          const uint32_t wb = d ? f.v[2 * kp + 1].y : f.v[2 * kp + 1].x;
-          i8x4_to_h(__builtin_amdgcn_perm(wb, wa, 0x05010400u), pr[kp][0], pr[kp][1]);
-          i8x4_to_h(__builtin_amdgcn_perm(wb, wa, 0x07030602u), pr[kp][2], pr[kp][3]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f16x4 col = {pr[0][i][0], pr[0][i][1], pr[1][i][0], pr[1][i][1]};
-          *(f16x4*)(st.vt + (dg * 8 + 4 * d + i) * VStage<D>::kStride + pos) = col;
-        }
-      }
+  uint8_t* dst = kbuf + (tid / 8) * Geo<D>::kKStride + (tid % 8) * (D / 8);
+  if constexpr (KQT == QFA_INT4) {
+    if constexpr (D == 128) {
+      const uint2 a = unpack_int4x8(f.k[0]), b = unpack_int4x8(f.k[1]);
+      *(uint4*)dst = make_uint4(a.x, a.y, b.x, b.y);
     } else {
-    f16x2 val[4][4];  // [key][channel pair]
+      const uint2 a = unpack_int4x8(f.k[0]);
+      *(uint2*)dst = a;
+    }
+  } else if constexpr (D == 128) {
+    *(uint4*)dst = make_uint4(f.k[0], f.k[1], f.k[2], f.k[3]);
+  } else {
+    *(uint2*)dst = make_uint2(f.k[0], f.k[1]);
+  }
+}
+
+// V^T: channel c of keys (2kp, 2kp+1) as one fp16 pair (exact for INT8, INT4
+// and e4m3 codes).
+template <int D, int KQT, int VQT>
+__device__ __forceinline__ void stage_v(_Float16* vbuf, const Stage<D, KQT, VQT>& f) {
+  using S = Stage<D, KQT, VQT>;
+  const int tid = threadIdx.x;
+  const int kp = tid % 32, cg = tid / 32;
+  _Float16* base = vbuf + (cg * S::kVCh) * Geo<D>::kVStride + vt_pos(2 * kp);
+  auto put = [&](int c, f16x2 h) __attribute__((always_inline)) { *(f16x2*)(base + c * Geo<D>::kVStride) = h; };
+  if constexpr (VQT == QFA_INT4) {
+    // Nibble c of key a (b) sits in byte c/2 of its word(s); gather byte j of
+    // both keys, then shift each nibble pair under the exponent.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint2 w = f.v[r];
-      if constexpr (VQT == QFA_INT4) w = unpack_int4x8(w.x);
-      if constexpr (VQT == QFA_FP8_E4M3) {
+    for (int w = 0; w < (S::kVSrc + 3) / 4; ++w) {
+      const uint32_t a = f.v[0][w], b = f.v[1][w];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t ww = j ? w.y : w.x;
-          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww, false);
-          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ww, true);
-          val[r][2 * j] = (f16x2){(_Float16)a[0], (_Float16)a[1]};
-          val[r][2 * j + 1] = (f16x2){(_Float16)b[0], (_Float16)b[1]};
-        }
-      } else {
-        i8x4_to_h(w.x, val[r][0], val[r][1]);
-        i8x4_to_h(w.y, val[r][2], val[r][3]);
+      for (int j = 0; j < (S::kVSrc >= 4 ? 4 : S::kVSrc); j += 2) {
+        // bytes j, j+1 of a in bytes 0-1, of b in bytes 2-3
+        const uint32_t sel = (j == 0) ? 0x05040100u : 0x07060302u;
+        const uint32_t u = __builtin_amdgcn_perm(b, a, sel);
+        // channel 2j' + s of byte j' (j' = j, j+1): a in bits 0-3 / b in bits 16-19
+        // after shifting byte j' of each half down
+        const uint32_t pr0 = (u & 0x00FF00FFu);          // byte j of a, byte j of b
+        const uint32_t pr1 = ((u >> 8) & 0x00FF00FFu);   // byte j+1 of a, of b
+        const int c0 = 8 * w + 2 * j;
+        put(c0 + 0, i4pair_to_h(pr0));
+        put(c0 + 1, i4pair_to_h(pr0 >> 4));
+        put(c0 + 2, i4pair_to_h(pr1));
+        put(c0 + 3, i4pair_to_h(pr1 >> 4));
       }
     }
+  } else if constexpr (VQT == QFA_FP8_E4M3) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = e >> 1, s = e & 1;
-      f16x4 col = {val[0][j][s], val[1][j][s], val[2][j][s], val[3][j][s]};
-      *(f16x4*)(st.vt + (dg * 8 + e) * VStage<D>::kStride + pos) = col;
+    for (int w = 0; w < S::kVSrc / 4; ++w) {
+      const uint32_t a = f.v[0][w], b = f.v[1][w];
+      const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+      const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+      put(4 * w + 0, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+      put(4 * w + 1, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+      put(4 * w + 2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+      put(4 * w + 3, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
     }
+  } else {
+#pragma unroll
+    for (int w = 0; w < S::kVSrc / 4; ++w) {
+      const uint32_t a = f.v[0][w], b = f.v[1][w];
+      const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+      const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+      put(4 * w + 0, i8pair_to_h(lo, 0x05010400u));
+      put(4 * w + 1, i8pair_to_h(lo, 0x07030602u));
+      put(4 * w + 2, i8pair_to_h(hi, 0x05010400u));
+      put(4 * w + 3, i8pair_to_h(hi, 0x07030602u));
     }
   }
-  // Every thread holds the scales of key tid % kBN; the copies write equal
-  // values, which keeps this store free of a branch.
-  const uint32_t mask = scale_f16 ? 0xFFFFu : 0xFFFFFFFFu;
-  st.ksc[tid % kBN] = scale_from_bits((f.ks >> f.shift) & mask, scale_f16);
-  st.vsc[tid % kBN] = scale_from_bits((f.vs >> f.shift) & mask, scale_f16);
+}
+
+// Scales of one tile, handled by wavefront 0 (lane = key): loaded a tile
+// ahead, then written to the ring slot of the tile. With per-key scales the V
+// scales are divided by the running maximum V scale `vref` (carried by the
+// wavefront across tiles), which is also stored for the tile.
+// The raw bits of this lane's K and V scale (fp16: the low half; fp32: both
+// halves). They are converted only when staged, a tile later: converting
+// them at load time would make the wavefront wait for the load.
+struct ScaleRegs {
+  uint32_t klo, khi, vlo, vhi;
+};
+
+__device__ __forceinline__ void fetch_scales(ScaleRegs& r, const FwdParams& p, long sbase, int n0,
+                                             bool tok) {
+  const int key = min(n0 + (int)(threadIdx.x & 63), p.Sk - 1);
+  const long g = sbase + (tok ? (p.kv_block == 1 ? key : key / p.kv_block) : n0 / p.kv_block);
+  // Two 16-bit loads per scale, neither past the scale's own bytes.
+  const long i0 = p.kv_scale_f16 ? g : 2 * g, i1 = p.kv_scale_f16 ? g : 2 * g + 1;
+  r.klo = ((const uint16_t*)p.ks)[i0];
+  r.khi = ((const uint16_t*)p.ks)[i1];
+  r.vlo = ((const uint16_t*)p.vs)[i0];
+  r.vhi = ((const uint16_t*)p.vs)[i1];
+}
+
+template <bool TOK>
+__device__ __forceinline__ void stage_scales(ScaleRing& sm, int slot, const ScaleRegs& r,
+                                             bool f16, float& vref_run) {
+  const int lane = threadIdx.x & 63;
+  const float ks = f16 ? f16_bits_to_f32(r.klo) : __uint_as_float(r.klo | (r.khi << 16));
+  const float vs = f16 ? f16_bits_to_f32(r.vlo) : __uint_as_float(r.vlo | (r.vhi << 16));
+  sm.ks[slot][lane] = ks;
+  if constexpr (TOK) {
+    float m = vs;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    vref_run = fmaxf(vref_run, m);
+    sm.vs[slot][lane] = vref_run > 0.0f ? vs / vref_run : 0.0f;
+    if (lane == 0) sm.vref[slot] = vref_run;
+  } else {
+    if (lane == 0) sm.vref[slot] = vs;
+  }
 }
 
 template <int D, bool FP8>
@@ -300,17 +343,6 @@ struct QK {
       return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
     }
   }
-  // a . b plus an accumulator that starts at 0x3E22F983 in every element,
-  // given as the inline constant 1/(2 pi) (INT8 only; the compiler does not
-  // fold a splat into that operand). The result is only read as the
-  // accumulator of the next matrix instruction of the same kind, which needs
-  // no wait states; the leading s_nop covers a vector write of a or b just
-  // before, which the hazard check cannot see through the asm.
-  static __device__ __forceinline__ Acc mma_biased(const Op& a, const Op& b) {
-    Acc r;
-    asm("s_nop 2\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, 0x3e22f983" : "=&v"(r) : "v"(a), "v"(b));
-    return r;
-  }
   static __device__ __forceinline__ Op load(const uint8_t* p) {
     if constexpr (FP8) {
       const i32x4 lo = *(const i32x4*)p;
@@ -322,250 +354,317 @@ struct QK {
   }
 };
 
-// Key offset (within the tile) of accumulator register r of 32-key block kb,
-// for the lane half `half`: MFMA 32x32 result rows 8*(r/4) + 4*half + r%4.
+// Key offset (within the tile) of accumulator register r of 32-key block kb
+// for lane half 0 (lane half 1 holds keys 4 further): MFMA 32x32 result rows
+// 8*(r/4) + 4*half + r%4.
 __device__ __forceinline__ constexpr int key_of(int kb, int r) { return kb * 32 + 8 * (r >> 2) + (r & 3); }
 
-// RAGGED (non-causal only): Sk is not a multiple of the tile, so the last tile
-// needs the end-of-keys mask; otherwise no tile does and the mask is compiled out.
-template <int D, int KVM, bool CAUSAL, bool TOK, bool RAGGED>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
+template <int D, int KVM, bool CAUSAL, bool TOK>
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   constexpr bool FP8 = KVM == KV_F8_F8;
   constexpr int KQT = KVTypes<KVM>::K, VQT = KVTypes<KVM>::V;
   using T = QK<D, FP8>;
   using Op = typename T::Op;
   using Acc = typename T::Acc;
+  using St = Stage<D, KQT, VQT>;
+  using G = Geo<D>;
   constexpr int kDB = D / 32;  // 32-channel blocks of the output
-  // INT8 scores with one scale per tile: the integer accumulator starts at the
-  // bit pattern kBiasBits of the float kBiasInt * 2^-26 (the inline constant
-  // 1/(2 pi) of the matrix instruction), so 'kBiasBits + dot' is the bit
-  // pattern of the float (kBiasInt + dot) * 2^-26 exactly as long as the sum
-  // stays in that binade, i.e. -2292099 <= dot < 6096509, which any 8-bit
-  // codes with D <= 128 satisfy (|dot| <= 128 * 128 * 128). The scores then
-  // need no integer-to-float conversion, and their max is a float max.
+  constexpr int kNK = 2 * T::kSteps;  // K operand reads (and QK MFMAs) per tile
+  constexpr int kNV = 4 * kDB;        // V operand reads (and PV MFMAs) per tile
+  // INT8 scores with one scale per tile: the integer accumulator starts at
+  // the bit pattern kBiasBits of the float kBiasInt * 2^-26, so
+  // 'kBiasBits + dot' is the bit pattern of the float (kBiasInt + dot) * 2^-26
+  // exactly as long as the sum stays in that binade, i.e.
+  // -2292099 <= dot < 6096509, which any 8-bit codes with D <= 128 satisfy
+  // (|dot| <= 128 * 128 * 128). The scores then need no integer-to-float
+  // conversion, and their max is a float max.
   constexpr bool kBiasAcc = !FP8 && !TOK;
   constexpr uint32_t kBiasBits = 0x3E22F983u;
   constexpr int kBiasInt = 10680707;  // 2^23 + 0x22F983
   static_assert(D <= 128, "biased INT8 scores need |dot| < 2^21");
-  __shared__ KStage<D> kst[2];
-  __shared__ VStage<D> vst[2];
+  constexpr float kSlack = TOK ? kRescaleSlackTok : kRescaleSlack;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  __shared__ __align__(16) uint8_t kbuf0[G::kKBytes];
+  __shared__ __align__(16) uint8_t kbuf1[G::kKBytes];
+  __shared__ __align__(16) _Float16 vbuf0[G::kVElems];
+  __shared__ __align__(16) _Float16 vbuf1[G::kVElems];
+  __shared__ __align__(16) ScaleRing sc;
+  __shared__ __align__(16) uint16_t obuf[kWaves * 32 * G::kOutStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = wave >> 2;   // 0: group A, 1: group B
   const int half = lane >> 5;  // lane half: keys 4*half + {0..3} of every 8
   const int col = lane & 31;   // query row of this lane within the wavefront
 
-  // Work item of this workgroup.
-  int mb, h, b;
+  // Work item: (batch, KV head, head group, row block).
+  int rb, b, kvh, hg;
   {
     const int id = blockIdx.x;
-    const int G = p.group;
     const int ngroups = p.B * p.Hkv;
-    int mrank, gidx, hig;
+    int rank, gidx;
     if (p.xcd_order) {
       const int xcd = id % kXcds, k = id / kXcds;
-      const int per_rank = (ngroups / kXcds) * G;
-      mrank = k / per_rank;
+      const int per_rank = (ngroups / kXcds) * p.n_hg;
+      rank = k / per_rank;
       const int rem = k % per_rank;
-      gidx = (rem / G) * kXcds + xcd;
-      hig = rem % G;
+      gidx = (rem / p.n_hg) * kXcds + xcd;
+      hg = rem % p.n_hg;
     } else {
-      const int per_rank = ngroups * G;
-      mrank = id / per_rank;
+      const int per_rank = ngroups * p.n_hg;
+      rank = id / per_rank;
       const int rem = id % per_rank;
-      gidx = rem / G;
-      hig = rem % G;
+      gidx = rem / p.n_hg;
+      hg = rem % p.n_hg;
     }
-    mb = CAUSAL ? p.n_mblocks - 1 - mrank : mrank;
+    rb = CAUSAL ? p.n_rb - 1 - rank : rank;
     b = gidx / p.Hkv;
-    h = (gidx % p.Hkv) * G + hig;
+    kvh = gidx % p.Hkv;
   }
-  const int kvh = h / p.group;
-  const int m0 = mb * kBM;
-  const int wrow0 = m0 + wave * 32;
+  const int h = kvh * p.group + hg * p.hpw + wave % p.hpw;
+  const int m0 = rb * p.rph;
+  const int wrow0 = m0 + 32 * (wave / p.hpw);
   const int qrow = wrow0 + col;
   const bool qvalid = qrow < p.Sq;
 
   // Q slice of this lane (B operand of S^T = K . Q^T), kept in registers.
   Op qop[T::kSteps];
   {
-    const uint8_t* qp = p.q + (long)b * p.q_batch + (long)h * p.q_head + (long)qrow * p.q_row;
+    const uint8_t* qp = p.q + (long)b * p.q_batch + (long)h * p.q_head + (long)min(qrow, p.Sq - 1) * p.q_row;
 #pragma unroll
     for (int s = 0; s < T::kSteps; ++s) {
-      qop[s] = (Op){};
-      if (qvalid) qop[s] = T::load(qp + s * 2 * T::kSlice + half * T::kSlice);
+      qop[s] = T::load(qp + s * 2 * T::kSlice + half * T::kSlice);
+      if (!qvalid) qop[s] = (Op){};
     }
   }
-  const float sq = qvalid ? load_scale(p.qs, ((long)b * p.Hq + h) * p.nqblk + qrow / p.q_block,
-                                       p.q_scale_f16)
-                          : 0.0f;
-  const float cq = sq * p.scale_log2;
+  const float sq = load_scale(p.qs, ((long)b * p.Hq + h) * p.nqblk + min(qrow, p.Sq - 1) / p.q_block,
+                              p.q_scale_f16);
+  const float cq = qvalid ? sq * p.scale_log2 : 0.0f;
 
   const uint8_t* kbase = p.k + (long)b * p.k_batch + (long)kvh * p.k_head;
   const uint8_t* vbase = p.v + (long)b * p.v_batch + (long)kvh * p.v_head;
   const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
+
+  // The accumulator start of the biased INT8 scores, kept in registers (an
+  // opaque copy, so the compiler does not rebuild the splat for every use).
+  i32x16 bias_acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bias_acc[i] = (int)kBiasBits;
+  if constexpr (kBiasAcc) asm volatile("" : "+v"(bias_acc));
 
   f32x16 o[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i) o[i] = (f32x16){};
   float m_run = -INFINITY;  // reference row max (log2 units)
   float l_run = 0.0f;       // row sum of this lane half, in units of exp2(-m_run)
-  float sv_cur = 0.0f;      // V scale O is expressed in (one scale per tile)
+  float sv_cur = 0.0f;      // V scale O is expressed in
+  float vref_run = 0.0f;    // (wavefront 0, per-key scales) running max V scale
 
-  const int n_end = CAUSAL ? min(p.Sk, m0 + kBM) : p.Sk;
+  const int n_end = CAUSAL ? min(p.Sk, m0 + p.rph) : p.Sk;
   const int ntiles = (n_end + kBN - 1) / kBN;
-  // Keys beyond this offset from the tile start are masked for this lane
-  // (causal diagonal or end of the keys), per lane half.
+  const int last_tile = ntiles - 1;
+  // Keys beyond this offset from the tile start are masked for this lane.
   const int lim_base = (CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1) - 4 * half;
-  auto wave_active = [&](int t) { return !CAUSAL || t * kBN <= wrow0 + 31; };
+  auto tile_n0 = [&](int t) __attribute__((always_inline)) { return min(t, last_tile) * kBN; };
 
-  // S^T tile t = K_t . Q^T from K buffer t % 2 (two 32-key blocks).
-  auto qk = [&](Acc* sacc, const KStage<D>& ks) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* krow = ks.k + (kb * 32 + col) * KStage<D>::kStride + half * T::kSlice;
-      if constexpr (kBiasAcc) {
-        sacc[kb] = T::mma_biased(T::load(krow), qop[0]);
-      } else {
-        sacc[kb] = T::mma(T::load(krow), qop[0], (Acc){});
+  Acc sacc[2];
+  f16x8 pb[2][2];  // P^T operand: [32-key block][16-key half]
+  St pf;
+  ScaleRegs sr;
+  // Uniform scales of the tile whose softmax comes next, read during the
+  // preceding matrix phase (a read at the start of the softmax phase would
+  // queue behind the other group's operand reads).
+  float tile_ks = 0.0f, tile_vref = 0.0f;
+
+  // Matrix phase for tile index t, with K_t in kb and V_{t-1} in vb (PV when
+  // the template flag says so): operand reads, the staging of the registers
+  // fetched two phases ago (K_{t+1} into kst, V_t into vst, scales of tile t+1
+  // into the ring) and the loads of the next tiles, then S(t) = K_t Q^T and
+  // O += P(t-1) V(t-1). Staging and loads happen unconditionally: past the
+  // last tile they rewrite buffers nobody reads again with clamped tiles.
+  auto mphase = [&](int t, const uint8_t* kb, const _Float16* vb, uint8_t* kst, _Float16* vst,
+                    auto with_pv) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(with_pv)::value;
+    // Operand stream: kNR 16-byte LDS reads (K operands, then V operands),
+    // kNM matrix instructions. A ring of kDepth registers keeps kDepth reads
+    // in flight ahead of the instruction that consumes them; the order is
+    // pinned with scheduling fences so that each read has several matrix
+    // instructions' time to arrive.
+    constexpr int kKR = FP8 ? 2 : 1;              // reads per QK instruction
+    constexpr int kNR = kKR * kNK + (PV ? kNV : 0);
+    constexpr int kNM = kNK + (PV ? kNV : 0);
+    constexpr int kDepth = 8;
+    tile_ks = sc.ks[t % kScaleRing][0];
+    tile_vref = sc.vref[t % kScaleRing];
+    const uint8_t* kaddr = kb + col * G::kKStride + half * T::kSlice;
+    const _Float16* vaddr = vb + col * G::kVStride + half * 8;
+    // P.V comes first, so that the probabilities are dead before the new
+    // scores are written (the two can share registers). Read r: V operands
+    // (16-key group-major), then K operands in MFMA order (step-major, the
+    // two 32-key blocks interleaved).
+    constexpr int kNVR = PV ? kNV : 0;
+    auto rd = [&](int r) __attribute__((always_inline)) -> i32x4 {
+      if (r < kNVR) {
+        const int g = r / kDB, db = r % kDB;
+        return *(const i32x4*)(vaddr + db * 32 * G::kVStride + g * 16);
       }
+      const int m = (r - kNVR) / kKR, part = (r - kNVR) % kKR;
+      const int s = m / 2, kb2 = m % 2;
+      return *(const i32x4*)(kaddr + kb2 * 32 * G::kKStride + s * 2 * T::kSlice + part * 16);
+    };
+    i32x4 ring[kDepth];
 #pragma unroll
-      for (int s = 1; s < T::kSteps; ++s)
-        sacc[kb] = T::mma(T::load(krow + s * 2 * T::kSlice), qop[s], sacc[kb]);
+    for (int r = 0; r < kDepth; ++r) ring[r] = rd(r);
+    __builtin_amdgcn_sched_barrier(0);
+    // Reads consumed by instructions 0..m.
+    auto consumed = [](int m) constexpr { return m < kNVR ? m + 1 : kNVR + (m + 1 - kNVR) * kKR; };
+#pragma unroll
+    for (int m = 0; m < kNM; ++m) {
+      const int r0 = m < kNVR ? m : kNVR + (m - kNVR) * kKR;  // first read of this instruction
+      if (m < kNVR) {
+        if constexpr (PV) {
+          const int g = m / kDB, db = m % kDB;
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ring[r0 % kDepth]),
+                                                         pb[g >> 1][g & 1], o[db], 0, 0, 0);
+        }
+      } else {
+        const int s = (m - kNVR) / 2, kb2 = (m - kNVR) % 2;
+        Op a;
+        if constexpr (FP8) {
+          const i32x4 lo = ring[r0 % kDepth], hi = ring[(r0 + 1) % kDepth];
+          a = (Op){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          a = ring[r0 % kDepth];
+        }
+        if (s == 0) {
+          if constexpr (kBiasAcc) sacc[kb2] = T::mma(a, qop[0], bias_acc);
+          else sacc[kb2] = T::mma(a, qop[0], (Acc){});
+        } else {
+          sacc[kb2] = T::mma(a, qop[s], sacc[kb2]);
+        }
+      }
+      // Refill the slots this instruction freed.
+      const int from = min(kNR, kDepth + (m ? consumed(m - 1) : 0));
+      const int to = min(kNR, kDepth + consumed(m));
+#pragma unroll
+      for (int r = from; r < to; ++r) ring[r % kDepth] = rd(r);
+      if (m + 4 < kNM) __builtin_amdgcn_sched_barrier(0);
     }
+    // Staging of the next tiles and their loads; the compiler may interleave
+    // this vector work with the last matrix instructions.
+    stage_k<D, KQT, VQT>(kst, pf);
+    stage_v<D, KQT, VQT>(vst, pf);
+    if (wave == 0) stage_scales<TOK>(sc, (t + 1) % kScaleRing, sr, p.kv_scale_f16, vref_run);
+    fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, tile_n0(t + 2), tile_n0(t + 1));
+    if (wave == 0) fetch_scales(sr, p, sbase, tile_n0(t + 2), TOK);
   };
 
-  // One-scale-per-tile softmax in two parts. tile_max converts the scores of
-  // a tile, takes their max and applies the lazy O rescale (a rare, uniform
-  // branch); tile_exp forms the fp16 probabilities in the B-operand layout of
-  // P.V and their row sums. Returns the score multiplier of the tile.
-  auto tile_max = [&](const Acc* sacc, const VStage<D>& vs, float (&x)[2][16], auto mask_c,
-                      bool rt_mask, int lim) -> float {
-    const bool need_mask = decltype(mask_c)::value || rt_mask;
-    const float ck = cq * vs.ksc[0];
-    const float sv_t = vs.vsc[0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = sacc[kb][r];
-        x[kb][r] = kBiasAcc ? __int_as_float(v) : (float)v;
-      }
-    // Tile max as four independent chains (short dependency depth).
-    float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (need_mask) {
+  // Softmax of the scores of tile t (in sacc) into pb and the running
+  // statistics; mask_c: compile-time switch for tiles that need the mask
+  // (a wavefront whose rows all lie above the tile masks every key).
+  auto softmax = [&](int t, auto mask_c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const int slot = t % kScaleRing;
+    const int lim = lim_base - t * kBN;  // masked iff key_of(kb, r) > lim
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
+    if constexpr (!TOK) {
+      // A zero Q or K scale makes every score of the row 0; the floor keeps
+      // -inf (masked) times the factor from giving NaN and changes no
+      // probability at fp32 precision.
+      const float ck = fmaxf(cq * tile_ks, 1e-30f);
+      const float sv_t = tile_vref;
+      float x[2][16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          mc[r & 3] = fmaxf(mc[r & 3], key_of(kb, r) > lim ? -INFINITY : x[kb][r]);
-    } else {
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (kBiasAcc) x[kb][r] = __int_as_float(sacc[kb][r]);
+          else x[kb][r] = sacc[kb][r];
+          // Causal: masked keys are real keys and must not raise the max.
+          if constexpr (MASK && CAUSAL) x[kb][r] = key_of(kb, r) > lim ? -INFINITY : x[kb][r];
+        }
+      float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mc[r & 3] = fmaxf(mc[r & 3], x[kb][r]);
-    }
-    const float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
-    // Max of this lane half; the row max over both halves is only formed when
-    // some row needs a rescale (or the V scale changes), which is rare.
-    // (x - kBiasInt * 2^-26) * 2^26 is the integer dot product, exactly.
-    const float mt = mx == -INFINITY ? -INFINITY
-                     : kBiasAcc ? (mx - __int_as_float(kBiasBits)) * (ck * 67108864.0f)
-                                : mx * ck;  // ck >= 0
-    const float sv_eff = sv_t > 0.0f ? sv_t : (sv_cur > 0.0f ? sv_cur : 1.0f);
-    if (__any(mt > m_run + kRescaleSlack) || sv_eff != sv_cur) {
-      const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = mrow > m_run + kRescaleSlack ? fmaxf(m_run, mrow) : m_run;
-      const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      const float f = sv_cur > 0.0f ? alpha * (sv_cur / sv_eff) : 0.0f;
-      l_run *= alpha;
+      const float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+      // Max of this lane half in log2 units; (x - kBiasInt 2^-26) 2^26 is the
+      // integer dot product, exactly.
+      const float mt = mx == -INFINITY ? -INFINITY
+                       : kBiasAcc ? (mx - __int_as_float(kBiasBits)) * (ck * 67108864.0f)
+                                  : mx * ck;
+      // A zero V scale (all-zero V block) keeps O's unit.
+      const bool sv_change = sv_t > 0.0f && sv_t != sv_cur;
+      if (__any(mt > m_run + kSlack) || sv_change) {
+        const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = mrow > m_run + kSlack ? fmaxf(m_run, mrow) : m_run;
+        const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float sv_new = sv_t > 0.0f ? sv_t : (sv_cur > 0.0f ? sv_cur : 1.0f);
+        const float f = sv_cur > 0.0f ? alpha * (sv_cur / sv_new) : 0.0f;
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < kDB; ++i) o[i] *= f;
-      m_run = m_new;
-      sv_cur = sv_eff;
-    }
-    return ck;
-  };
-  auto tile_exp = [&](const float (&x)[2][16], float ck, f16x8 (&pb)[2][2], auto mask_c,
-                      bool rt_mask, int lim) {
-    const bool need_mask = decltype(mask_c)::value || rt_mask;
-    float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
-    if constexpr (kBiasAcc) {
-      // x = (kBiasInt + dot) * 2^-26: scale by ck * 2^26 and fold the offset
-      // into the subtrahend (one rounding, an error below one unit of dot).
-      msub = __builtin_fmaf(-(float)kBiasInt, ck, msub);
-      ck *= 67108864.0f;
-    }
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
+        for (int i = 0; i < kDB; ++i) o[i] *= f;
+        m_run = m_new;
+        sv_cur = sv_new;
+      }
+      float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
+      float c = ck;
+      if constexpr (kBiasAcc) {
+        // x = (kBiasInt + dot) 2^-26: scale by ck 2^26 and fold the offset
+        // into the subtrahend (one rounding, below one unit of dot).
+        msub = __builtin_fmaf(-(float)kBiasInt, ck, msub);
+        c = ck * 67108864.0f;
+      }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float a0 = __builtin_fmaf(x[kb][r], ck, msub);
-        float a1 = __builtin_fmaf(x[kb][r + 1], ck, msub);
-        if (need_mask) {
-          a0 = key_of(kb, r) > lim ? -INFINITY : a0;
-          a1 = key_of(kb, r + 1) > lim ? -INFINITY : a1;
+        for (int r = 0; r < 16; r += 2) {
+          const float a0 = __builtin_fmaf(x[kb][r], c, msub);
+          const float a1 = __builtin_fmaf(x[kb][r + 1], c, msub);
+          f16x2 h2 = {(_Float16)__builtin_amdgcn_exp2f(a0), (_Float16)__builtin_amdgcn_exp2f(a1)};
+          if constexpr (MASK && !CAUSAL) {
+            // Keys past the end were loaded as copies of the last key: they
+            // leave the max unchanged, and their probabilities are dropped.
+            if (key_of(kb, r) > lim) h2[0] = (_Float16)0.0f;
+            if (key_of(kb, r + 1) > lim) h2[1] = (_Float16)0.0f;
+          }
+          ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2(h2, one, ls[(r >> 1) & 3], false);
+          pb[kb][r >> 3][r & 7] = h2[0];
+          pb[kb][r >> 3][(r & 7) + 1] = h2[1];
         }
-        const f16x2 h2 = {(_Float16)__builtin_amdgcn_exp2f(a0),
-                          (_Float16)__builtin_amdgcn_exp2f(a1)};
-        ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2(h2, one, ls[(r >> 1) & 3], false);
-        pb[kb][r >> 3][r & 7] = h2[0];
-        pb[kb][r >> 3][(r & 7) + 1] = h2[1];
-      }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  };
-  // O^T += V_t^T . P_t^T; consecutive matrix instructions update different
-  // output blocks.
-  auto tile_pv = [&](const f16x8 (&pb)[2][2], const VStage<D>& vs) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const _Float16* vrow = vs.vt + (db * 32 + col) * VStage<D>::kStride + half * 8;
-        const f16x8 a = *(const f16x8*)(vrow + g * 16);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[g >> 1][g & 1], o[db], 0, 0, 0);
-      }
-    }
-  };
-
-  // Softmax of tile t and O^T += V_t^T . P_t^T (V and scales from V buffer t % 2).
-  // The mask (causal diagonal or end of the keys) is a compile-time switch
-  // for causal attention, so its many unmasked tiles carry no per-element
-  // compare and select; without causality only a ragged last tile is masked
-  // and a runtime flag (cheaper in registers there) selects it.
-  auto softmax_pv = [&](const Acc* sacc, const VStage<D>& vs, int t, auto mask_c, bool rt_mask) {
-    const int n0 = t * kBN;
-    const bool need_mask = decltype(mask_c)::value || rt_mask;
-    const int lim = lim_base - n0;  // masked iff key_of(kb, r) > lim
-    f16x8 pb[2][2];
-    if constexpr (!TOK) {
-      float x[2][16];
-      const float ck = tile_max(sacc, vs, x, mask_c, rt_mask, lim);
-      tile_exp(x, ck, pb, mask_c, rt_mask, lim);
     } else {
-      // Per-key scales (e.g. INT4 K/V with one scale per token).
+      // Per-key scales: x = dot * cq * sk_j; weight = p * sv_j / sv_ref.
+      const float vr = tile_vref;
+      if (vr != sv_cur && vr > 0.0f) {
+        // sv_ref only grows; O moves to the new unit (rare).
+        const float f = sv_cur > 0.0f ? sv_cur / vr : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kDB; ++i) o[i] *= f;
+        sv_cur = vr;
+      }
       float x[2][16];
       float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 s4 = *(const f32x4*)(vs.ksc + kb * 32 + 8 * rg + 4 * half);
+          const f32x4 s4 = *(const f32x4*)(sc.ks[slot] + kb * 32 + 8 * rg + 4 * half);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * rg + i;
             float xv = (float)sacc[kb][r] * (cq * s4[i]);
-            if (need_mask) xv = key_of(kb, r) > lim ? -INFINITY : xv;
+            if constexpr (MASK) xv = key_of(kb, r) > lim ? -INFINITY : xv;
             x[kb][r] = xv;
             mc[i] = fmaxf(mc[i], xv);
           }
         }
       const float mt = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
-      if (__any(mt > m_run + kRescaleSlackTok)) {
+      if (__any(mt > m_run + kSlack)) {
         const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = mrow > m_run + kRescaleSlackTok ? fmaxf(m_run, mrow) : m_run;
+        const float m_new = mrow > m_run + kSlack ? fmaxf(m_run, mrow) : m_run;
         const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
@@ -573,114 +672,78 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         m_run = m_new;
       }
       const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-      float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float lsf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 v4 = *(const f32x4*)(vs.vsc + kb * 32 + 8 * rg + 4 * half);
+          const f32x4 v4 = *(const f32x4*)(sc.vs[slot] + kb * 32 + 8 * rg + 4 * half);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * rg + i;
             const float pr = __builtin_amdgcn_exp2f(x[kb][r] - msub);
-            ls[i] += pr;
+            lsf[i] += pr;
             pb[kb][r >> 3][r & 7] = (_Float16)(pr * v4[i]);
           }
         }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      ls[0] = (lsf[0] + lsf[1]) + (lsf[2] + lsf[3]);
     }
-    tile_pv(pb, vs);
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  auto vphase = [&](int t) __attribute__((always_inline)) {
+    const int n0 = t * kBN;
+    // The mask is needed only on tiles crossing this wavefront's diagonal
+    // (causal) and on a ragged last tile.
+    const bool m = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
+    if (m) softmax(t, std::true_type());
+    else softmax(t, std::false_type());
   };
 
-  // Pipeline: K runs one tile ahead of V. Step t issues S(t+1) = K_{t+1} Q^T on
-  // the matrix unit, computes the softmax of S(t) on the vector unit meanwhile,
-  // issues P(t) V_t, then writes the prefetched K_{t+2} and V_{t+1} (loaded
-  // during the previous step) to the buffers freed by the last barrier.
-  const int last_tile = ntiles - 1;
-  auto tile_n0 = [&](int t) { return min(t, last_tile) * kBN; };
-  Prefetch pf;
-  fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, 0, 0);
-  store_k<D, KQT>(kst[0], pf);
-  store_v<D, VQT>(vst[0], pf, p.kv_scale_f16);
-  fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, tile_n0(1), tile_n0(1));
-  store_k<D, KQT>(kst[1], pf);
-  fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, tile_n0(2), tile_n0(1));
+  // Prologue: K_0 and the scales of tile 0 staged; V buffer 1 (read as
+  // "V_{-1}" by the first matrix phase, with zero probabilities) cleared;
+  // K_1, V_0 and the scales of tile 1 in registers.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pb[i][0] = pb[i][1] = (f16x8){};
+  fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, 0, 0);
+  if (wave == 0) fetch_scales(sr, p, sbase, 0, TOK);
+  for (int i = tid; i < G::kVElems / 8; i += kThreads) ((uint4*)vbuf1)[i] = make_uint4(0, 0, 0, 0);
+  stage_k<D, KQT, VQT>(kbuf0, pf);
+  if (wave == 0) stage_scales<TOK>(sc, 0, sr, p.kv_scale_f16, vref_run);
+  fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, tile_n0(1), 0);
+  if (wave == 0) fetch_scales(sr, p, sbase, tile_n0(1), TOK);
   __syncthreads();
 
-  Acc sa[2], sb[2];
-  if (wave_active(0)) qk(sa, kst[0]);
-  // One step with one scale per tile. After the max and the rare rescale,
-  // S(t+1), the exponentials of tile t, the staging of the next tiles and
-  // P(t) V(t) form one straight-line block, which leaves the compiler free to
-  // interleave the matrix instructions with the vector work. S(t+1) is also
-  // formed when tile t is the last one (from the clamped tile already staged;
-  // the result is not used), and every wavefront runs every step (a step whose
-  // keys all lie beyond a wavefront's rows is fully masked and adds nothing),
-  // so the loop has no data-dependent paths besides the rescale.
-  auto steady_step = [&](const int t, Acc* scur, Acc* snext, auto par, auto mask_c, bool rt_mask) {
-    constexpr int PAR = decltype(par)::value;  // t % 2
-    const int lim = lim_base - t * kBN;
-    float x[2][16];
-    f16x8 pb[2][2];
-    const float ck = tile_max(scur, vst[PAR], x, mask_c, rt_mask, lim);
-    qk(snext, kst[PAR ^ 1]);
-    tile_exp(x, ck, pb, mask_c, rt_mask, lim);
-    // K_{t+2} into K buffer t % 2 and V_{t+1} into V buffer (t+1) % 2, both
-    // last read in step t-1, while P(t) V(t) runs.
-    store_k<D, KQT>(kst[PAR], pf);
-    store_v<D, VQT>(vst[PAR ^ 1], pf, p.kv_scale_f16);
-    tile_pv(pb, vst[PAR]);
-  };
-  auto step = [&](const int t, Acc* scur, Acc* snext, auto par) {
-    constexpr int PAR = decltype(par)::value;  // t % 2
-    if constexpr (!TOK && !FP8) {
-      const int n0 = t * kBN;
-      // Masked: the causal diagonal, keys past the end, or a wavefront whose
-      // rows all lie above the tile (every key masked, so the tile adds
-      // nothing and the step runs the same instructions as the others).
-      const bool m = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
-      if constexpr (CAUSAL) {
-        if (m) steady_step(t, scur, snext, par, std::true_type(), false);
-        else steady_step(t, scur, snext, par, std::false_type(), false);
+  // Each wavefront walks M_0, V_0, M_1, V_1, ..., V_{T-1}, M_T (M_t: matrix
+  // work of tile t and staging; V_t: softmax of tile t), one element per
+  // phase with a barrier after each; group B runs one phase behind group A,
+  // so on every SIMD one wavefront is in a matrix phase while the other is
+  // in a softmax phase. K_t sits in K buffer t % 2, V_{t-1} in V buffer
+  // (t-1) % 2; M_t stages K_{t+1} and V_t into the other buffers.
+  const int nphase = 2 * ntiles + 2;
+  for (int i = 0; i < nphase; ++i) {
+    const int j = i - grp;  // this wavefront's element
+    if (j >= 0 && j <= 2 * ntiles) {
+      const int tt = j >> 1;
+      if ((j & 1) == 0) {
+        const bool odd = tt & 1;
+        mphase(tt, odd ? kbuf1 : kbuf0, odd ? vbuf0 : vbuf1, odd ? kbuf0 : kbuf1,
+               odd ? vbuf1 : vbuf0, std::true_type());
       } else {
-        steady_step(t, scur, snext, par, std::false_type(), RAGGED && m);
+        vphase(tt);
       }
-    } else {
-      // Per-key scales and FP8 (measured faster this way): wavefronts skip the
-      // tiles beyond their rows, and S(t+1) is a block of its own.
-      if (t + 1 < ntiles && wave_active(t + 1)) qk(snext, kst[PAR ^ 1]);
-      if (wave_active(t)) {
-        const int n0 = t * kBN;
-        const bool m = (n0 + kBN > p.Sk) || (CAUSAL && n0 + kBN - 1 > wrow0);
-        if constexpr (CAUSAL) {
-          if (m) softmax_pv(scur, vst[PAR], t, std::true_type(), false);
-          else softmax_pv(scur, vst[PAR], t, std::false_type(), false);
-        } else {
-          softmax_pv(scur, vst[PAR], t, std::false_type(), RAGGED && m);
-        }
-      }
-      // K_{t+2} into K buffer t % 2 (K_t was last read in step t-1) and
-      // V_{t+1} into V buffer (t+1) % 2 (V_{t-1} was last read in step t-1).
-      store_k<D, KQT>(kst[PAR], pf);
-      store_v<D, VQT>(vst[PAR ^ 1], pf, p.kv_scale_f16);
     }
     __syncthreads();
-    fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, sbase, tile_n0(t + 3), tile_n0(t + 2));
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sa, sb, std::integral_constant<int, 0>());
-    if (t + 1 < ntiles) step(t + 1, sb, sa, std::integral_constant<int, 1>());
   }
 
   // Epilogue: lane holds row qrow, channels 32*db + 8*(r/4) + 4*half + (r%4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = (TOK ? 1.0f : sv_cur) / l_tot;
+  const float inv = sv_cur / l_tot;
+  const long hbase = (long)b * p.o_batch + (long)h * p.o_head;
   if (p.out_dtype != QFA_F32) {
-    // 16-bit output goes through LDS (the V buffers: every wavefront passed
-    // the last step's barrier after its last read of them), one 32-row region
-    // per wavefront, and leaves with 16-byte stores along the rows.
-    constexpr int kOS = D + 8;  // 16-bit elements per staged row
-    uint16_t* so = reinterpret_cast<uint16_t*>(&vst[0]) + wave * 32 * kOS;
+    // 16-bit output goes through LDS, one 32-row region per wavefront, and
+    // leaves with 16-byte stores along the rows.
+    constexpr int kOS = G::kOutStride;
+    uint16_t* so = obuf + wave * 32 * kOS;
 #pragma unroll
     for (int db = 0; db < kDB; ++db) {
 #pragma unroll
@@ -699,8 +762,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
         *(uint2*)(so + col * kOS + d0) = make_uint2(w0, w1);
       }
     }
-    __syncthreads();
-    const long hbase = (long)b * p.o_batch + (long)h * p.o_head;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     constexpr int kCPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
     for (int q = lane; q < 32 * kCPR; q += 64) {
@@ -712,40 +776,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdParams p) {
     return;
   }
   if (!qvalid) return;
-  const long obase = (long)b * p.o_batch + (long)h * p.o_head + (long)qrow * p.o_row;
+  const long obase = hbase + (long)qrow * p.o_row;
 #pragma unroll
   for (int db = 0; db < kDB; ++db) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
       const int d0 = db * 32 + 8 * rg + 4 * half;
-      const float v0 = o[db][4 * rg] * inv, v1 = o[db][4 * rg + 1] * inv;
-      const float v2 = o[db][4 * rg + 2] * inv, v3 = o[db][4 * rg + 3] * inv;
-      if (p.out_dtype == QFA_F32) {
-        *(f32x4*)((float*)p.out + obase + d0) = (f32x4){v0, v1, v2, v3};
-      } else if (p.out_dtype == QFA_F16) {
-        *(f16x4*)((_Float16*)p.out + obase + d0) =
-            (f16x4){(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
-      } else {
-        const uint32_t w0 = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
-        *(uint2*)((uint16_t*)p.out + obase + d0) = make_uint2(w0, w1);
-      }
+      *(f32x4*)((float*)p.out + obase + d0) =
+          (f32x4){o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv, o[db][4 * rg + 2] * inv,
+                  o[db][4 * rg + 3] * inv};
     }
   }
 }
 
 template <int D, int KVM>
 hipError_t launch_kv(const FwdParams& p, int grid, bool causal, bool tok, hipStream_t st) {
-  const bool ragged = (p.Sk % kBN) != 0;
   if (causal) {
-    if (tok) fwd_kernel<D, KVM, true, true, false><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, KVM, true, false, false><<<grid, kThreads, 0, st>>>(p);
-  } else if (ragged) {
-    if (tok) fwd_kernel<D, KVM, false, true, true><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, KVM, false, false, true><<<grid, kThreads, 0, st>>>(p);
+    if (tok) fwd_kernel<D, KVM, true, true><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, true, false><<<grid, kThreads, 0, st>>>(p);
   } else {
-    if (tok) fwd_kernel<D, KVM, false, true, false><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, KVM, false, false, false><<<grid, kThreads, 0, st>>>(p);
+    if (tok) fwd_kernel<D, KVM, false, true><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, false, false><<<grid, kThreads, 0, st>>>(p);
   }
   return hipGetLastError();
 }
@@ -778,6 +829,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.Sq = a.Sq;
   p.Sk = a.Sk;
   p.group = a.Hq / a.Hkv;
+  // Heads per workgroup: the largest power of two <= 8 that divides the group.
+  p.hpw = 1;
+  while (p.hpw < 8 && p.group % (2 * p.hpw) == 0) p.hpw *= 2;
+  p.rph = kPairs / p.hpw;
+  p.n_hg = p.group / p.hpw;
+  p.n_rb = (a.Sq + p.rph - 1) / p.rph;
   const long kD = a.k_qtype == QFA_INT4 ? a.D / 2 : a.D;
   const long vD = a.v_qtype == QFA_INT4 ? a.D / 2 : a.D;
   if (a.layout == QFA_BNSD) {
@@ -801,13 +858,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.nkblk = (a.Sk + a.kv_block - 1) / a.kv_block;
   p.q_scale_f16 = a.q_scale_dtype == QFA_F16;
   p.kv_scale_f16 = a.kv_scale_dtype == QFA_F16;
-  p.k_qtype = a.k_qtype;
-  p.v_qtype = a.v_qtype;
   p.out_dtype = a.out_dtype;
   p.scale_log2 = a.softmax_scale * kLog2e;
-  p.n_mblocks = (a.Sq + kBM - 1) / kBM;
   p.xcd_order = ((long)a.B * a.Hkv) % kXcds == 0;
-  const long grid = (long)p.n_mblocks * a.B * a.Hq;
+  const long grid = (long)p.n_rb * a.B * a.Hkv * p.n_hg;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   // Per-key scales unless every tile lies inside one scale block.
   const bool tok = (a.kv_block % kBN) != 0;

@@ -42,16 +42,17 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
-// Load a scale stored as fp32 or fp16: one dword load (for fp16, the aligned
-// dword that holds it) and a select, no branch. A branch around the load
-// makes the compiler wait for it, and for every load issued before it, at
-// the merge point.
+// Load a scale stored as fp32 or fp16 without reading past its own bytes:
+// two 16-bit loads (for fp16 both read the scale itself; for fp32 they read
+// its low and high halves) and a select, no branch. A branch around a load
+// makes the compiler wait for it, and for every load issued before it, at the
+// merge point.
 __device__ __forceinline__ float load_scale(const void* p, long idx, bool f16) {
-  const long off = f16 ? idx * 2 : idx * 4;
-  const int mis = f16 ? (int)(((uintptr_t)p + (uintptr_t)off) & 2u) : 0;
-  const uint32_t w = *(const uint32_t*)((const char*)p + (off - mis));
-  const float h = f16_bits_to_f32((w >> (8 * mis)) & 0xFFFFu);
-  return f16 ? h : __uint_as_float(w);
+  const uint16_t* h = (const uint16_t*)p;
+  const long i0 = f16 ? idx : 2 * idx;
+  const long i1 = f16 ? idx : 2 * idx + 1;
+  const uint32_t lo = h[i0], hi = h[i1];
+  return f16 ? f16_bits_to_f32(lo) : __uint_as_float(lo | (hi << 16));
 }
 
 }  // namespace qfa
