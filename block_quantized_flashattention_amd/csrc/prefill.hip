@@ -110,9 +110,10 @@ struct Geo {
   static constexpr int kOutStride = D + 8;
 };
 struct ScaleRing {
-  float ks[kScaleRing][kBN];
-  float vs[kScaleRing][kBN];
-  float vref[kScaleRing];
+  float ks[kScaleRing][kBN];   // per key: K scale (times 2^26 for biased INT8 scores)
+  float kb[kScaleRing][kBN];   // per key: offset removing the INT8 score bias
+  float vs[kScaleRing][kBN];   // per key: V scale / running maximum V scale
+  float vref[kScaleRing];      // the V scale O is expressed in
 };
 
 // Position of key `key` (0..kBN-1) inside a staged V^T row: groups of 4 keys
@@ -234,13 +235,24 @@ __device__ __forceinline__ void stage_k(uint8_t* kbuf, const Stage<D, KQT, VQT>&
 
 // V^T: channel c of keys (2kp, 2kp+1) as one fp16 pair (exact for INT8, INT4
 // and e4m3 codes).
+// With per-key scales (vsn != nullptr) each key's values are multiplied by
+// its V scale over the running maximum V scale, vsn[key] <= 1, in fp16.
 template <int D, int KQT, int VQT>
-__device__ __forceinline__ void stage_v(_Float16* vbuf, const Stage<D, KQT, VQT>& f) {
+__device__ __forceinline__ void stage_v(_Float16* vbuf, const Stage<D, KQT, VQT>& f,
+                                        const float* vsn) {
   using S = Stage<D, KQT, VQT>;
   const int tid = threadIdx.x;
   const int kp = tid % 32, cg = tid / 32;
   _Float16* base = vbuf + (cg * S::kVCh) * Geo<D>::kVStride + vt_pos(2 * kp);
-  auto put = [&](int c, f16x2 h) __attribute__((always_inline)) { *(f16x2*)(base + c * Geo<D>::kVStride) = h; };
+  f16x2 vscale = {(_Float16)1.0f, (_Float16)1.0f};
+  if (vsn) {
+    const f32x2 v2 = *(const f32x2*)(vsn + 2 * kp);
+    vscale = (f16x2){(_Float16)v2[0], (_Float16)v2[1]};
+  }
+  auto put = [&](int c, f16x2 h) __attribute__((always_inline)) {
+    if (vsn) h = h * vscale;
+    *(f16x2*)(base + c * Geo<D>::kVStride) = h;
+  };
   if constexpr (VQT == QFA_INT4) {
     // Nibble c of key a (b) sits in byte c/2 of its word(s); gather byte j of
     // both keys, then shift each nibble pair under the exponent.
@@ -311,14 +323,20 @@ __device__ __forceinline__ void fetch_scales(ScaleRegs& r, const FwdParams& p, l
   r.vhi = ((const uint16_t*)p.vs)[i1];
 }
 
-template <bool TOK>
+// With per-key scales each key gets the two constants of its score,
+// y_j = sk_j * dot_j = fma(x_j, a_j, b_j), where x_j is the accumulator read
+// as a float: for biased INT8 scores x = (kBiasInt + dot) 2^-26, so
+// a_j = sk_j 2^26 and b_j = -sk_j kBiasInt (one rounding, below one unit of
+// dot); for FP8 scores a_j = sk_j, b_j = 0.
+template <bool TOK, bool BIAS>
 __device__ __forceinline__ void stage_scales(ScaleRing& sm, int slot, const ScaleRegs& r,
                                              bool f16, float& vref_run) {
   const int lane = threadIdx.x & 63;
   const float ks = f16 ? f16_bits_to_f32(r.klo) : __uint_as_float(r.klo | (r.khi << 16));
   const float vs = f16 ? f16_bits_to_f32(r.vlo) : __uint_as_float(r.vlo | (r.vhi << 16));
-  sm.ks[slot][lane] = ks;
   if constexpr (TOK) {
+    sm.ks[slot][lane] = BIAS ? ks * 67108864.0f : ks;
+    sm.kb[slot][lane] = BIAS ? -ks * 10680707.0f : 0.0f;
     float m = vs;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -326,6 +344,7 @@ __device__ __forceinline__ void stage_scales(ScaleRing& sm, int slot, const Scal
     sm.vs[slot][lane] = vref_run > 0.0f ? vs / vref_run : 0.0f;
     if (lane == 0) sm.vref[slot] = vref_run;
   } else {
+    sm.ks[slot][lane] = ks;
     if (lane == 0) sm.vref[slot] = vs;
   }
 }
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // -2292099 <= dot < 6096509, which any 8-bit codes with D <= 128 satisfy
   // (|dot| <= 128 * 128 * 128). The scores then need no integer-to-float
   // conversion, and their max is a float max.
-  constexpr bool kBiasAcc = !FP8 && !TOK;
+  constexpr bool kBiasAcc = !FP8;
   constexpr uint32_t kBiasBits = 0x3E22F983u;
   constexpr int kBiasInt = 10680707;  // 2^23 + 0x22F983
   static_assert(D <= 128, "biased INT8 scores need |dot| < 2^21");
@@ -554,8 +573,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     // Staging of the next tiles and their loads; the compiler may interleave
     // this vector work with the last matrix instructions.
     stage_k<D, KQT, VQT>(kst, pf);
-    stage_v<D, KQT, VQT>(vst, pf);
-    if (wave == 0) stage_scales<TOK>(sc, (t + 1) % kScaleRing, sr, p.kv_scale_f16, vref_run);
+    stage_v<D, KQT, VQT>(vst, pf, TOK ? sc.vs[t % kScaleRing] : nullptr);
+    if (wave == 0) stage_scales<TOK, kBiasAcc>(sc, (t + 1) % kScaleRing, sr, p.kv_scale_f16, vref_run);
     fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, tile_n0(t + 2), tile_n0(t + 1));
     if (wave == 0) fetch_scales(sr, p, sbase, tile_n0(t + 2), TOK);
   };
@@ -636,32 +655,40 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
           pb[kb][r >> 3][(r & 7) + 1] = h2[1];
         }
     } else {
-      // Per-key scales: x = dot * cq * sk_j; weight = p * sv_j / sv_ref.
+      // Per-key scales: y_j = sk_j dot_j = fma(x_j, a_j, b_j) and the score
+      // in log2 units is cq y_j. The V scales are folded into the staged V
+      // (code * sv_j / sv_ref), so the weights are the probabilities
+      // themselves and O is kept in units of sv_ref, which only grows.
       const float vr = tile_vref;
       if (vr != sv_cur && vr > 0.0f) {
-        // sv_ref only grows; O moves to the new unit (rare).
         const float f = sv_cur > 0.0f ? sv_cur / vr : 0.0f;
 #pragma unroll
         for (int i = 0; i < kDB; ++i) o[i] *= f;
         sv_cur = vr;
       }
-      float x[2][16];
+      // A zero Q scale makes every score of the row 0; the floor keeps -inf
+      // (masked) times it from giving NaN.
+      const float cqe = fmaxf(cq, 1e-30f);
+      float y[2][16];
       float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 s4 = *(const f32x4*)(sc.ks[slot] + kb * 32 + 8 * rg + 4 * half);
+          const f32x4 a4 = *(const f32x4*)(sc.ks[slot] + kb * 32 + 8 * rg + 4 * half);
+          const f32x4 b4 = *(const f32x4*)(sc.kb[slot] + kb * 32 + 8 * rg + 4 * half);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * rg + i;
-            float xv = (float)sacc[kb][r] * (cq * s4[i]);
-            if constexpr (MASK) xv = key_of(kb, r) > lim ? -INFINITY : xv;
-            x[kb][r] = xv;
-            mc[i] = fmaxf(mc[i], xv);
+            const float xv = kBiasAcc ? __int_as_float(sacc[kb][r]) : (float)sacc[kb][r];
+            float yv = __builtin_fmaf(xv, a4[i], b4[i]);
+            if constexpr (MASK && CAUSAL) yv = key_of(kb, r) > lim ? -INFINITY : yv;
+            y[kb][r] = yv;
+            mc[i] = fmaxf(mc[i], yv);
           }
         }
-      const float mt = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+      const float my = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+      const float mt = my * cqe;
       if (__any(mt > m_run + kSlack)) {
         const float mrow = fmaxf(mt, __shfl_xor(mt, 32));
         const float m_new = mrow > m_run + kSlack ? fmaxf(m_run, mrow) : m_run;
@@ -671,22 +698,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < kDB; ++i) o[i] *= alpha;
         m_run = m_new;
       }
-      const float msub = (m_run == -INFINITY) ? 0.0f : m_run;
-      float lsf[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float msub = (m_run == -INFINITY) ? 0.0f : -m_run;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 v4 = *(const f32x4*)(sc.vs[slot] + kb * 32 + 8 * rg + 4 * half);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * rg + i;
-            const float pr = __builtin_amdgcn_exp2f(x[kb][r] - msub);
-            lsf[i] += pr;
-            pb[kb][r >> 3][r & 7] = (_Float16)(pr * v4[i]);
+        for (int r = 0; r < 16; r += 2) {
+          const float a0 = __builtin_fmaf(y[kb][r], cqe, msub);
+          const float a1 = __builtin_fmaf(y[kb][r + 1], cqe, msub);
+          f16x2 h2 = {(_Float16)__builtin_amdgcn_exp2f(a0), (_Float16)__builtin_amdgcn_exp2f(a1)};
+          if constexpr (MASK && !CAUSAL) {
+            if (key_of(kb, r) > lim) h2[0] = (_Float16)0.0f;
+            if (key_of(kb, r + 1) > lim) h2[1] = (_Float16)0.0f;
           }
+          ls[(r >> 1) & 3] = __builtin_amdgcn_fdot2(h2, one, ls[(r >> 1) & 3], false);
+          pb[kb][r >> 3][r & 7] = h2[0];
+          pb[kb][r >> 3][(r & 7) + 1] = h2[1];
         }
-      ls[0] = (lsf[0] + lsf[1]) + (lsf[2] + lsf[3]);
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
@@ -708,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   if (wave == 0) fetch_scales(sr, p, sbase, 0, TOK);
   for (int i = tid; i < G::kVElems / 8; i += kThreads) ((uint4*)vbuf1)[i] = make_uint4(0, 0, 0, 0);
   stage_k<D, KQT, VQT>(kbuf0, pf);
-  if (wave == 0) stage_scales<TOK>(sc, 0, sr, p.kv_scale_f16, vref_run);
+  if (wave == 0) stage_scales<TOK, kBiasAcc>(sc, 0, sr, p.kv_scale_f16, vref_run);
   fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, tile_n0(1), 0);
   if (wave == 0) fetch_scales(sr, p, sbase, tile_n0(1), TOK);
   __syncthreads();

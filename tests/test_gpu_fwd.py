@@ -109,3 +109,29 @@ def test_full_size_sampled_rows(w, heads):
     codes of the listed heads checked byte for byte, output rows sampled
     across the sequence (first, last, block edges, evenly spaced)."""
     prefill_parity(w, heads=heads, rows=_ROWS(w.S))
+
+
+@pytest.mark.parametrize("vscale", [1e4, 1e-4])
+def test_per_token_path_large_and_small_v(vscale):
+    """INT4 K/V with one fp16 scale per token (the GQA workload's path), V
+    scaled by 1e4 and by 1e-4: the fp16 weights and staged values stay in
+    range whatever the V scales' magnitude. The tolerance is stated for
+    unit-variance V, so the error is compared in units of the V scale."""
+    w = wl.scaled(wl.GQA_INT4, name=f"gqa8x2_int4_v{vscale:g}", Hq=8, Hkv=2, S=300)
+    q, k, v = wl.make_prefill_inputs(w)
+    v = (v.float() * vscale).half()
+    say(f"per-token path, V x {vscale:g}: V amax {float(v.float().abs().max()):.3g}")
+    qc, qs = qfa.block_quant(q.cuda(), w.q_block, "int8")
+    kc, ks = qfa.block_quant(k.cuda(), 1, "int4", torch.float16)
+    vc, vs = qfa.block_quant(v.cuda(), 1, "int4", torch.float16)
+    out = qfa.fwd(qc, qs, kc, ks, vc, vs, q_qtype="int8", k_qtype="int4", v_qtype="int4",
+                  q_block=w.q_block, kv_block=1, softmax_scale=w.softmax_scale, causal=True,
+                  out_dtype=torch.float32)
+    rq, rqs = oracle.block_quant(q, w.q_block, "int8")
+    rk, rks = oracle.block_quant(k, 1, "int4", "f16")
+    rv, rvs = oracle.block_quant(v, 1, "int4", "f16")
+    assert np.array_equal(vc.cpu().numpy(), rv) and np.array_equal(vs.cpu().numpy(), rvs)
+    ref = oracle.attention(oracle.dequantize(rq, rqs, w.q_block, "int8"),
+                           oracle.dequantize(rk, rks, 1, "int4"),
+                           oracle.dequantize(rv, rvs, 1, "int4"), w.softmax_scale, causal=True)
+    assert_close(out.double().cpu().numpy() / vscale, ref / vscale, f"V x {vscale:g}")
