@@ -1,13 +1,20 @@
 """Benchmark: block-quantized FlashAttention on one MI355X.
 
-One step = quantize Q, K and V (one qfa_block_quant_multi call) and run the INT8 causal
-attention forward (qfa_fwd) on the LLaMA-2-7B head shape workload
-``int8_causal_h32_s4096`` (B=1, H=32, S=4096, D=128, fp16 inputs with four
-outlier K channels), inputs resident in HBM. ``value`` is the attention's
-algorithmic ops (unmasked pairs, multiply and add counted) per second of the
-whole step. The dominant kernel (the forward) is also timed alone with HIP
-events and reported against the dense INT8 MFMA peak; the decode kernel on the
-``int8_kv_decode_b32_h32`` workload is reported in GB/s against HBM peak.
+One step = quantize Q, K and V (one qfa_block_quant_multi call) and run the
+attention forward (qfa_fwd) on the largest single-GPU workload,
+``gqa64x8_int4kv_causal_s16384``: B=1, 64 query heads over 8 KV heads, S=16384,
+D=128, fp16 inputs (1% of K elements x10), Q in INT8 per 128-row block, K and V
+in packed INT4 with one fp16 scale per token, causal, fp16 output; inputs
+resident in HBM. ``value`` is the attention's algorithmic ops (unmasked pairs,
+multiply and add counted) per second of the whole step. The dominant kernel
+(the forward) is also timed alone with HIP events and reported against the
+dense INT8 MFMA peak (``roofline``).
+
+Sub-objects: the same step on the INT8 causal (``int8_causal_h32_s4096``) and
+FP8 rotated (``fp8_rot_b2_h24_s4608``) workloads, the tiny INT8 workload's
+latency, the quantizer and the fused rotate+quantize (after a 512 MiB cache
+flush and cache-resident), the INT8 and INT4 KV-cache decode (after a flush),
+the KV append, and the mixed INT8 Q/K + INT4 V forward.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -23,8 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # dense INT8 MFMA, MI355X
-PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP8_TFLOPS = 5000.0     # dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 512 << 20      # larger than the 256 MiB last-level cache
 
 
 def log(*a):
@@ -38,74 +46,171 @@ def _events(torch):
 def settle(torch, fn, seconds=0.1):
     """Run ``fn`` untimed for about ``seconds`` of GPU time before the warmup
     steps: the GPU's clocks ramp up over the first tens of milliseconds of
-    sustained work (the first ~25 ms of forwards run up to ~10% slower)."""
+    sustained work."""
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        for _ in range(8):
+        for _ in range(4):
             fn()
         torch.cuda.synchronize()
 
 
-def bench_prefill(torch, qfa, wl, steps, warmup):
-    w = wl.INT8_CAUSAL
+def _sdt(torch, name):
+    return {"f32": torch.float32, "f16": torch.float16}[name]
+
+
+def prepare_step(torch, qfa, wl, w):
+    """Inputs of workload ``w`` on the GPU and the two marshalled calls of one
+    step: quantize Q/K/V (one qfa_block_quant_multi) and the forward."""
     q, k, v = wl.make_prefill_inputs(w, device="cuda")
-    sdt = torch.float32
-    qc, qs = qfa.block_quant(q, w.q_block, w.q_qtype, sdt)
-    kc, ks = qfa.block_quant(k, w.kv_block, w.k_qtype, sdt)
-    vc, vs = qfa.block_quant(v, w.kv_block, w.v_qtype, sdt)
-    out = torch.empty_like(q)
-
-    jobs = [dict(x=q, block_rows=w.q_block, qtype=w.q_qtype, scale_dtype=sdt, codes=qc, scales=qs),
-            dict(x=k, block_rows=w.kv_block, qtype=w.k_qtype, scale_dtype=sdt, codes=kc, scales=ks),
-            dict(x=v, block_rows=w.kv_block, qtype=w.v_qtype, scale_dtype=sdt, codes=vc, scales=vs)]
-
-    # Arguments are marshalled once: each step is then two ctypes calls, so the
-    # host enqueues faster than the GPU runs and the events time the kernels,
-    # not host-side gaps between them.
-    quant, _ = qfa.prepare_block_quant_multi(jobs)
+    jobs = [dict(x=q, block_rows=w.q_block, qtype=w.q_qtype, scale_dtype=_sdt(torch, w.q_scale_dtype)),
+            dict(x=k, block_rows=w.kv_block, qtype=w.k_qtype,
+                 scale_dtype=_sdt(torch, w.kv_scale_dtype)),
+            dict(x=v, block_rows=w.kv_block, qtype=w.v_qtype,
+                 scale_dtype=_sdt(torch, w.kv_scale_dtype))]
+    quant, outs = qfa.prepare_block_quant_multi(jobs)
+    quant()
+    (qc, qs), (kc, ks), (vc, vs) = outs
+    out = torch.empty(q.shape, dtype=wl.torch_dtype(w.out_dtype), device="cuda")
     attn, _ = qfa.prepare_fwd(qc, qs, kc, ks, vc, vs, q_qtype=w.q_qtype, k_qtype=w.k_qtype,
                               v_qtype=w.v_qtype, q_block=w.q_block, kv_block=w.kv_block,
                               softmax_scale=w.softmax_scale, causal=w.causal, out=out)
+    nbytes = sum(t.numel() * t.element_size() for t in (q, k, v, qc, kc, vc, qs, ks, vs))
+    keep = (q, k, v, qc, qs, kc, ks, vc, vs, out)
+    return quant, attn, nbytes, keep
 
+
+def time_step(torch, quant, attn, steps, warmup):
+    """Exactly ``steps`` steps between two synchronizations (wall clock), with
+    HIP events around each call on the stream they run on."""
     def step(ev=None):
         if ev is not None:
-            ev[2].record()
+            ev[0].record()
         quant()
         if ev is not None:
-            ev[0].record()
+            ev[1].record()
         attn()
         if ev is not None:
-            ev[1].record()
+            ev[2].record()
 
     settle(torch, step)
     for _ in range(warmup):
         step()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     torch.cuda.synchronize()
-    evs = [_events(torch) + (torch.cuda.Event(enable_timing=True),) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
-    quant_ms = sum(c.elapsed_time(a) for a, b, c in evs) / steps
+    quant_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    fwd_ms = sum(b.elapsed_time(c) for _, b, c in evs) / steps
+    return wall * 1e3 / steps, fwd_ms, quant_ms
+
+
+def time_calls(torch, fn, n, flush=None):
+    """Median time of ``n`` single calls (HIP events); with ``flush`` a buffer
+    larger than the last-level cache is read (not written, so no write-back
+    lands in the timed call) before each one."""
+    times = []
+    for _ in range(n):
+        if flush is not None:
+            flush.max()
+        torch.cuda.synchronize()
+        a, b = _events(torch)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return sorted(times)[len(times) // 2]
+
+
+def mfma_roofline(ops, ms, peak, traffic=None, kernel=None):
+    achieved = ops / (ms * 1e-3) / 1e12
+    r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    if kernel:
+        r["kernel"] = kernel
+        r["kernel_ms"] = round(ms, 4)
+    return r
+
+
+def hbm_roofline(nbytes, ms, traffic=None):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+def profiled_traffic(profile, source):
+    """HBM bytes per dispatch from a committed rocprofv3 summary, or None when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+        src = open(os.path.join(ROOT, source), "rb").read()
+    except OSError:
+        return None
+    m = re.search(r"sha256 prefix `([0-9a-f]+)`", text)
+    t = re.search(r"traffic_bytes_per_dispatch: (\d+)", text)
+    if not m or not t or hashlib.sha256(src).hexdigest()[:len(m.group(1))] != m.group(1):
+        return None
+    return int(t.group(1))
+
+
+PREFILL_SRC = "block_quantized_flashattention_amd/csrc/prefill.hip"
+QUANT_SRC = "block_quantized_flashattention_amd/csrc/quant.hip"
+DECODE_SRC = "block_quantized_flashattention_amd/csrc/decode.hip"
+
+
+def bench_prefill_step(torch, qfa, wl, w, steps, warmup, peak, flush):
+    """One workload's step (quantize Q/K/V + forward): step wall time, forward
+    and quantizer event times, the quantizer alone after a cache flush."""
+    quant, attn, qbytes, keep = prepare_step(torch, qfa, wl, w)
+    ms_step, fwd_ms, quant_ms = time_step(torch, quant, attn, steps, warmup)
+    quant_flushed = time_calls(torch, quant, 10, flush)
     ops = w.attention_ops()
-    return w, wall, fwd_ms, quant_ms, ops
+    del keep
+    torch.cuda.empty_cache()
+    prof = f"fwd_{w.name}.md"
+    return {
+        "workload": w.name,
+        "ms_per_step": round(ms_step, 4),
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TOPS",
+        "fwd_ms": round(fwd_ms, 4),
+        "roofline": mfma_roofline(ops, fwd_ms, peak, profiled_traffic(prof, PREFILL_SRC)),
+        "quantize": {"ms": round(quant_ms, 4), "ms_flushed": round(quant_flushed, 4),
+                     "bytes": qbytes,
+                     "roofline": hbm_roofline(qbytes, quant_flushed),
+                     "roofline_cached": hbm_roofline(qbytes, quant_ms)},
+    }
+
+
+def bench_tiny_latency(torch, qfa, wl, steps, warmup):
+    """The tiny INT8 workload (one workgroup): per-call latency of the step and
+    of the forward alone."""
+    w = wl.TINY
+    quant, attn, _, keep = prepare_step(torch, qfa, wl, w)
+
+    def step():
+        quant()
+        attn()
+    for _ in range(warmup + 5):
+        step()
+    n = max(steps, 20)
+    step_ms = time_calls(torch, step, n)
+    fwd_ms = time_calls(torch, attn, n)
+    del keep
+    return {"workload": w.name, "step_latency_us": round(step_ms * 1e3, 2),
+            "fwd_latency_us": round(fwd_ms * 1e3, 2),
+            "note": "one workgroup: launch-bound, correctness and latency only"}
 
 
 def bench_forward(torch, qfa, wl, w, steps, warmup):
     """Forward alone on workload ``w`` (codes quantized once): average kernel
-    time from per-call HIP events over ``steps`` back-to-back calls."""
-    q, k, v = wl.make_prefill_inputs(w, device="cuda")
-    sdt = torch.float32
-    qc, qs = qfa.block_quant(q, w.q_block, w.q_qtype, sdt)
-    kc, ks = qfa.block_quant(k, w.kv_block, w.k_qtype, sdt)
-    vc, vs = qfa.block_quant(v, w.kv_block, w.v_qtype, sdt)
-    out = torch.empty_like(q)
-    del q, k, v
-    attn, _ = qfa.prepare_fwd(qc, qs, kc, ks, vc, vs, q_qtype=w.q_qtype, k_qtype=w.k_qtype,
-                              v_qtype=w.v_qtype, q_block=w.q_block, kv_block=w.kv_block,
-                              softmax_scale=w.softmax_scale, causal=w.causal, out=out)
+    time from per-call HIP events over back-to-back calls."""
+    quant, attn, _, keep = prepare_step(torch, qfa, wl, w)
     settle(torch, attn)
     for _ in range(warmup):
         attn()
@@ -116,14 +221,16 @@ def bench_forward(torch, qfa, wl, w, steps, warmup):
         attn()
         b.record()
     torch.cuda.synchronize()
+    del keep
     return sum(a.elapsed_time(b) for a, b in evs) / steps
 
 
-def bench_rotate_quant(torch, qfa, wl, steps, warmup):
+def bench_rotate_quant(torch, qfa, wl, steps, warmup, flush):
     """Fused rotation + FP8 block quantization of Q (128-row blocks) and K
-    (256-row blocks) of the FP8 workload's shape: average time of the pair
-    from per-call HIP events, and the algorithmic bytes (bf16 read once, e4m3
-    codes and fp32 scales written once)."""
+    (256-row blocks) of the FP8 workload's shape: the pair's time, cache
+    resident (average of back-to-back pairs) and after a flush (median), and
+    the algorithmic bytes (bf16 read once, e4m3 codes and fp32 scales written
+    once)."""
     w = wl.FP8_ROT
     gen = torch.Generator(device="cuda").manual_seed(w.seed)
     q = torch.randn(w.B, w.Hq, w.S, w.D, generator=gen, device="cuda").to(torch.bfloat16)
@@ -146,9 +253,12 @@ def bench_rotate_quant(torch, qfa, wl, steps, warmup):
         b.record()
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    ms_flushed = time_calls(torch, pair, 10, flush)
     nq, nk = q.numel(), k.numel()
     nbytes = 3 * (nq + nk) + 4 * (w.B * w.Hq * -(-w.S // w.q_block) + w.B * w.Hkv * -(-w.S // w.kv_block))
-    return w, ms, nbytes
+    return {"workload": w.name, "ms": round(ms, 4), "ms_flushed": round(ms_flushed, 4),
+            "bytes": nbytes, "roofline": hbm_roofline(nbytes, ms_flushed),
+            "roofline_cached": hbm_roofline(nbytes, ms)}
 
 
 def bench_kv_append(torch, qfa, wl, steps, warmup):
@@ -183,10 +293,12 @@ def bench_kv_append(torch, qfa, wl, steps, warmup):
         pair()
         b.record()
     torch.cuda.synchronize()
-    return w, sum(a.elapsed_time(b) for a, b in evs) / steps
+    return {"workload": w.name, "ms": round(sum(a.elapsed_time(b) for a, b in evs) / steps, 4),
+            "note": "latency of one decode step's K and V row appends (two launches); "
+                    "no roofline: a few KB per call"}
 
 
-def bench_decode(torch, qfa, wl, w, steps, warmup):
+def bench_decode(torch, qfa, wl, w, steps, warmup, flush, prof):
     q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
     sdt = torch.float16
     kc, ks = qfa.block_quant(k, w.kv_block, w.kv_qtype, sdt)
@@ -195,55 +307,24 @@ def bench_decode(torch, qfa, wl, w, steps, warmup):
     out = torch.empty_like(q)
     ws = torch.empty(qfa.decode_workspace_bytes(w.B, w.Hq, w.S_max, w.D), dtype=torch.uint8,
                      device="cuda")
-    # A buffer larger than the 256 MiB last-level cache, read (not written)
-    # between timed calls: the cache then holds clean lines of this buffer, so
-    # the KV cache comes from HBM and no write-back of the flush itself lands
-    # inside the timed region.
-    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-
     call, _ = qfa.prepare_decode(q, kc, vc, ks, vs, lens, kv_qtype=w.kv_qtype,
                                  kv_block=w.kv_block, softmax_scale=w.softmax_scale, out=out,
                                  workspace=ws)
-
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        flush.max()
-        torch.cuda.synchronize()
-        a, b = _events(torch)
-        a.record()
-        call()
-        b.record()
-        b.synchronize()
-        times.append(a.elapsed_time(b))
-    ms = sorted(times)[len(times) // 2]
+    ms = time_calls(torch, call, max(steps, 10), flush)
     nbytes = wl.decode_kv_bytes(w, lens.cpu().tolist())
-    return w, ms, nbytes
-
-
-def profiled_traffic(profile, source):
-    """HBM bytes per dispatch from a committed rocprofv3 summary, or None when
-    the kernel source has changed since the counters were taken."""
-    import hashlib
-    import re
-    try:
-        text = open(os.path.join(ROOT, "profiles", profile)).read()
-        src = open(os.path.join(ROOT, source), "rb").read()
-    except OSError:
-        return None
-    m = re.search(r"sha256 prefix `([0-9a-f]+)`", text)
-    t = re.search(r"traffic_bytes_per_dispatch: (\d+)", text)
-    if not m or not t or hashlib.sha256(src).hexdigest()[:len(m.group(1))] != m.group(1):
-        return None
-    return int(t.group(1))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
+            "bytes": nbytes,
+            "roofline": hbm_roofline(nbytes, ms, profiled_traffic(prof, DECODE_SRC))}
 
 
 def cpu_baseline(wl, target_s=10.0):
-    """The oracle (quantize + float64 attention) on whole heads of the bench
-    workload, cycling over the heads until about ``target_s`` seconds have
-    passed; ops/s in TOPS."""
+    """The oracle (quantize + float64 causal attention) on blocks of 512 query
+    rows of the headline workload, cycling over heads and row blocks until
+    about ``target_s`` seconds have passed; ops/s in TOPS (the algorithmic ops
+    of exactly the rows computed)."""
     import numpy as np
     import oracle
     try:
@@ -251,27 +332,38 @@ def cpu_baseline(wl, target_s=10.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
     except Exception:
         cores = os.cpu_count()
-    w = wl.INT8_CAUSAL
+    w = wl.GQA_INT4
     q, k, v = wl.make_prefill_inputs(w)
-    done_heads, ops, t0 = 0, 0, time.perf_counter()
+    group = w.Hq // w.Hkv
+    rows_per, done, ops, kv_cache = 512, 0, 0, {}
+    t0 = time.perf_counter()
     while True:
-        h = done_heads % w.Hq
-        qc, qs = oracle.block_quant(q[:, h:h + 1], w.q_block, w.q_qtype)
-        kc, ks = oracle.block_quant(k[:, h:h + 1], w.kv_block, w.k_qtype)
-        vc, vs = oracle.block_quant(v[:, h:h + 1], w.kv_block, w.v_qtype)
-        oracle.attention(oracle.dequantize(qc, qs, w.q_block, w.q_qtype),
-                         oracle.dequantize(kc, ks, w.kv_block, w.k_qtype),
-                         oracle.dequantize(vc, vs, w.kv_block, w.v_qtype),
-                         w.softmax_scale, w.causal)
-        done_heads += 1
-        ops += 2 * w.D * w.S * (w.S + 1)
+        h = (done * 7) % w.Hq                      # spread over heads and KV heads
+        r0 = ((done * 13) % (w.S // rows_per)) * rows_per
+        kvh = h // group
+        if kvh not in kv_cache:
+            kc, ks = oracle.block_quant(k[:, kvh:kvh + 1], w.kv_block, w.k_qtype, w.kv_scale_dtype)
+            vc, vs = oracle.block_quant(v[:, kvh:kvh + 1], w.kv_block, w.v_qtype, w.kv_scale_dtype)
+            kv_cache[kvh] = (oracle.dequantize(kc, ks, w.kv_block, w.k_qtype),
+                             oracle.dequantize(vc, vs, w.kv_block, w.v_qtype))
+        kh, vh = kv_cache[kvh]
+        qb = q[:, h:h + 1, r0:r0 + rows_per]
+        qc, qs = oracle.block_quant(qb, w.q_block, w.q_qtype, w.q_scale_dtype)
+        qh = oracle.dequantize(qc, qs, w.q_block, w.q_qtype)
+        rows = np.arange(r0, r0 + rows_per)
+        qfull = np.zeros((1, 1, w.S, w.D))
+        qfull[0, 0, r0:r0 + rows_per] = qh[0, 0]
+        oracle.attention_rows(qfull, kh, vh, w.softmax_scale, True, 0, 0, rows)
+        ops += int(sum(4 * w.D * (i + 1) for i in rows))
+        done += 1
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{done_heads} head passes (cycling over the {w.Hq} heads) of {w.name}: "
-                      f"quantize Q/K/V + float64 causal attention, {dt:.1f} s"}
+            "sample": f"{done} blocks of {rows_per} query rows of {w.name} (spread over heads): "
+                      f"quantize Q block + K/V head (INT4 per token) and float64 causal attention "
+                      f"of those rows, {dt:.1f} s"}
 
 
 def main():
@@ -281,6 +373,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time the headline step only (for profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -293,87 +387,58 @@ def main():
     import block_quantized_flashattention_amd as qfa
     import qfa_workloads as wl
 
-    log(f"prefill: {wl.INT8_CAUSAL.name}, warmup {args.warmup}, steps {args.steps}")
-    w, wall, fwd_ms, quant_ms, ops = bench_prefill(torch, qfa, wl, args.steps, args.warmup)
-    ms_step = wall * 1e3 / args.steps
-    # Algorithmic bytes of the three quantizer calls: fp16 inputs read once,
-    # int8 codes and fp32 scales written once.
-    nel = w.B * w.Hq * w.S * w.D
-    qbytes = 3 * nel * 2 + 3 * nel + 4 * (w.B * w.Hq * (w.S // w.q_block) + 2 * w.B * w.Hkv * (w.S // w.kv_block))
-    value = ops / (ms_step * 1e-3) / 1e12
-    achieved = ops / (fwd_ms * 1e-3) / 1e12
-    log(f"prefill step {ms_step:.3f} ms, forward kernel {fwd_ms:.3f} ms, {achieved:.1f} TOPS, "
-        f"quantize Q/K/V {quant_ms:.3f} ms")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    w = wl.GQA_INT4
+    log(f"headline step: {w.name}, warmup {args.warmup}, steps {args.steps}")
+    head = bench_prefill_step(torch, qfa, wl, w, args.steps, args.warmup, PEAK_INT8_TOPS, flush)
+    log(f"{w.name}: step {head['ms_per_step']:.3f} ms, forward {head['fwd_ms']:.3f} ms "
+        f"({head['roofline']['achieved']:.0f} TOPS), quantize {head['quantize']['ms']:.3f} ms "
+        f"({head['quantize']['ms_flushed']:.3f} ms flushed)")
     rec = {
         "metric": "quantized FA prefill TOPS + decode KV GB/s, % of MI355X MFMA/HBM peak",
-        "value": round(value, 3),
+        "value": head["value"],
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.Hq, "S": w.S, "D": w.D,
-                   "causal": w.causal, "qtype": "int8", "q_block": w.q_block,
-                   "kv_block": w.kv_block, "step": "block_quant_multi(Q,K,V) + fwd"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": profiled_traffic("fwd_int8_causal_h32_s4096.md",
-                                                 "block_quantized_flashattention_amd/csrc/prefill.hip"),
-                     "kernel": "fwd_kernel<128,int8,causal>",
-                     "kernel_ms": round(fwd_ms, 4)},
-        "quantize": {"ms": round(quant_ms, 4), "bytes": qbytes,
-                     "roofline": {"bound": "hbm",
-                                  "achieved": round(qbytes / (quant_ms * 1e-3) / 1e9, 1),
-                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                  "traffic": profiled_traffic(
-                                      "block_quant_qkv_int8_causal_h32_s4096.md",
-                                      "block_quantized_flashattention_amd/csrc/quant.hip")}},
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+                   "causal": w.causal, "q_qtype": w.q_qtype, "kv_qtype": w.k_qtype,
+                   "q_block": w.q_block, "kv_block": w.kv_block,
+                   "step": "block_quant_multi(Q,K,V) + fwd"},
+        "roofline": dict(head["roofline"], kernel="fwd_kernel<128,int4kv,causal,per-token>",
+                         kernel_ms=head["fwd_ms"]),
+        "quantize": head["quantize"],
     }
-    # The same shape with packed INT4 V codes (INT8 Q and K): forward only.
-    mw = wl.INT8QK_INT4V
-    log(f"forward: {mw.name}")
-    mms = bench_forward(torch, qfa, wl, mw, args.steps, args.warmup)
-    mtops = mw.attention_ops() / (mms * 1e-3) / 1e12
-    log(f"forward {mw.name} {mms:.3f} ms, {mtops:.1f} TOPS")
-    rec["fwd_int8qk_int4v"] = {"workload": mw.name, "ms": round(mms, 4),
-                               "roofline": {"bound": "mfma", "achieved": round(mtops, 2),
-                                            "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                                            "frac": round(mtops / PEAK_INT8_TOPS, 4),
-                                            "traffic": None}}
-    rw, rms, rbytes = bench_rotate_quant(torch, qfa, wl, args.steps, args.warmup)
-    rgbs = rbytes / (rms * 1e-3) / 1e9
-    log(f"rotate+quantize Q/K of {rw.name}: {rms:.3f} ms, {rgbs:.0f} GB/s")
-    rec["rotate_quantize"] = {"workload": rw.name, "ms": round(rms, 4), "bytes": rbytes,
-                              "roofline": {"bound": "hbm", "achieved": round(rgbs, 1),
-                                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                           "frac": round(rgbs / PEAK_HBM_GBS, 4),
-                                           "traffic": None}}
-    aw, ams = bench_kv_append(torch, qfa, wl, args.steps, args.warmup)
-    log(f"kv append (K and V of {aw.B} x {aw.Hkv} heads): {ams * 1e3:.1f} us")
-    rec["kv_append"] = {"workload": aw.name, "ms": round(ams, 4),
-                        "note": "latency of one decode step's K and V row appends (two launches); "
-                                "no roofline: a few KB per call"}
-    if not args.no_decode:
-        # INT8 cache, then the same shape with a packed INT4 cache.
-        for key, dwl, prof in (("decode", wl.DECODE, "decode_int8_kv_b32_h32.md"),
-                               ("decode_int4", wl.DECODE_INT4, "decode_int4_kv_b32_h32.md")):
-            log(f"{key}: {dwl.name}")
-            dw, dms, nbytes = bench_decode(torch, qfa, wl, dwl, max(args.steps, 10), args.warmup)
-            gbs = nbytes / (dms * 1e-3) / 1e9
-            log(f"{key} {dms:.3f} ms, {gbs:.0f} GB/s")
-            rec[key] = {"workload": dw.name, "value": round(gbs, 1), "unit": "GB/s",
-                        "ms": round(dms, 4), "bytes": nbytes,
-                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
-                                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                     "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                     "traffic": profiled_traffic(
-                                         prof, "block_quantized_flashattention_amd/csrc/decode.hip")}}
+    if not args.only_headline:
+        for key, pw, peak in (("int8_causal", wl.INT8_CAUSAL, PEAK_INT8_TOPS),
+                              ("fp8_rot", wl.FP8_ROT, PEAK_FP8_TFLOPS)):
+            log(f"step: {pw.name}")
+            r = bench_prefill_step(torch, qfa, wl, pw, args.steps, args.warmup, peak, flush)
+            log(f"{pw.name}: step {r['ms_per_step']:.3f} ms, forward {r['fwd_ms']:.3f} ms "
+                f"({r['roofline']['achieved']:.0f} TOPS)")
+            rec[key] = r
+        rec["tiny"] = bench_tiny_latency(torch, qfa, wl, args.steps, args.warmup)
+        log(f"tiny: step {rec['tiny']['step_latency_us']} us, forward {rec['tiny']['fwd_latency_us']} us")
+        mw = wl.INT8QK_INT4V
+        mms = bench_forward(torch, qfa, wl, mw, args.steps, args.warmup)
+        rec["fwd_int8qk_int4v"] = {"workload": mw.name, "fwd_ms": round(mms, 4),
+                                   "roofline": mfma_roofline(mw.attention_ops(), mms, PEAK_INT8_TOPS)}
+        log(f"forward {mw.name}: {mms:.3f} ms")
+        rec["rotate_quantize"] = bench_rotate_quant(torch, qfa, wl, args.steps, args.warmup, flush)
+        log(f"rotate+quantize: {rec['rotate_quantize']['ms']:.4f} ms cached, "
+            f"{rec['rotate_quantize']['ms_flushed']:.4f} ms flushed")
+        rec["kv_append"] = bench_kv_append(torch, qfa, wl, args.steps, args.warmup)
+        if not args.no_decode:
+            for key, dwl, prof in (("decode", wl.DECODE, "decode_int8_kv_b32_h32.md"),
+                                   ("decode_int4", wl.DECODE_INT4, "decode_int4_kv_b32_h32.md")):
+                rec[key] = bench_decode(torch, qfa, wl, dwl, args.steps, args.warmup, flush, prof)
+                log(f"{key} {rec[key]['ms']:.3f} ms, {rec[key]['value']:.0f} GB/s")
     if args.copy_probe:
         # A plain elementwise copy of known size: reads 1 GiB (fp32), writes 512 MiB (fp16).
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
