@@ -34,12 +34,12 @@ pages fix, hand-computed cases, library routines and closed forms.
 """
 from .quant import (QMAX, bf16_round, block_quant, code_values, dequantize, e4m3fn_decode,
                     e4m3fn_encode, fp16_round, kv_append, pack_int4, quantize_with_scale,
-                    rotate_block_quant, unpack_int4)
+                    rotate16, rotate_block_quant, unpack_int4)
 from .attention import attention, attention_rows, decode
 
 __all__ = [
     "QMAX", "bf16_round", "block_quant", "code_values", "dequantize", "e4m3fn_decode",
     "e4m3fn_encode", "fp16_round", "kv_append", "pack_int4", "quantize_with_scale",
-    "rotate_block_quant", "unpack_int4", "attention",
+    "rotate16", "rotate_block_quant", "unpack_int4", "attention",
     "attention_rows", "decode",
 ]

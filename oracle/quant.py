@@ -31,6 +31,8 @@ the [Ascend-INT8] listing has the same rule).
 """
 from __future__ import annotations
 
+from fractions import Fraction
+
 import numpy as np
 
 QMAX = {"int8": 127.0, "fp8": 448.0, "int4": 7.0}
@@ -196,25 +198,61 @@ def bf16_round(y) -> np.ndarray:
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
+def _round_fraction16(v: Fraction, in_dtype: str) -> float:
+    """Nearest value of ``in_dtype`` ("bf16": 8 significant bits, exponents
+    down to -126; "f16": 11 bits, down to -14, subnormals below) to the exact
+    rational ``v``, ties to even (``round`` of a Fraction rounds half to even)."""
+    if v == 0:
+        return 0.0
+    bits, emin = (8, -126) if in_dtype == "bf16" else (11, -14)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2^e <= a < 2^(e+2)
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - bits + 1)
+    r = float(round(a / quantum) * quantum)
+    return r if v > 0 else -r
+
+
+def rotate16(x, w, in_dtype: str) -> np.ndarray:
+    """``y[..., i] = round16(sum_k x[..., k] * w[i, k])`` as float64: the exact
+    sum of products, rounded once to ``in_dtype`` ("bf16" or "f16"), nearest-even.
+
+    Every product of a 16-bit x and a float32 w is exact in float64, so the
+    float64 matrix product differs from the exact sum by at most
+    ``D * 2^-53 * sum_k |x_k w_ik|`` (the bound for any summation order). Where
+    the 16-bit roundings of the two ends of that interval agree, rounding is
+    monotone, so the exact sum rounds to the same value; elsewhere the sum is
+    recomputed in exact rational arithmetic and rounded from there.
+    """
+    if in_dtype not in ("bf16", "f16"):
+        raise ValueError(f"unknown input dtype {in_dtype!r}")
+    x64 = np.asarray(_to_f32(x), dtype=np.float64)
+    w64 = np.asarray(_to_f32(w), dtype=np.float64)
+    r16 = bf16_round if in_dtype == "bf16" else (lambda t: t.astype(np.float16).astype(np.float64))
+    y = x64 @ w64.T
+    err = 2.0 * x64.shape[-1] * 2.0 ** -53 * (np.abs(x64) @ np.abs(w64).T)  # 2x margin
+    out = r16(y)
+    for idx in np.argwhere(r16(y - err) != r16(y + err)):
+        idx = tuple(idx)
+        xs, ws = x64[idx[:-1]], w64[idx[-1]]
+        exact = sum((Fraction(a) * Fraction(b) for a, b in zip(xs.tolist(), ws.tolist())),
+                    Fraction(0))
+        out[idx] = _round_fraction16(exact, in_dtype)
+    return out
+
+
 def rotate_block_quant(x, w, block_rows: int, qtype: str, in_dtype: str,
                        scale_dtype: str = "f32", layout: str = "bnsd"):
     """Rotate, then block-quantize ([MindIE-SD] FP8 attention: Q and K are
     multiplied by an orthogonal matrix before the dynamic block quantization).
 
-    ``y[..., i] = round16(sum_k x[..., k] * w[i, k])``: the exact product of the
-    16-bit inputs (x and w hold values of ``in_dtype``, "bf16" or "f16"),
-    evaluated in float64, rounded once to ``in_dtype`` (nearest-even); then
-    ``block_quant`` on y. Returns (codes, scales) as ``block_quant`` does.
+    ``y = rotate16(x, w, in_dtype)``: the exact product of the 16-bit inputs
+    rounded once to ``in_dtype``, with x in ``layout``; then ``block_quant`` on
+    y. Returns (codes, scales) as ``block_quant`` does.
     """
-    x64 = np.asarray(_to_f32(x), dtype=np.float64)
-    w64 = np.asarray(_to_f32(w), dtype=np.float64)
-    y = x64 @ w64.T
-    if in_dtype == "bf16":
-        y = bf16_round(y)
-    elif in_dtype == "f16":
-        y = y.astype(np.float16).astype(np.float64)
-    else:
-        raise ValueError(f"unknown input dtype {in_dtype!r}")
+    y = rotate16(x, w, in_dtype)
     return block_quant(y.astype(np.float32), block_rows, qtype, scale_dtype, layout)
 
 

@@ -279,6 +279,80 @@ def test_rotate_rounds_sums_once(dt):
     np.testing.assert_array_equal(s1, s0)
 
 
+def _row_w(D, cols, vals=None):
+    """w whose row 0 sums the listed channels of x (times vals); identity elsewhere."""
+    w = np.eye(D, dtype=np.float32)
+    w[0] = 0.0
+    for j, c in enumerate(cols):
+        w[0, c] = 1.0 if vals is None else vals[j]
+    return w
+
+
+@pytest.mark.parametrize("dt,terms,want", [
+    # 1 + 2^-8 is the midpoint between bf16 1 and 1 + 2^-7; a float64 sum drops
+    # the 2^-70 term and would round the tie to even (1.0). The exact sum lies
+    # above the midpoint and rounds up.
+    ("bf16", [(1.0, 1.0), (2.0 ** -8, 1.0), (2.0 ** -70, 1.0)], 1.0 + 2.0 ** -7),
+    ("bf16", [(1.0, 1.0), (2.0 ** -8, 1.0), (-(2.0 ** -70), 1.0)], 1.0),
+    # the same in fp16 (midpoint 1 + 2^-11); the tiny term is 2^-24 * 2^-40
+    ("f16", [(1.0, 1.0), (2.0 ** -11, 1.0), (2.0 ** -24, 2.0 ** -40)], 1.0 + 2.0 ** -10),
+    # exact ties round to even: 1 + 2^-8 -> 1, (1 + 2^-7) + 2^-8 -> 1 + 2^-6
+    ("bf16", [(1.0, 1.0), (2.0 ** -8, 1.0)], 1.0),
+    ("bf16", [(1.0 + 2.0 ** -7, 1.0), (2.0 ** -8, 1.0)], 1.0 + 2.0 ** -6),
+    ("f16", [(1.0 + 2.0 ** -10, 1.0), (2.0 ** -11, 1.0)], 1.0 + 2.0 ** -9),
+    # f16 subnormal result: 2^-24 + 2^-25 is a tie between 2^-24 and 2^-23
+    ("f16", [(2.0 ** -24, 1.0), (2.0 ** -24, 0.5)], 2.0 ** -23),
+])
+def test_rotate16_rounds_the_exact_sum(dt, terms, want):
+    D = 8
+    x = torch.zeros(1, 1, 1, D, dtype=torch.float32)
+    vals = []
+    for c, (xv, wv) in enumerate(terms):
+        x[0, 0, 0, c] = xv
+        vals.append(wv)
+    x = x.to(torch.bfloat16 if dt == "bf16" else torch.float16)
+    assert [float(x[0, 0, 0, c]) for c in range(len(terms))] == [t[0] for t in terms]
+    w = _row_w(D, range(len(terms)), vals)
+    y = oracle.rotate16(x, w, dt)
+    assert y[0, 0, 0, 0] == want
+    # channels 1.. are the identity rows of w: y equals x there
+    np.testing.assert_array_equal(y[0, 0, 0, 1:], x.double().numpy()[0, 0, 0, 1:])
+
+
+def _neighbours16(v: float, dt):
+    """The two 16-bit values adjacent to the 16-bit value nearest v (by bits)."""
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    c = torch.tensor([v], dtype=torch.float64).to(tdt)
+    bits = c.view(torch.int16)
+    out = [c]
+    for d in (-1, 1):
+        out.append((bits + d).view(tdt))
+    return [float(t) for t in out], [int(t.view(torch.int16)) for t in out]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_rotate16_brute_force(dt):
+    """Tiny random case: every output against the exact rational sum. The
+    result must be the closest of the candidate 16-bit values around it (the
+    even one on a tie)."""
+    from fractions import Fraction
+    x = _rand16((1, 2, 3, 16), dt, 31)
+    rot = np.linalg.qr(np.random.default_rng(7).standard_normal((16, 16)))[0]
+    w = torch.from_numpy(rot).to(torch.bfloat16 if dt == "bf16" else torch.float16)
+    y = oracle.rotate16(x, w, dt)
+    xs, ws = x.double().numpy(), w.double().numpy()
+    for idx in np.ndindex(*y.shape):
+        exact = sum((Fraction(a) * Fraction(b) for a, b in zip(xs[idx[:-1]], ws[idx[-1]])),
+                    Fraction(0))
+        vals, bits = _neighbours16(float(exact), dt)
+        dist = [abs(Fraction(v) - exact) for v in vals]
+        best = min(dist)
+        cands = [(v, b) for v, b, d in zip(vals, bits, dist) if d == best]
+        if len(cands) > 1:  # a tie: the even significand
+            cands = [c for c in cands if c[1] % 2 == 0]
+        assert y[idx] == cands[0][0], (idx, float(exact), y[idx], cands)
+
+
 # ---- quantizing into an existing scale; KV-cache append --------------------
 
 @pytest.mark.parametrize("qtype", ["int8", "int4", "fp8"])
