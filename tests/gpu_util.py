@@ -121,3 +121,59 @@ def prefill_parity(w: wl.PrefillWorkload, layout: str = "bnsd", heads=None, rows
             errs_out.append(got.double().numpy())
     assert_close(np.concatenate(errs_out), np.concatenate(errs_ref), f"{w.name} output")
     return out
+
+
+def prefill_parity_every_head(w: wl.PrefillWorkload, rows_per_head: int = 3):
+    """Every (batch, query head) of a full workload, a few rows each.
+
+    The HIP path quantizes the whole Q, K and V and runs the forward in the
+    launch configuration the benchmark times. The oracle quantizes K and V of
+    every KV head (the GPU's codes and scales must equal them byte for byte)
+    and, per query head, only the Q blocks that hold the sampled rows (blocks
+    are independent, so a block-aligned slice quantizes as in the whole
+    tensor; checked against the GPU's bytes too). The reference rows are the
+    oracle's float64 attention on the oracle's own codes.
+    """
+    say(f"prefill every head {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} S={w.S} "
+        f"{rows_per_head} rows per head")
+    q, k, v = wl.make_prefill_inputs(w)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    qc, qs = qfa.block_quant(qg, w.q_block, w.q_qtype, SDT[w.q_scale_dtype])
+    kc, ks = qfa.block_quant(kg, w.kv_block, w.k_qtype, SDT[w.kv_scale_dtype])
+    vc, vs = qfa.block_quant(vg, w.kv_block, w.v_qtype, SDT[w.kv_scale_dtype])
+    out = qfa.fwd(qc, qs, kc, ks, vc, vs, q_qtype=w.q_qtype, k_qtype=w.k_qtype, v_qtype=w.v_qtype,
+                  q_block=w.q_block, kv_block=w.kv_block, softmax_scale=w.softmax_scale,
+                  causal=w.causal, out_dtype=wl.torch_dtype(w.out_dtype))
+    torch.cuda.synchronize()
+    del qg, kg, vg
+    rk, rks = oracle.block_quant(k, w.kv_block, w.k_qtype, w.kv_scale_dtype)
+    rv, rvs = oracle.block_quant(v, w.kv_block, w.v_qtype, w.kv_scale_dtype)
+    assert_codes_equal(kc, ks, rk, rks, "K codes, every head")
+    assert_codes_equal(vc, vs, rv, rvs, "V codes, every head")
+    kh = oracle.dequantize(rk, rks, w.kv_block, w.k_qtype)
+    vh = oracle.dequantize(rv, rvs, w.kv_block, w.v_qtype)
+    del rk, rv
+    qcn, qsn, outc = qc.cpu().numpy(), qs.cpu().numpy(), out.cpu()
+    group = w.Hq // w.Hkv
+    S, R = w.S, w.q_block
+    got, ref = [], []
+    for b in range(w.B):
+        for h in range(w.Hq):
+            rng = np.random.default_rng(w.seed * 100003 + b * 1009 + h)
+            rows = set(rng.integers(0, S, rows_per_head).tolist())
+            rows.add(S - 1 if h % 2 else int(rng.integers(0, min(S, 2 * R))))
+            rows = np.array(sorted(rows))
+            qhat = np.zeros((1, 1, S, w.D))
+            for blk in sorted({int(r) // R for r in rows}):
+                sl = slice(blk * R, min(S, (blk + 1) * R))
+                bc, bs = oracle.block_quant(q[b:b + 1, h:h + 1, sl], R, w.q_qtype,
+                                            w.q_scale_dtype)
+                assert_codes_equal(torch.from_numpy(np.ascontiguousarray(qcn[b:b + 1, h:h + 1, sl])),
+                                   torch.from_numpy(qsn[b:b + 1, h:h + 1, blk:blk + 1]), bc, bs,
+                                   f"Q block {blk} of head {h}")
+                qhat[0, 0, sl] = oracle.dequantize(bc, bs, R, w.q_qtype)[0, 0]
+            kvh = h // group
+            ref.append(oracle.attention_rows(qhat, kh[b:b + 1, kvh:kvh + 1], vh[b:b + 1, kvh:kvh + 1],
+                                             w.softmax_scale, w.causal, 0, 0, rows))
+            got.append(outc[b, h, rows].double().numpy())
+    assert_close(np.concatenate(got), np.concatenate(ref), f"{w.name} every head")

@@ -8,7 +8,7 @@ import torch
 import block_quantized_flashattention_amd as qfa
 import oracle
 import qfa_workloads as wl
-from gpu_util import assert_close, prefill_parity, say
+from gpu_util import assert_close, prefill_parity, prefill_parity_every_head, say
 
 pytestmark = pytest.mark.gpu
 
@@ -109,6 +109,15 @@ def test_full_size_sampled_rows(w, heads):
     codes of the listed heads checked byte for byte, output rows sampled
     across the sequence (first, last, block edges, evenly spaced)."""
     prefill_parity(w, heads=heads, rows=_ROWS(w.S))
+
+
+@pytest.mark.parametrize("w", [wl.INT8_CAUSAL, wl.FP8_ROT, wl.GQA_INT4, wl.INT8QK_INT4V],
+                         ids=lambda w: w.name)
+def test_full_size_every_head(w):
+    """Every (batch, query head) of the full workloads: a few rows each, one of
+    them the last row or one in the first two Q blocks, against the oracle's
+    attention on the oracle's own codes."""
+    prefill_parity_every_head(w)
 
 
 @pytest.mark.parametrize("vscale", [1e4, 1e-4])

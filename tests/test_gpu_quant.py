@@ -9,7 +9,7 @@ import block_quantized_flashattention_amd as qfa
 import oracle
 import qfa_workloads as wl
 from golden_io import load
-from gpu_util import assert_codes_equal, quantize_both, say
+from gpu_util import SDT, assert_codes_equal, quantize_both, say
 
 pytestmark = pytest.mark.gpu
 
@@ -156,18 +156,29 @@ def test_quant_multi_matches_oracle():
         assert_codes_equal(c, s, rc, rs, f"multi {qt} R={R} {layout}")
 
 
-def test_quant_multi_qkv_full_size():
-    """The Q, K and V of the INT8 causal workload in one call, equal to three
-    single calls byte for byte (those are checked against the oracle above)."""
-    w = wl.INT8_CAUSAL
+@pytest.mark.parametrize("w", [wl.INT8_CAUSAL, wl.GQA_INT4], ids=lambda w: w.name)
+def test_quant_multi_qkv_full_size(w):
+    """Q, K and V of a full workload in one call (the benchmark's quantization
+    step): each output equals the oracle's codes and scales byte for byte
+    (every head of K and V; every head of Q, or every seventh of the largest),
+    and the single-tensor calls give the same bytes."""
     say(f"quant multi full size {w.name}")
-    q, k, v = wl.make_prefill_inputs(w, device="cuda")
-    outs = qfa.block_quant_multi([dict(x=q, block_rows=w.q_block, qtype=w.q_qtype),
-                                  dict(x=k, block_rows=w.kv_block, qtype=w.k_qtype),
-                                  dict(x=v, block_rows=w.kv_block, qtype=w.v_qtype)])
-    for t, R, qt, (c, s) in zip((q, k, v), (w.q_block, w.kv_block, w.kv_block),
-                                (w.q_qtype, w.k_qtype, w.v_qtype), outs):
-        c1, s1 = qfa.block_quant(t, R, qt)
+    q, k, v = wl.make_prefill_inputs(w)
+    qheads = None if w.Hq <= 32 else list(range(0, w.Hq, 7))
+    jobs = [(q, w.q_block, w.q_qtype, w.q_scale_dtype, "Q", qheads),
+            (k, w.kv_block, w.k_qtype, w.kv_scale_dtype, "K", None),
+            (v, w.kv_block, w.v_qtype, w.kv_scale_dtype, "V", None)]
+    outs = qfa.block_quant_multi([dict(x=t.cuda(), block_rows=R, qtype=qt, scale_dtype=SDT[sdt])
+                                  for t, R, qt, sdt, _, _ in jobs])
+    torch.cuda.synchronize()
+    for (t, R, qt, sdt, name, heads), (c, s) in zip(jobs, outs):
+        if heads is None:
+            rc, rs = oracle.block_quant(t, R, qt, sdt, "bnsd")
+            assert_codes_equal(c, s, rc, rs, f"multi full size {name}")
+        else:
+            rc, rs = oracle.block_quant(t[:, heads], R, qt, sdt, "bnsd")
+            assert_codes_equal(c[:, heads], s[:, heads], rc, rs, f"multi full size {name}")
+        c1, s1 = qfa.block_quant(t.cuda(), R, qt, SDT[sdt])
         torch.cuda.synchronize()
         assert torch.equal(c.view(torch.uint8), c1.view(torch.uint8))
         assert torch.equal(s, s1)

@@ -4,9 +4,12 @@ product rounded once to 16 bits) followed by block quantization.
 The GPU sums the 16-bit products in fp32 on the matrix unit. Where the exact
 product lies within the fp32 error bound of a 16-bit rounding midpoint, either
 neighbour is a correct rounding of a correctly computed sum, so those
-elements ("ambiguous") may differ by one code step; a block whose amax such an
-element could change may get the other scale. Everything else is compared
-byte for byte."""
+elements ("ambiguous") may get any code between those of the two ends of
+that interval (one step apart away from zero, several near zero); a block whose amax such an
+element could change may get the other scale. Every block is compared: where the
+GPU took the other scale, the oracle's 16-bit values are re-quantized with the
+GPU's scale (after checking that an ambiguous element explains it) and the
+codes compared as elsewhere; all other elements match byte for byte."""
 import numpy as np
 import pytest
 import torch
@@ -36,6 +39,12 @@ def _inputs(B, N, S, D, dt, layout, seed):
     return x, w
 
 
+def _scale_of(amax, qtype, sdt):
+    """The stored scale the definition gives for a block with this amax."""
+    s = np.float32(np.float32(amax) / np.float32(oracle.QMAX[qtype]))
+    return np.float16(s) if sdt == "f16" else s
+
+
 def _check(x, w, R, qtype, dt, sdt, layout, heads=None):
     say(f"rotate+quant {tuple(x.shape)} {dt} {qtype} R={R} scales={sdt} {layout} heads={heads}")
     gc, gs = qfa.rotate_block_quant(x.cuda(), w.cuda(), R, qtype, SDT[sdt], layout)
@@ -46,7 +55,8 @@ def _check(x, w, R, qtype, dt, sdt, layout, heads=None):
     if heads is not None:
         xb, gcb, gsb = xb[:, heads], gcb[:, heads], gsb[:, heads]
     xb = xb.contiguous()
-    rc, rs = oracle.rotate_block_quant(xb, w, R, qtype, dt, sdt, "bnsd")
+    y16 = oracle.rotate16(xb, w, dt)
+    rc, rs = oracle.block_quant(y16.astype(np.float32), R, qtype, sdt, "bnsd")
     gcb = gcb.contiguous().numpy()
     gsb = gsb.numpy()
     # Ambiguous elements: the 16-bit rounding of the exact sum moved by a bound
@@ -57,38 +67,58 @@ def _check(x, w, R, qtype, dt, sdt, layout, heads=None):
     w64 = w.double().numpy()
     y64 = x64 @ w64.T
     bound = 2.0 ** -18 * (np.abs(x64) @ np.abs(w64).T)
-    amb = _round16(y64 - bound, dt) != _round16(y64 + bound, dt)
+    lo16, hi16 = _round16(y64 - bound, dt), _round16(y64 + bound, dt)
+    amb = lo16 != hi16
     B, N, S, D = x64.shape
     nblk = -(-S // R)
-    bad_blocks = 0
-    ok = np.ones(rc.shape, dtype=bool)
+    other_scale = 0
+    ndiff = 0
     for b in range(B):
         for n in range(N):
             for r in range(nblk):
                 sl = slice(r * R, min(S, (r + 1) * R))
-                same_scale = gsb[b, n, r] == rs[b, n, r]
-                if not same_scale:
-                    # only possible when an ambiguous element can reach the amax
-                    yb = np.abs(_round16(y64[b, n, sl], dt))
-                    alt = np.maximum(np.abs(_round16(y64[b, n, sl] - bound[b, n, sl], dt)),
-                                     np.abs(_round16(y64[b, n, sl] + bound[b, n, sl], dt)))
-                    assert (amb[b, n, sl] & (alt >= yb.max())).any(), (b, n, r, gsb[b, n, r], rs[b, n, r])
-                    bad_blocks += 1
-                    continue
+                yb = y16[b, n, sl]
+                if gsb[b, n, r] == rs[b, n, r]:
+                    ev = oracle.code_values(rc[b, n, sl], qtype)
+                else:
+                    # The GPU's amax must come from an ambiguous element taking
+                    # its other 16-bit rounding. With that scale, every element
+                    # the GPU rounded as the oracle did must get the oracle's
+                    # code for it.
+                    ab = amb[b, n, sl]
+                    alts = np.where(yb[ab] == lo16[b, n, sl][ab], hi16[b, n, sl][ab],
+                                    lo16[b, n, sl][ab])
+                    # the GPU amax is some element's |value| (the oracle's, or
+                    # an ambiguous element's alternative), at least the largest
+                    # non-ambiguous |value|
+                    cands = np.concatenate([np.abs(yb).ravel(), np.abs(alts)])
+                    cands = cands[cands >= np.abs(yb[~ab]).max(initial=0.0)]
+                    assert any(_scale_of(a, qtype, sdt) == gsb[b, n, r] for a in cands), \
+                        (b, n, r, gsb[b, n, r], rs[b, n, r])
+                    other_scale += 1
+                    ev = oracle.code_values(
+                        oracle.quantize_with_scale(yb.astype(np.float32), float(gsb[b, n, r]),
+                                                   qtype), qtype)
                 gv = oracle.code_values(gcb[b, n, sl], qtype)
-                rv = oracle.code_values(rc[b, n, sl], qtype)
-                diff = gv != rv
+                diff = gv != ev
                 if diff.any():
-                    assert amb[b, n, sl][diff].all(), "code differs where the rounding is not ambiguous"
-                    # one code step at most
-                    step = np.maximum(np.abs(rv), np.abs(gv))[diff]
-                    tol = 1.0 if qtype == "int8" else np.maximum(step * 2.0 ** -3, 2.0 ** -9)
-                    assert (np.abs(gv - rv)[diff] <= tol).all()
-                ok[b, n, sl] = ~diff
+                    assert amb[b, n, sl][diff].all(), \
+                        f"code differs where the rounding is not ambiguous at block {(b, n, r)}"
+                    # quantization is monotone: the GPU's code lies between the
+                    # codes of the two ends of the element's rounding interval
+                    sg = float(gsb[b, n, r])
+                    clo = oracle.code_values(oracle.quantize_with_scale(
+                        lo16[b, n, sl][diff].astype(np.float32), sg, qtype), qtype)
+                    chi = oracle.code_values(oracle.quantize_with_scale(
+                        hi16[b, n, sl][diff].astype(np.float32), sg, qtype), qtype)
+                    g = gv[diff]
+                    assert ((np.minimum(clo, chi) <= g) & (g <= np.maximum(clo, chi))).all(), \
+                        ((b, n, r), g[:5], clo[:5], chi[:5])
+                    ndiff += int(diff.sum())
     nblocks = B * N * nblk
-    say(f"  ambiguous elements {int(amb.sum())} of {amb.size}; code differences {int((~ok).sum())}; "
-        f"blocks with the other scale {bad_blocks} of {nblocks}")
-    assert bad_blocks <= max(1, nblocks // 100)
+    say(f"  ambiguous elements {int(amb.sum())} of {amb.size}; code differences {ndiff}; "
+        f"blocks with the other scale {other_scale} of {nblocks} (all blocks compared)")
+    assert other_scale <= max(1, nblocks // 100)
 
 
 @pytest.mark.parametrize("case", [
