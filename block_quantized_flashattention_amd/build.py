@@ -1,4 +1,6 @@
-"""Build libqfa.so (HIP, gfx950) in-tree with hipcc.
+"""Build libqfa.so (HIP, gfx950) in-tree with hipcc, and libqfa_ixcheck.so, a
+host-only library that checks the forward kernel's address arithmetic (the
+same index functions, compiled for the host) for the CPU tests.
 
 Usage: python -m block_quantized_flashattention_amd.build  (or build() from Python).
 """
@@ -13,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqfa.so")
+IXCHECK_LIB = os.path.join(PKG, "libqfa_ixcheck.so")
+IXCHECK_SRC = "index_check.hip"
 
 SOURCES = ["api.hip", "quant.hip", "prefill.hip", "decode.hip"]
 
@@ -34,8 +38,27 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
+def build_ixcheck(verbose: bool = False) -> str:
+    """Compile the host-only index checker into libqfa_ixcheck.so."""
+    tmp = IXCHECK_LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, IXCHECK_SRC),
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    pr = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    lines = [ln for ln in pr.stdout.decode(errors="replace").splitlines()
+             if "packed-fp32-ops" not in ln]
+    if lines and (verbose or pr.returncode):
+        print("\n".join(lines), file=sys.stderr)
+    if pr.returncode:
+        raise RuntimeError(f"hipcc failed for {IXCHECK_SRC}")
+    os.replace(tmp, IXCHECK_LIB)
+    return IXCHECK_LIB
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source into libqfa.so next to this file. Always recompiles."""
+    """Compile every source into libqfa.so next to this file, and the index
+    checker. Always recompiles."""
     objs = []
     procs = []
     objdir = os.path.join(PKG, "_build")
@@ -64,6 +87,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_ixcheck(verbose)
     return LIB
 
 

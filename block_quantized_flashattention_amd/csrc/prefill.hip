@@ -56,6 +56,7 @@
 #include <type_traits>
 
 #include "qfa_device.h"
+#include "qfa_index.h"
 #include "qfa_launch.h"
 
 namespace qfa {
@@ -63,9 +64,8 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPairs = 256;       // (row, head) pairs per workgroup
-constexpr int kBN = 64;           // keys per tile
-constexpr int kXcds = 8;
+constexpr int kPairs = ix::kFwdPairs;  // (row, head) pairs per workgroup
+constexpr int kBN = ix::kFwdBN;        // keys per tile
 constexpr int kScaleRing = 3;     // tiles of scales in flight
 constexpr float kRescaleSlack = 12.0f;
 // With per-key scales the fp16 weight is p * sv_j / sv_ref <= p; the smaller
@@ -167,9 +167,9 @@ template <> struct KVTypes<KV_F8_F8> { static constexpr int K = QFA_FP8_E4M3, V 
 // V; group B the rest, so each group stages half of every tile.
 template <int D, int KQT, int VQT>
 struct Stage {
-  static constexpr int kKSrc = KQT == QFA_INT4 ? D / 16 : D / 8;   // bytes
-  static constexpr int kVCh = D / 16;                              // channels per key
-  static constexpr int kVSrc = VQT == QFA_INT4 ? kVCh / 2 : kVCh;  // bytes per key
+  static constexpr int kKSrc = ix::fwd_k_src(D, KQT == QFA_INT4);  // bytes
+  static constexpr int kVCh = D / 16;                               // channels per key
+  static constexpr int kVSrc = ix::fwd_v_src(D, VQT == QFA_INT4);  // bytes per key
   uint32_t k[kKSrc / 4];
   uint32_t v[2][kVSrc / 4 > 0 ? kVSrc / 4 : 1];
 };
@@ -196,16 +196,12 @@ __device__ __forceinline__ void fetch_tile(Stage<D, KQT, VQT>& f, const FwdParam
                                            int vn0) {
   using S = Stage<D, KQT, VQT>;
   const int tid = threadIdx.x;
-  const int last = p.Sk - 1;
-  {
-    const uint32_t key = (uint32_t)min(kn0 + tid / 8, last);
-    load_words(f.k, kbase + (key * (uint32_t)p.k_row + (uint32_t)(tid % 8) * S::kKSrc));
-  }
-  const int kp = tid % 32, cg = tid / 32;
+  load_words(f.k, kbase + ix::fwd_k_offset(ix::fwd_k_key(kn0, tid, p.Sk), (uint32_t)p.k_row, tid,
+                                            S::kKSrc));
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const uint32_t key = (uint32_t)min(vn0 + 2 * kp + r, last);
-    const uint8_t* src = vbase + (key * (uint32_t)p.v_row + (uint32_t)cg * S::kVSrc);
+    const uint8_t* src = vbase + ix::fwd_v_offset(ix::fwd_v_key(vn0, tid, r, p.Sk),
+                                                  (uint32_t)p.v_row, tid, S::kVSrc);
     if constexpr (S::kVSrc >= 4) {
       load_words(f.v[r], src);
     } else {
@@ -313,10 +309,10 @@ struct ScaleRegs {
 
 __device__ __forceinline__ void fetch_scales(ScaleRegs& r, const FwdParams& p, long sbase, int n0,
                                              bool tok) {
-  const int key = min(n0 + (int)(threadIdx.x & 63), p.Sk - 1);
-  const long g = sbase + (tok ? (p.kv_block == 1 ? key : key / p.kv_block) : n0 / p.kv_block);
+  const long g = ix::fwd_kv_scale_block(sbase, n0, (int)(threadIdx.x & 63), p.Sk, p.kv_block, tok);
   // Two 16-bit loads per scale, neither past the scale's own bytes.
-  const long i0 = p.kv_scale_f16 ? g : 2 * g, i1 = p.kv_scale_f16 ? g : 2 * g + 1;
+  long i0, i1;
+  ix::scale_halves(g, p.kv_scale_f16, i0, i1);
   r.klo = ((const uint16_t*)p.ks)[i0];
   r.khi = ((const uint16_t*)p.ks)[i1];
   r.vlo = ((const uint16_t*)p.vs)[i0];
@@ -418,46 +414,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   const int col = lane & 31;   // query row of this lane within the wavefront
 
   // Work item: (batch, KV head, head group, row block).
-  int rb, b, kvh, hg;
-  {
-    const int id = blockIdx.x;
-    const int ngroups = p.B * p.Hkv;
-    int rank, gidx;
-    if (p.xcd_order) {
-      const int xcd = id % kXcds, k = id / kXcds;
-      const int per_rank = (ngroups / kXcds) * p.n_hg;
-      rank = k / per_rank;
-      const int rem = k % per_rank;
-      gidx = (rem / p.n_hg) * kXcds + xcd;
-      hg = rem % p.n_hg;
-    } else {
-      const int per_rank = ngroups * p.n_hg;
-      rank = id / per_rank;
-      const int rem = id % per_rank;
-      gidx = rem / p.n_hg;
-      hg = rem % p.n_hg;
-    }
-    rb = CAUSAL ? p.n_rb - 1 - rank : rank;
-    b = gidx / p.Hkv;
-    kvh = gidx % p.Hkv;
-  }
-  const int h = kvh * p.group + hg * p.hpw + wave % p.hpw;
-  const int m0 = rb * p.rph;
-  const int wrow0 = m0 + 32 * (wave / p.hpw);
-  const int qrow = wrow0 + col;
+  const ix::FwdItem it = ix::fwd_item(blockIdx.x, p.B, p.Hkv, p.n_hg, p.n_rb, p.xcd_order, CAUSAL);
+  const int b = it.b, kvh = it.kvh;
+  const int h = ix::fwd_head(it, p.group, p.hpw, wave);
+  const int m0 = it.rb * p.rph;
+  const int qrow = ix::fwd_row(it, p.rph, p.hpw, wave, lane);
+  const int wrow0 = qrow - col;
   const bool qvalid = qrow < p.Sq;
 
   // Q slice of this lane (B operand of S^T = K . Q^T), kept in registers.
   Op qop[T::kSteps];
   {
-    const uint8_t* qp = p.q + (long)b * p.q_batch + (long)h * p.q_head + (long)min(qrow, p.Sq - 1) * p.q_row;
+    const uint8_t* qp = p.q + (long)b * p.q_batch + (long)h * p.q_head + (long)ix::fwd_read_row(qrow, p.Sq) * p.q_row;
 #pragma unroll
     for (int s = 0; s < T::kSteps; ++s) {
       qop[s] = T::load(qp + s * 2 * T::kSlice + half * T::kSlice);
       if (!qvalid) qop[s] = (Op){};
     }
   }
-  const float sq = load_scale(p.qs, ((long)b * p.Hq + h) * p.nqblk + min(qrow, p.Sq - 1) / p.q_block,
+  const float sq = load_scale(p.qs, ((long)b * p.Hq + h) * p.nqblk + ix::fwd_read_row(qrow, p.Sq) / p.q_block,
                               p.q_scale_f16);
   const float cq = qvalid ? sq * p.scale_log2 : 0.0f;
 
@@ -480,12 +455,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   float sv_cur = 0.0f;      // V scale O is expressed in
   float vref_run = 0.0f;    // (wavefront 0, per-key scales) running max V scale
 
-  const int n_end = CAUSAL ? min(p.Sk, m0 + p.rph) : p.Sk;
-  const int ntiles = (n_end + kBN - 1) / kBN;
+  const int n_end = ix::fwd_key_end(CAUSAL, p.Sk, m0, p.rph);
+  const int ntiles = ix::fwd_tiles(n_end);
   const int last_tile = ntiles - 1;
   // Keys beyond this offset from the tile start are masked for this lane.
   const int lim_base = (CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1) - 4 * half;
-  auto tile_n0 = [&](int t) __attribute__((always_inline)) { return min(t, last_tile) * kBN; };
+  auto tile_n0 = [&](int t) __attribute__((always_inline)) { return ix::fwd_tile_n0(t, last_tile); };
 
   Acc sacc[2];
   f16x8 pb[2][2];  // P^T operand: [32-key block][16-key half]
@@ -855,43 +830,31 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.Sq = a.Sq;
   p.Sk = a.Sk;
-  p.group = a.Hq / a.Hkv;
-  // Heads per workgroup: the largest power of two <= 8 that divides the group.
-  p.hpw = 1;
-  while (p.hpw < 8 && p.group % (2 * p.hpw) == 0) p.hpw *= 2;
-  p.rph = kPairs / p.hpw;
-  p.n_hg = p.group / p.hpw;
-  p.n_rb = (a.Sq + p.rph - 1) / p.rph;
-  const long kD = a.k_qtype == QFA_INT4 ? a.D / 2 : a.D;
-  const long vD = a.v_qtype == QFA_INT4 ? a.D / 2 : a.D;
-  if (a.layout == QFA_BNSD) {
-    p.q_row = a.D; p.q_head = (long)a.Sq * a.D;
-    p.k_row = kD; p.k_head = (long)a.Sk * kD;
-    p.v_row = vD; p.v_head = (long)a.Sk * vD;
-    p.o_row = a.D; p.o_head = (long)a.Sq * a.D;
-  } else {
-    p.q_row = (long)a.Hq * a.D; p.q_head = a.D;
-    p.k_row = (long)a.Hkv * kD; p.k_head = kD;
-    p.v_row = (long)a.Hkv * vD; p.v_head = vD;
-    p.o_row = (long)a.Hq * a.D; p.o_head = a.D;
-  }
-  p.q_batch = (long)a.Hq * a.Sq * a.D;
-  p.k_batch = (long)a.Hkv * a.Sk * kD;
-  p.v_batch = (long)a.Hkv * a.Sk * vD;
-  p.o_batch = (long)a.Hq * a.Sq * a.D;
+  const ix::FwdShape f = ix::fwd_shape(a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.D, a.layout == QFA_BSND,
+                                        a.k_qtype == QFA_INT4, a.v_qtype == QFA_INT4, a.q_block,
+                                        a.kv_block);
+  p.group = f.group;
+  p.hpw = f.hpw;
+  p.rph = f.rph;
+  p.n_hg = f.n_hg;
+  p.n_rb = f.n_rb;
+  p.q_row = f.q.row; p.q_head = f.q.head; p.q_batch = f.q.batch;
+  p.k_row = f.k.row; p.k_head = f.k.head; p.k_batch = f.k.batch;
+  p.v_row = f.v.row; p.v_head = f.v.head; p.v_batch = f.v.batch;
+  p.o_row = f.q.row; p.o_head = f.q.head; p.o_batch = f.q.batch;  // out: Q's shape, D per row
   p.q_block = a.q_block;
   p.kv_block = a.kv_block;
-  p.nqblk = (a.Sq + a.q_block - 1) / a.q_block;
-  p.nkblk = (a.Sk + a.kv_block - 1) / a.kv_block;
+  p.nqblk = f.nqblk;
+  p.nkblk = f.nkblk;
   p.q_scale_f16 = a.q_scale_dtype == QFA_F16;
   p.kv_scale_f16 = a.kv_scale_dtype == QFA_F16;
   p.out_dtype = a.out_dtype;
   p.scale_log2 = a.softmax_scale * kLog2e;
-  p.xcd_order = ((long)a.B * a.Hkv) % kXcds == 0;
-  const long grid = (long)p.n_rb * a.B * a.Hkv * p.n_hg;
+  p.xcd_order = f.xcd_order;
+  const long grid = f.grid;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   // Per-key scales unless every tile lies inside one scale block.
-  const bool tok = (a.kv_block % kBN) != 0;
+  const bool tok = f.per_key;
   int kvm = -1;
   if (a.q_qtype == QFA_FP8_E4M3 && a.k_qtype == QFA_FP8_E4M3 && a.v_qtype == QFA_FP8_E4M3) kvm = KV_F8_F8;
   if (a.q_qtype == QFA_INT8 && a.k_qtype == QFA_INT8 && a.v_qtype == QFA_INT8) kvm = KV_I8_I8;

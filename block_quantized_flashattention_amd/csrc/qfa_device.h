@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "qfa.h"
+#include "qfa_index.h"
 
 namespace qfa {
 
@@ -49,8 +50,8 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 // merge point.
 __device__ __forceinline__ float load_scale(const void* p, long idx, bool f16) {
   const uint16_t* h = (const uint16_t*)p;
-  const long i0 = f16 ? idx : 2 * idx;
-  const long i1 = f16 ? idx : 2 * idx + 1;
+  long i0, i1;
+  ix::scale_halves(idx, f16, i0, i1);
   const uint32_t lo = h[i0], hi = h[i1];
   return f16 ? f16_bits_to_f32(lo) : __uint_as_float(lo | (hi << 16));
 }
