@@ -436,7 +436,10 @@ def main():
         rec["kv_append"] = bench_kv_append(torch, qfa, wl, args.steps, args.warmup)
         if not args.no_decode:
             for key, dwl, prof in (("decode", wl.DECODE, "decode_int8_kv_b32_h32.md"),
-                                   ("decode_int4", wl.DECODE_INT4, "decode_int4_kv_b32_h32.md")):
+                                   ("decode_int4", wl.DECODE_INT4, "decode_int4_kv_b32_h32.md"),
+                                   ("decode_gqa4", wl.DECODE_GQA4, "decode_int8_kv_b32_h32_gqa4.md"),
+                                   ("decode_gqa16_int4", wl.DECODE_GQA16_INT4,
+                                    "decode_int4_kv_b32_h32_gqa16.md")):
                 rec[key] = bench_decode(torch, qfa, wl, dwl, args.steps, args.warmup, flush, prof)
                 log(f"{key} {rec[key]['ms']:.3f} ms, {rec[key]['value']:.0f} GB/s")
     if args.copy_probe:

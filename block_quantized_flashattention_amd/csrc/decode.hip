@@ -1,45 +1,52 @@
-// Decode attention: one query token per sequence against an INT8 or packed
-// INT4 KV cache with block scales (gfx950).
+// Decode attention: one query token per sequence and query head against an
+// INT8 or packed INT4 KV cache with block or per-token scales (gfx950).
 //
 // What it computes ([Ascend-INT8] INT8-operator section 3: the decode KV
 // cache is stored as INT8 and attention reads it without writing a
 // dequantized copy; [FA-INT8/INT4] INT4 layer for the INT4 codes):
 //   o_bh = sum_{j < L_b} softmax_j(softmax_scale * q_bh . (sk_j Kc_j)) * sv_j Vc_j
 //
-// Design (HBM-bound: every valid cache byte is read once):
-//   * Split-K: a workgroup of 8 wavefronts owns one (batch, query head,
-//     1024-token chunk); each wavefront owns 128 consecutive tokens (short
-//     per-wavefront score arrays keep the registers low, so more wavefronts
-//     are resident per SIMD to cover the HBM latency). Chunks
-//     past a sequence's length exit at once. A second small kernel merges the
-//     chunks' partial (max, sum, o) by log-sum-exp; a sequence that fits one
-//     chunk is written directly.
-//   * Lane geometry: a 16-byte load per lane, LPT = row_bytes/16 lanes per
-//     token, so one wavefront load covers 64/LPT consecutive tokens; loads are
-//     issued four at a time ahead of their use.
-//   * Two passes per 128 tokens: all scores first (a per-lane partial dot
-//     product, then a DPP butterfly over the LPT lanes of the token), their
-//     max, then exp2 and the V accumulation. The first V loads are issued
-//     while the last keys are scored, so their latency overlaps that work.
-//     Every lane accumulates o for its own channels over its own tokens; the
-//     token groups are then summed by a reduce-scatter across the lanes (each
-//     exchange halves what a lane holds), which leaves every lane a slice of
-//     the channel sums to write.
-//   * With an fp16 query, INT8 K codes are converted exactly to packed fp16
-//     (the byte goes into the mantissa of 1024 + byte) and dotted with
-//     v_dot2_f32_f16 (fp32 accumulation); V codes are converted with the
-//     unsigned-byte converter after flipping the sign bit (code + 128) and
-//     accumulated in fp32. Packed INT4, which carries twice the codes per
-//     byte, stays in fp16 pairs for both: one shift and mask put a nibble
-//     pair under the exponent of 1024 (1032 + code, exact); keys pair
-//     channels e and e + 4 of each group of 8 (the query is paired the same
-//     way) and drop 1032 * sum(q) once per token; values pair one channel of
-//     two tokens against the two fp16 weights and drop 1032 times the sum of
-//     those weights once per output channel. With an fp32/bf16 query the
-//     codes go to fp32 (offset 128 or 8, removed once per channel).
-//   * When one scale block covers a wavefront's 128 tokens (block size a
-//     multiple of 128), its K and V scales are two scalar loads.
+// Design (HBM-bound: every valid cache byte is read once, for all the query
+// heads that share it):
+//   * A workgroup of four wavefronts owns one (batch, KV head, 1024-token
+//     chunk) and serves every query head of that KV head (up to 16): each K
+//     and V row is read from HBM once for all of them. Each wavefront owns 256
+//     consecutive tokens, walked in steps of 32, with its own softmax state;
+//     the four merge through LDS at the end. Chunks past a sequence's length
+//     exit at once. A second small kernel merges the chunks' partial (max,
+//     sum, o) by log-sum-exp; a sequence that fits one chunk is written
+//     directly.
+//   * Scores on the matrix unit: S^T [16 tokens x 16 heads] = K Q^T with
+//     v_mfma_f32_16x16x32 (fp16; bf16 for a bf16 query; an fp32 query is split
+//     into a high and a low bf16 part, two products). Lane l supplies token
+//     l%16 of a 16-token block and its channels [g D/4, (g+1) D/4), g = l/16,
+//     loaded straight from the cache (one or two 16-byte loads). The sum over
+//     channels does not depend on which channel sits in which operand slot, so
+//     the query operand uses the same slot assignment (packed INT4 keeps the
+//     nibble-pair order of its fp16 conversion). Codes become exact fp16 or
+//     bf16 in registers.
+//   * Softmax on the MFMA output layout: lane l holds head l%16 and tokens
+//     4g..4g+3 of each block, so a head's maximum over a step is the maximum
+//     of the lane's 8 values and two exchanges across lane groups. The
+//     reference maximum moves only when a score exceeds it by more than
+//     kSlack (probabilities stay below 2^kSlack, well inside fp16).
+//   * P.V on the matrix unit: O^T [16 channels x 16 heads] += V^T P^T per
+//     16-channel block, summed over the step's 32 tokens. The probabilities
+//     are already in operand layout (slot i of lane group g is token 4g + i of
+//     the first block for i < 4, token 16 + 4g + i - 4 of the second for
+//     i >= 4); V is staged transposed through LDS with its tokens in that
+//     order, four tokens of one channel per 8-byte write, so each lane's
+//     operand is one 16-byte read. The V scale is folded into P as
+//     p_j sv_j / sv_ref, sv_ref the largest V scale the wavefront has seen
+//     (o is scaled down when it grows, as when the reference max moves).
+//   * Loads go out in batches of 32 rows of 128 bytes (one 32-token step of
+//     INT8 with D = 128, two of packed INT4): 8 KB per wavefront. The next
+//     batch is in flight while one is computed, and the first two are
+//     requested before the query is read. A wavefront walks an even number
+//     of batches (a trailing batch past its tokens is fully masked), so the
+//     loop carries no branch around its loads.
 #include <mutex>
+#include <type_traits>
 
 #include "qfa_device.h"
 #include "qfa_launch.h"
@@ -53,9 +60,16 @@ namespace {
 // stand-in): decode_scratch() looks up each device's address once.
 static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
 
-constexpr int kDecWaves = 8;
-constexpr int kWaveTokens = kDecodeChunk / kDecWaves;  // 128
-constexpr int kGroup = 4;                              // loads issued together
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kGWaves = 4;
+constexpr int kGWaveTokens = kDecodeChunk / kGWaves;  // 256
+constexpr int kStep = 32;                              // tokens per step
+constexpr int kVtStride = kStep + 8;                   // fp16 per staged V^T row (16-byte rows)
+constexpr float kSlack = 8.0f;
+
+// Query dtype handling: fp16 MFMA, bf16 MFMA, or an fp32 query as two bf16 parts.
+enum QMode { Q_F16 = 0, Q_BF16 = 1, Q_F32 = 2 };
 
 struct DecParams {
   const void* q;
@@ -79,7 +93,470 @@ __device__ __forceinline__ void store_out(void* out, long i, float v, int dt) {
   else ((uint16_t*)out)[i] = (uint16_t)f32_to_bf16_bits(v);
 }
 
-// Sum over groups of LPT consecutive lanes (LPT in {2, 4, 8}) with DPP moves.
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero. The last word is the gfx9 default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
+}
+
+// BYTES (4, 8, 16, or 32 as two loads) at byte offset `off` of a buffer.
+template <int BYTES>
+__device__ __forceinline__ void bload(uint32_t* dst, __amdgpu_buffer_rsrc_t rs, int off) {
+  if constexpr (BYTES == 32) {
+    bload<16>(dst, rs, off);
+    bload<16>(dst + 4, rs, off + 16);
+  } else if constexpr (BYTES == 16) {
+    const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    dst[0] = r[0]; dst[1] = r[1]; dst[2] = r[2]; dst[3] = r[3];
+  } else if constexpr (BYTES == 8) {
+    const auto r = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    dst[0] = r[0]; dst[1] = r[1];
+  } else {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+  }
+}
+
+// A scale as loaded: the fp16 bits or the fp32 value, one load each, kept
+// untouched until the value is used. Any operation on a loaded value makes
+// the compiler wait for that load (and, counting in order, for every load
+// issued before it); two 16-bit halves combined into one register right
+// after the next batch's loads were issued waited for the whole batch in the
+// middle of the current step.
+template <bool F16S>
+struct ScaleT {
+  using type = typename std::conditional<F16S, uint16_t, float>::type;
+};
+template <bool F16S>
+__device__ __forceinline__ typename ScaleT<F16S>::type raw_scale(const void* p, long idx) {
+  return ((const typename ScaleT<F16S>::type*)p)[idx];
+}
+template <bool F16S>
+__device__ __forceinline__ float scale_value(typename ScaleT<F16S>::type r) {
+  if constexpr (F16S) return (float)__builtin_bit_cast(_Float16, r);
+  else return r;
+}
+
+// Four signed bytes as two exact fp16 pairs (1024 + (byte ^ 0x80) - 1152).
+__device__ __forceinline__ void i8x4_to_h(uint32_t w, f16x2& lo, f16x2& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u)) - bias;
+  hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u)) - bias;
+}
+
+// Nibbles at bits s..s+3 and 16+s..19+s of w, whose sign bits were already
+// flipped, as the fp16 pair 1032 + code (exact).
+__device__ __forceinline__ f16x2 i4_pair_h(uint32_t wflip, int s) {
+  return __builtin_bit_cast(f16x2, ((wflip >> s) & 0x000F000Fu) | 0x64006400u);
+}
+
+// Element i of a bf16 pair vector from the bf16 bits of two exact values.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  // a and b are small integers (codes): their fp32 bits end in 16 zero bits.
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// K operand of k-step j from the lane's K words (D/4 channels of one token).
+// fp16: INT8 channels in order; INT4 in the nibble-pair order
+// (d, d+4, d+1, d+5, d+2, d+6, d+3, d+7) of one word. bf16: channels in order.
+template <bool INT4>
+__device__ __forceinline__ f16x8 k_operand_f16(const uint32_t* kw, int j) {
+  f16x8 r;
+  if constexpr (!INT4) {
+    f16x2 a, b, c, d;
+    i8x4_to_h(kw[2 * j], a, b);
+    i8x4_to_h(kw[2 * j + 1], c, d);
+    r = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  } else {
+    const uint32_t w = kw[j] ^ 0x88888888u;
+    const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const f16x2 a = i4_pair_h(w, 0) - bias, b = i4_pair_h(w, 4) - bias;
+    const f16x2 c = i4_pair_h(w, 8) - bias, d = i4_pair_h(w, 12) - bias;
+    r = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+  return r;
+}
+// Code u - off as a float, exactly: u (at most 8 bits) goes into the low
+// mantissa bits of 2^23, and 2^23 + off is subtracted. No integer-to-float
+// conversion: the compiler rewrote a sign-extract plus conversion into an
+// unsigned conversion of the sign-extended byte, which is wrong for
+// negative codes.
+__device__ __forceinline__ float code_f32(uint32_t u, float off) {
+  return __uint_as_float(0x4B000000u | u) - (8388608.0f + off);
+}
+
+template <bool INT4>
+__device__ __forceinline__ bf16x8 k_operand_bf16(const uint32_t* kw, int j) {
+  uint32_t u[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float a, b;
+    if constexpr (!INT4) {
+      const uint32_t w = kw[2 * j + e / 2] ^ 0x80808080u;
+      const int s = 16 * (e & 1);
+      a = code_f32((w >> s) & 0xFFu, 128.0f);
+      b = code_f32((w >> (s + 8)) & 0xFFu, 128.0f);
+    } else {
+      const uint32_t w = kw[j] ^ 0x88888888u;
+      a = code_f32((w >> (8 * e)) & 0xFu, 8.0f);
+      b = code_f32((w >> (8 * e + 4)) & 0xFu, 8.0f);
+    }
+    u[e] = bf16_pair(a, b);
+  }
+  return __builtin_bit_cast(bf16x8, (i32x4){(int)u[0], (int)u[1], (int)u[2], (int)u[3]});
+}
+
+// Channel offset (within the lane's D/4 channels) of slot i of k-step j.
+template <bool INT4, int QM>
+__device__ __forceinline__ int slot_channel(int j, int i) {
+  if constexpr (INT4 && QM == Q_F16) return 8 * j + (i >> 1) + 4 * (i & 1);
+  return 8 * j + i;
+}
+
+template <int D, bool INT4>
+struct DecGeo {
+  static constexpr int kRowBytes = INT4 ? D / 2 : D;
+  static constexpr int kKBytes = kRowBytes / 4;  // per lane and 16-token block
+  static constexpr int kKWords = kKBytes / 4;
+  static constexpr int kVBytes = kRowBytes / 8;  // per lane and token (D/8 channels)
+  static constexpr int kVWords = kVBytes / 4;
+  static constexpr int kKSteps = D / 32;         // MFMA k-steps per 16-token block
+  static constexpr int kCB = D / 16;             // 16-channel blocks of O
+  // 32-token steps per load batch: a batch always carries 32 rows of 128
+  // bytes (8 KB per wavefront in flight), whatever the row size.
+  static constexpr int kSub = 128 / kRowBytes;
+};
+
+// One load batch: the codes of kSub steps (and, with block scales, each
+// step's K and V scale).
+template <int D, bool INT4, bool F16S>
+struct StepRegs {
+  static constexpr int kSub = DecGeo<D, INT4>::kSub;
+  uint32_t k[kSub][2][DecGeo<D, INT4>::kKWords];
+  uint32_t v[kSub][4][DecGeo<D, INT4>::kVWords];
+  typename ScaleT<F16S>::type ks[kSub], vs[kSub];
+};
+
+// Stage this lane's 4 tokens x D/8 channels of V (codes) into the wavefront's
+// V^T buffer as fp16: channel c of the lane's group, tokens in operand order.
+template <int D, bool INT4>
+__device__ __forceinline__ void stage_v(const uint32_t (&v)[4][DecGeo<D, INT4>::kVWords],
+                                        _Float16* vt, int c0, int pos0) {
+  using G = DecGeo<D, INT4>;
+#pragma unroll
+  for (int k = 0; k < G::kVWords; ++k) {
+    if constexpr (!INT4) {
+      // Channels 4k..4k+3: transpose the 4x4 bytes (tokens x channels), then
+      // convert each channel's token pairs.
+      const uint32_t d01l = __builtin_amdgcn_perm(v[1][k], v[0][k], 0x05010400u);
+      const uint32_t d01h = __builtin_amdgcn_perm(v[1][k], v[0][k], 0x07030602u);
+      const uint32_t d23l = __builtin_amdgcn_perm(v[3][k], v[2][k], 0x05010400u);
+      const uint32_t d23h = __builtin_amdgcn_perm(v[3][k], v[2][k], 0x07030602u);
+      f16x2 a0, a1, b0, b1, c0h, c1h, e0, e1;
+      i8x4_to_h(d01l, a0, a1);   // channel 4k: tokens 0,1 | channel 4k+1: tokens 0,1
+      i8x4_to_h(d23l, b0, b1);   // the same, tokens 2,3
+      i8x4_to_h(d01h, c0h, c1h); // channels 4k+2, 4k+3: tokens 0,1
+      i8x4_to_h(d23h, e0, e1);   // tokens 2,3
+      const int c = c0 + 4 * k;
+      *(f16x4*)(vt + (c + 0) * kVtStride + pos0) = (f16x4){a0[0], a0[1], b0[0], b0[1]};
+      *(f16x4*)(vt + (c + 1) * kVtStride + pos0) = (f16x4){a1[0], a1[1], b1[0], b1[1]};
+      *(f16x4*)(vt + (c + 2) * kVtStride + pos0) = (f16x4){c0h[0], c0h[1], e0[0], e0[1]};
+      *(f16x4*)(vt + (c + 3) * kVtStride + pos0) = (f16x4){c1h[0], c1h[1], e1[0], e1[1]};
+    } else {
+      // Channels 8k..8k+7: nibble pairs (c, c+4) per token, then token pairs.
+      const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[t] = v[t][k] ^ 0x88888888u;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = __builtin_bit_cast(uint32_t, i4_pair_h(w[t], 4 * s));
+        const f16x2 lo01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[1], x[0], 0x05040100u)) - bias;
+        const f16x2 lo23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[3], x[2], 0x05040100u)) - bias;
+        const f16x2 hi01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[1], x[0], 0x07060302u)) - bias;
+        const f16x2 hi23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[3], x[2], 0x07060302u)) - bias;
+        const int c = c0 + 8 * k + s;  // shift 4s: channel s and s + 4 of the word
+        *(f16x4*)(vt + c * kVtStride + pos0) = (f16x4){lo01[0], lo01[1], lo23[0], lo23[1]};
+        *(f16x4*)(vt + (c + 4) * kVtStride + pos0) = (f16x4){hi01[0], hi01[1], hi23[0], hi23[1]};
+      }
+    }
+  }
+}
+
+// Three workgroups per CU (at most 168 VGPRs); the fp32 query, which keeps
+// two bf16 operand sets, two (it would spill at three).
+template <int D, bool INT4, int QM, bool BS, bool F16S>
+__global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_kernel(DecParams p) {
+  using G = DecGeo<D, INT4>;
+  using Regs = StepRegs<D, INT4, F16S>;
+  // Per wavefront: V^T [D][kVtStride] fp16. After the loop the same bytes
+  // hold the merge of the four wavefronts: o [4][16][D], m [4][16], l [4][16].
+  __shared__ __attribute__((aligned(16))) _Float16 vt_all[kGWaves * D * kVtStride];
+  static_assert(kGWaves * 16 * (D + 2) * 4 <= (int)sizeof(vt_all), "merge area");
+
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = min(max(p.lens[b], 1), p.S_max);
+  const int nsplit = (L + kDecodeChunk - 1) / kDecodeChunk;
+  if (split >= nsplit) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;   // lane group: channels [g D/4, (g+1) D/4) of K, tokens 4g.. of S^T
+  const int n = lane & 15;   // token of a K block (A operand); head of S^T, P^T and O^T
+  const int grp = p.group;
+  _Float16* vt = vt_all + wave * D * kVtStride;
+
+  constexpr int kSub = G::kSub;
+  constexpr int kBatch = kStep * kSub;  // tokens per load batch
+  const int t_begin = split * kDecodeChunk + wave * kGWaveTokens;
+  const int t_end = min(t_begin + kGWaveTokens, L);
+  const int nbatch = t_begin < t_end ? (t_end - t_begin + kBatch - 1) / kBatch : 0;
+  const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
+
+  // Rows [0, L) of this (batch, KV head) through buffer resources: rows at or
+  // past L read as zero (their scores are masked). Offsets stay below 2^31
+  // (the host checks (S_max + chunk) * row stride).
+  const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
+  const int span = (L - 1) * (int)p.c_row + G::kRowBytes;
+  const auto krs = rows_rsrc(p.k + cbase, span);
+  const auto vrs = rows_rsrc(p.v + cbase, span);
+  const int crow = (int)p.c_row;
+  const int tq = lane >> 3, cg = lane & 7;  // V staging: tokens 4tq..4tq+3, channel group cg
+  const int pos0 = tq < 4 ? 8 * tq : 8 * (tq - 4) + 4;
+
+  auto issue = [&](Regs& r, int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      const int t0 = t_begin + kBatch * s + kStep * u;
+      if constexpr (BS) {
+        const long blk = sbase + min(t0, L - 1) / p.kv_block;
+        r.ks[u] = raw_scale<F16S>(p.ks, blk);
+        r.vs[u] = raw_scale<F16S>(p.vs, blk);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        bload<G::kKBytes>(r.k[u][tb], krs, (t0 + 16 * tb + n) * crow + g * G::kKBytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bload<G::kVBytes>(r.v[u][i], vrs, (t0 + 4 * tq + i) * crow + cg * G::kVBytes);
+    }
+  };
+
+  // The first two load batches go out before anything else is read.
+  Regs ra, rb;
+  if (nbatch > 0) {
+    issue(ra, 0);
+    issue(rb, min(1, nbatch - 1));
+  }
+
+  // Query operand (B of S^T = K Q^T): head n of this KV head's group, the
+  // channels of this lane's slots; zero for heads past the group.
+  const bool hvalid = n < grp;
+  const long qoff = (long)b * p.q_batch + (long)(kvh * grp + (hvalid ? n : 0)) * p.q_head + g * (D / 4);
+  f16x8 qh[G::kKSteps];
+  bf16x8 qb[G::kKSteps], qb2[G::kKSteps];
+#pragma unroll
+  for (int j = 0; j < G::kKSteps; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int d = slot_channel<INT4, QM>(j, i);
+      if constexpr (QM == Q_F16) {
+        const uint16_t bits = ((const uint16_t*)p.q)[qoff + d];
+        qh[j][i] = hvalid ? __builtin_bit_cast(_Float16, bits) : (_Float16)0.0f;
+      } else if constexpr (QM == Q_BF16) {
+        const uint16_t bits = ((const uint16_t*)p.q)[qoff + d];
+        qb[j][i] = __builtin_bit_cast(__bf16, (uint16_t)(hvalid ? bits : 0));
+      } else {
+        const float x = hvalid ? ((const float*)p.q)[qoff + d] : 0.0f;
+        const uint32_t hi = f32_to_bf16_bits(x);
+        const float rest = x - __uint_as_float(hi << 16);
+        qb[j][i] = __builtin_bit_cast(__bf16, (uint16_t)hi);
+        qb2[j][i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(rest));
+      }
+    }
+  }
+
+  f32x4 o[G::kCB];
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb) o[cb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  float m_ref = -INFINITY;  // reference max of head n (log2 units), same in the 4 lane groups
+  float l_sum = 0.0f;       // this lane's part of head n's sum, in units of exp2(-m_ref)
+  // V scale o is expressed in: the largest V scale seen so far (o is scaled
+  // down when a larger one arrives), so the fp16 weights p sv / sv_ref stay
+  // at most 2^kSlack.
+  float sv_ref = 0.0f;
+
+  auto step = [&](const Regs& r, int u, int t0) __attribute__((always_inline)) {
+    stage_v<D, INT4>(r.v[u], vt, cg * (D / 8), pos0);
+
+    // Scores: two 16-token blocks.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      sacc[tb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < G::kKSteps; ++j) {
+        if constexpr (QM == Q_F16) {
+          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand_f16<INT4>(r.k[u][tb], j),
+                                                            qh[j], sacc[tb], 0, 0, 0);
+        } else {
+          const bf16x8 ka = k_operand_bf16<INT4>(r.k[u][tb], j);
+          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j], sacc[tb], 0, 0, 0);
+          if constexpr (QM == Q_F32)
+            sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb2[j], sacc[tb], 0, 0, 0);
+        }
+      }
+    }
+
+    // Scaled, masked scores of this lane (y[4 tb + i] is token t0 + 16 tb +
+    // 4g + i) and their V scales.
+    float y[8], sv[8];
+    const float ck_blk = BS ? scale_value<F16S>(r.ks[u]) * p.scale_log2 : 0.0f;
+    const float sv_blk = BS ? scale_value<F16S>(r.vs[u]) : 0.0f;
+    float sv_max = sv_blk;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * tb + 4 * g + i;
+        float ck = ck_blk, svt = sv_blk;
+        if constexpr (!BS) {
+          const long blk = sbase + min(t, L - 1) / p.kv_block;
+          ck = scale_value<F16S>(raw_scale<F16S>(p.ks, blk)) * p.scale_log2;
+          svt = scale_value<F16S>(raw_scale<F16S>(p.vs, blk));
+          sv_max = fmaxf(sv_max, t < t_end ? svt : 0.0f);
+        }
+        y[4 * tb + i] = t < t_end ? sacc[tb][i] * ck : -INFINITY;
+        sv[4 * tb + i] = svt;
+      }
+    if constexpr (!BS) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sv_max = fmaxf(sv_max, __shfl_xor(sv_max, off));
+    } else {
+      sv_max = t0 < t_end ? sv_max : 0.0f;
+    }
+    float mx = y[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Lazy rescale, decided for the whole wavefront: a new reference max, or
+    // a larger V scale (sv_max is uniform over the wavefront).
+    const bool need = mx > m_ref + kSlack;
+    if (__builtin_amdgcn_ballot_w64(need) || sv_max > sv_ref) {
+      const float m_new = need ? mx : m_ref;
+      const float sv_new = fmaxf(sv_ref, sv_max);
+      // 0 on the first step (m_ref = -inf, sv_ref = 0)
+      const float alpha = sv_ref > 0.0f ? __builtin_amdgcn_exp2f(m_ref - m_new) * (sv_ref / sv_new) : 0.0f;
+      const float lalpha = m_new == m_ref ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int cb = 0; cb < G::kCB; ++cb) o[cb] *= alpha;
+      l_sum *= lalpha;
+      m_ref = m_new;
+      sv_ref = sv_new;
+    }
+    const float mref = m_ref == -INFINITY ? 0.0f : m_ref;
+    const float inv_ref = sv_ref > 0.0f ? 1.0f / sv_ref : 0.0f;
+    f16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float pr = __builtin_amdgcn_exp2f(y[i] - mref);
+      l_sum += pr;
+      pb[i] = (_Float16)(pr * (sv[i] * inv_ref));
+    }
+
+    // P.V: the staged V^T rows of this lane's channels, tokens in slot order.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int cb = 0; cb < G::kCB; ++cb) {
+      const f16x8 a = *(const f16x8*)(vt + (cb * 16 + n) * kVtStride + 8 * g);
+      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, o[cb], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto compute = [&](const Regs& r, int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      step(r, u, t_begin + kBatch * s + kStep * u);
+      // one step's conversions at a time: interleaving two spills
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // An even number of batches; a trailing batch past the tokens is fully
+  // masked and its loads repeat the last batch's rows. While one batch is
+  // computed the next is in flight.
+  const int nbatch2 = (nbatch + 1) & ~1;
+  // The fences keep every use of a batch after the issue of the next one:
+  // the scheduler otherwise moved the start of a batch's work above the
+  // following issue, leaving nothing in flight while the batch was awaited.
+  for (int s = 0; s < nbatch2; s += 2) {
+    compute(ra, s);
+    issue(ra, min(s + 2, nbatch - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(rb, s + 1);
+    issue(rb, min(s + 3, nbatch - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  l_sum += __shfl_xor(l_sum, 16);
+  l_sum += __shfl_xor(l_sum, 32);
+
+  // Merge the four wavefronts (o in V-scale units: times sv_ref).
+  __syncthreads();
+  float* mo = (float*)vt_all;            // [4][16][D]
+  float* mm = mo + kGWaves * 16 * D;   // [4][16]
+  float* ml = mm + kGWaves * 16;       // [4][16]
+#pragma unroll
+  for (int cb = 0; cb < G::kCB; ++cb)
+    *(f32x4*)(mo + (wave * 16 + n) * D + cb * 16 + 4 * g) = o[cb] * sv_ref;
+  if (g == 0) {
+    mm[wave * 16 + n] = m_ref;
+    ml[wave * 16 + n] = l_sum;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < grp * D; idx += 64 * kGWaves) {
+    const int hn = idx / D, c = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kGWaves; ++w) M = fmaxf(M, mm[w * 16 + hn]);
+    float lsum = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGWaves; ++w) {
+      const float mw = mm[w * 16 + hn];
+      const float cw = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      lsum += ml[w * 16 + hn] * cw;
+      acc += mo[(w * 16 + hn) * D + c] * cw;
+    }
+    const int h = kvh * grp + hn;
+    if (nsplit == 1) {
+      store_out(p.out, (long)b * p.q_batch + (long)h * p.q_head + c, acc / lsum, p.out_dtype);
+    } else {
+      float* part = p.ws + (((long)b * p.Hq + h) * p.max_splits + split) * (D + 2);
+      part[c] = acc;
+      if (c == 0) {
+        part[D] = M;
+        part[D + 1] = lsum;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One query head per KV head (no GQA sharing to exploit): dot products on the
+// vector unit, which for a single head reads the cache at a higher rate than
+// the matrix-unit kernel below.
+// ---------------------------------------------------------------------------
+
+constexpr int kSWaves = 8;
+constexpr int kSWaveTokens = kDecodeChunk / kSWaves;  // 128
+constexpr int kSLoadGroup = 4;                         // loads issued together
+
 template <int LPT>
 __device__ __forceinline__ float lane_group_sum(float v) {
   // quad_perm [1,0,3,2] and [2,3,0,1]: partners at lane xor 1 and xor 2.
@@ -91,20 +568,10 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   return v;
 }
 
-// Four signed bytes as two exact fp16 pairs (1024 + (byte ^ 0x80) - 1152).
-__device__ __forceinline__ void i8x4_to_h(uint32_t w, f16x2& lo, f16x2& hi) {
-  const uint32_t u = w ^ 0x80808080u;
-  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);
-  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u);
-  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  lo = __builtin_bit_cast(f16x2, a) - bias;
-  hi = __builtin_bit_cast(f16x2, b) - bias;
-}
-
 // The nibbles at bits 0-3 and 16-19 of w (two's-complement codes) as an fp16
 // pair 1032 + code, exact: flip the sign bit, keep the nibbles, set the
 // exponent of 1024.
-__device__ __forceinline__ uint32_t i4_pair_h(uint32_t w) {
+__device__ __forceinline__ uint32_t i4_pair_bits(uint32_t w) {
   return ((w ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
 }
 
@@ -163,30 +630,24 @@ __device__ __forceinline__ int scatter_base(int lane) {
   }
 }
 
-// Raw buffer resource over [base, base + bytes): loads past the end return
-// zero. The last word is the gfx9 default (32-bit data format, no swizzle).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
-}
-
 // Packed INT4 with an fp16 query and block scales asks for six wavefronts per
 // SIMD, i.e. three workgroups per CU (at most 80 VGPRs): its rows are half as
 // long, so more of them must be in flight to cover the HBM latency.
 template <int D, bool INT4, bool QF16, bool BLOCK_SCALE>
-__global__ __launch_bounds__(64 * kDecWaves, INT4 && QF16 && BLOCK_SCALE ? 6 : 2)
-void decode_split_kernel(DecParams p) {
+__global__ __launch_bounds__(64 * kSWaves, INT4 && QF16 && BLOCK_SCALE ? 6 : 2)
+void decode_mha_kernel(DecParams p) {
   constexpr int kRowBytes = INT4 ? D / 2 : D;
   constexpr int LPT = kRowBytes / 16;        // lanes per token
   constexpr int EPL = INT4 ? 32 : 16;        // channels per lane
   constexpr int TPS = 64 / LPT;              // tokens per wavefront load
-  constexpr int NSUB = kWaveTokens / TPS;    // loads per lane per wavefront chunk
-  constexpr int NG = NSUB / kGroup;
+  constexpr int NSUB = kSWaveTokens / TPS;    // loads per lane per wavefront chunk
+  constexpr int NG = NSUB / kSLoadGroup;
   constexpr float kOff = INT4 ? 8.0f : 128.0f;
-  static_assert(NSUB % kGroup == 0, "load groups");
+  static_assert(NSUB % kSLoadGroup == 0, "load groups");
   constexpr int NF = EPL / (64 / LPT);  // channels per lane after the token-group reduction
   static_assert(NF >= 1 && EPL % (64 / LPT) == 0, "reduce-scatter");
-  __shared__ float red_m[kDecWaves], red_l[kDecWaves];
-  __shared__ float red_o[kDecWaves][D];
+  __shared__ float red_m[kSWaves], red_l[kSWaves];
+  __shared__ float red_o[kSWaves][D];
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -252,8 +713,8 @@ void decode_split_kernel(DecParams p) {
   const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
   const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
 
-  const int t_begin = split * kDecodeChunk + wave * kWaveTokens;
-  const int t_end = min(t_begin + kWaveTokens, L);
+  const int t_begin = split * kDecodeChunk + wave * kSWaveTokens;
+  const int t_end = min(t_begin + kSWaveTokens, L);
   const int t_last = t_end - 1;
 
   float m_blk = -INFINITY, l_blk = 0.0f, wsum = 0.0f;
@@ -265,7 +726,7 @@ void decode_split_kernel(DecParams p) {
   if (t_begin < t_end) {
     // ---- scores: sc[j] for token t_begin + j*TPS + tg (log2 units) ----
     float sc[NSUB];
-    uint4 kw[2][kGroup];
+    uint4 kw[2][kSLoadGroup];
     // Rows [0, L) of this (batch, KV head) through buffer resources: one
     // 32-bit offset per lane (the host keeps every offset below 2^31), and
     // rows at or past L read as zero, so no clamp is needed (their scores
@@ -280,12 +741,12 @@ void decode_split_kernel(DecParams p) {
     };
     auto kload = [&](uint4* dst, int g) {
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) dst[i] = bload(krs, g * kGroup + i);
+      for (int i = 0; i < kSLoadGroup; ++i) dst[i] = bload(krs, g * kSLoadGroup + i);
     };
-    uint4 vw[2][kGroup];
+    uint4 vw[2][kSLoadGroup];
     auto vload = [&](uint4* dst, int g) {
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) dst[i] = bload(vrs, g * kGroup + i);
+      for (int i = 0; i < kSLoadGroup; ++i) dst[i] = bload(vrs, g * kSLoadGroup + i);
     };
     kload(kw[0], 0);
     if constexpr (BLOCK_SCALE) {
@@ -299,8 +760,8 @@ void decode_split_kernel(DecParams p) {
       if (g + 1 < NG) kload(kw[(g + 1) & 1], g + 1);
       else vload(vw[0], 0);  // first V group, in flight while the last keys are scored
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const int j = g * kGroup + i;
+      for (int i = 0; i < kSLoadGroup; ++i) {
+        const int j = g * kSLoadGroup + i;
         const uint4 w = kw[g & 1][i];
         float acc;
         if constexpr (QF16) {
@@ -313,7 +774,7 @@ void decode_split_kernel(DecParams p) {
             for (int i = 0; i < 4; ++i)
 #pragma unroll
               for (int sft = 0; sft < 4; ++sft)
-                kh[4 * i + sft] = __builtin_bit_cast(f16x2, i4_pair_h(ww[i] >> (4 * sft)));
+                kh[4 * i + sft] = __builtin_bit_cast(f16x2, i4_pair_bits(ww[i] >> (4 * sft)));
           } else {
             i8x4_to_h(w.x, kh[0], kh[1]);
             i8x4_to_h(w.y, kh[2], kh[3]);
@@ -357,11 +818,11 @@ void decode_split_kernel(DecParams p) {
         // Two tokens at a time: each channel's codes of tokens j and j + 1
         // form one fp16 pair (1032 + code), dotted with the two weights in
         // fp16; the sums of those same fp16 weights remove the offset.
-        static_assert(kGroup % 2 == 0, "token pairs");
+        static_assert(kSLoadGroup % 2 == 0, "token pairs");
         const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-        for (int i = 0; i < kGroup; i += 2) {
-          const int j = g * kGroup + i;
+        for (int i = 0; i < kSLoadGroup; i += 2) {
+          const int j = g * kSLoadGroup + i;
           const float pa = __builtin_amdgcn_exp2f(sc[j] - m_blk);  // 0 for masked tokens
           const float pb = __builtin_amdgcn_exp2f(sc[j + 1] - m_blk);
           float wa = pa, wb = pb;
@@ -391,16 +852,16 @@ void decode_split_kernel(DecParams p) {
             for (int c = 0; c < 4; ++c) {
               const uint32_t sft = (c & 1) * 4 + (c >> 1) * 8;
               o[8 * d + c] = __builtin_amdgcn_fdot2(
-                  wp, __builtin_bit_cast(f16x2, i4_pair_h(r0 >> sft)), o[8 * d + c], false);
+                  wp, __builtin_bit_cast(f16x2, i4_pair_bits(r0 >> sft)), o[8 * d + c], false);
               o[8 * d + 4 + c] = __builtin_amdgcn_fdot2(
-                  wp, __builtin_bit_cast(f16x2, i4_pair_h(r1 >> sft)), o[8 * d + 4 + c], false);
+                  wp, __builtin_bit_cast(f16x2, i4_pair_bits(r1 >> sft)), o[8 * d + 4 + c], false);
             }
           }
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-          const int j = g * kGroup + i;
+        for (int i = 0; i < kSLoadGroup; ++i) {
+          const int j = g * kSLoadGroup + i;
           const float pr = __builtin_amdgcn_exp2f(sc[j] - m_blk);  // 0 for masked tokens
           lp[i & 1] += pr;
           float wt = pr;
@@ -444,11 +905,11 @@ void decode_split_kernel(DecParams p) {
   if (wave != 0) return;
   float M = red_m[0];
 #pragma unroll
-  for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, red_m[w]);
-  float c[kDecWaves];
+  for (int w = 1; w < kSWaves; ++w) M = fmaxf(M, red_m[w]);
+  float c[kSWaves];
   float Lsum = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) {
+  for (int w = 0; w < kSWaves; ++w) {
     c[w] = red_m[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(red_m[w] - M);
     Lsum += red_l[w] * c[w];
   }
@@ -458,7 +919,7 @@ void decode_split_kernel(DecParams p) {
     for (int d = lane; d < D; d += 64) {
       float acc = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) acc += red_o[w][d] * c[w];
+      for (int w = 0; w < kSWaves; ++w) acc += red_o[w][d] * c[w];
       store_out(p.out, obase + d, acc * inv, p.out_dtype);
     }
     return;
@@ -467,7 +928,7 @@ void decode_split_kernel(DecParams p) {
   for (int d = lane; d < D; d += 64) {
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) acc += red_o[w][d] * c[w];
+    for (int w = 0; w < kSWaves; ++w) acc += red_o[w][d] * c[w];
     part[d] = acc;
   }
   if (lane == 0) {
@@ -534,23 +995,45 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecParams p) {
 }
 
 template <int D, bool INT4, bool QF16, bool BS>
-hipError_t launch_dec4(const DecParams& p, int B, hipStream_t st) {
-  decode_split_kernel<D, INT4, QF16, BS><<<dim3(p.max_splits, p.Hq, B), 64 * kDecWaves, 0, st>>>(p);
-  hipError_t e = hipGetLastError();
+hipError_t launch_mha(const DecParams& p, int B, hipStream_t st) {
+  decode_mha_kernel<D, INT4, QF16, BS><<<dim3(p.max_splits, p.Hq, B), 64 * kSWaves, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+template <int D, bool INT4, int QM, bool BS>
+hipError_t launch_gqa(const DecParams& p, int B, hipStream_t st) {
+  const dim3 grid(p.max_splits, p.Hkv, B);
+  if (p.kv_scale_f16) decode_gqa_kernel<D, INT4, QM, BS, true><<<grid, 64 * kGWaves, 0, st>>>(p);
+  else decode_gqa_kernel<D, INT4, QM, BS, false><<<grid, 64 * kGWaves, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+template <int D, bool INT4>
+hipError_t launch_dec(const DecParams& p, int B, hipStream_t st) {
+  hipError_t e;
+  if (p.group == 1) {
+    // Block scales are uniform over a wavefront's 128 tokens.
+    const bool bs = p.kv_block % kSWaveTokens == 0;
+    if (p.q_dtype == QFA_F16)
+      e = bs ? launch_mha<D, INT4, true, true>(p, B, st) : launch_mha<D, INT4, true, false>(p, B, st);
+    else
+      e = bs ? launch_mha<D, INT4, false, true>(p, B, st) : launch_mha<D, INT4, false, false>(p, B, st);
+  } else {
+    // Block scales are uniform over a 32-token step (steps start at multiples of 32).
+    const bool bs = p.kv_block % kStep == 0;
+    if (p.q_dtype == QFA_F16)
+      e = bs ? launch_gqa<D, INT4, Q_F16, true>(p, B, st) : launch_gqa<D, INT4, Q_F16, false>(p, B, st);
+    else if (p.q_dtype == QFA_BF16)
+      e = bs ? launch_gqa<D, INT4, Q_BF16, true>(p, B, st) : launch_gqa<D, INT4, Q_BF16, false>(p, B, st);
+    else
+      e = bs ? launch_gqa<D, INT4, Q_F32, true>(p, B, st) : launch_gqa<D, INT4, Q_F32, false>(p, B, st);
+  }
   if (e != hipSuccess) return e;
   if (p.max_splits > 1) {
     decode_reduce_kernel<D><<<dim3(p.Hq, B), 64, 0, st>>>(p);
     e = hipGetLastError();
   }
   return e;
-}
-
-template <int D, bool INT4>
-hipError_t launch_dec(const DecParams& p, int B, hipStream_t st) {
-  const bool qf16 = p.q_dtype == QFA_F16;
-  const bool bs = p.kv_block % kWaveTokens == 0;
-  if (qf16) return bs ? launch_dec4<D, INT4, true, true>(p, B, st) : launch_dec4<D, INT4, true, false>(p, B, st);
-  return bs ? launch_dec4<D, INT4, false, true>(p, B, st) : launch_dec4<D, INT4, false, false>(p, B, st);
 }
 
 }  // namespace
@@ -605,14 +1088,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.S_max = a.S_max;
   p.max_splits = (a.S_max + kDecodeChunk - 1) / kDecodeChunk;
   const long rb = a.kv_qtype == QFA_INT4 ? a.D / 2 : a.D;
-  if (a.layout == QFA_BNSD) {
-    p.c_row = rb;
-    p.c_head = (long)a.S_max * rb;
-  } else {
-    p.c_row = (long)a.Hkv * rb;
-    p.c_head = rb;
-  }
-  p.c_batch = (long)a.Hkv * a.S_max * rb;
+  const ix::Strides cs = ix::strides(a.layout == QFA_BSND, a.Hkv, a.S_max, rb);
+  p.c_row = cs.row;
+  p.c_head = cs.head;
+  p.c_batch = cs.batch;
   p.q_head = a.D;
   p.q_batch = (long)a.Hq * a.D;
   p.kv_block = a.kv_block;

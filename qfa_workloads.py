@@ -131,6 +131,11 @@ INT8QK_INT4V = dataclasses.replace(INT8_CAUSAL, name="int8qk_int4v_causal_h32_s4
 # fp16 scale per 256-token block): half the cache bytes of INT8.
 DECODE_INT4 = dataclasses.replace(DECODE, name="int4_kv_decode_b32_h32", kv_qtype="int4")
 
+# The same decode shape with grouped KV heads: 32 query heads over 8 (groups
+# of 4) with the INT8 cache, over 2 (groups of 16) with the packed INT4 cache.
+DECODE_GQA4 = dataclasses.replace(DECODE, name="int8_kv_decode_b32_h32_gqa4", Hkv=8)
+DECODE_GQA16_INT4 = dataclasses.replace(DECODE_INT4, name="int4_kv_decode_b32_h32_gqa16", Hkv=2)
+
 PREFILL_WORKLOADS = {w.name: w for w in (TINY, INT8_CAUSAL, FP8_ROT, GQA_INT4)}
 
 

@@ -93,11 +93,14 @@ def test_decode_query_dtypes(qdt, odt, qt, R):
     _run(w, q, k, v, torch.tensor(lens, dtype=torch.int32))
 
 
-@pytest.mark.parametrize("w", [wl.DECODE, wl.DECODE_INT4], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [wl.DECODE, wl.DECODE_INT4, wl.DECODE_GQA4, wl.DECODE_GQA16_INT4],
+                         ids=lambda w: w.name)
 def test_full_size_decode_sampled(w):
-    """The full decode workload (B=32, 32 heads, S_max=8192, L in [4096, 8192]),
-    INT8 or packed INT4 cache, inputs drawn on the GPU; 24 (batch, head) pairs
-    compared with the oracle."""
+    """The full decode workload (B=32, 32 query heads, S_max=8192, L in
+    [4096, 8192]), INT8 or packed INT4 cache, one query head per KV head or
+    grouped (4 and 16 per KV head, the matrix-unit kernel); inputs drawn on
+    the GPU; 24 (batch, KV head) pairs, every query head of each, compared
+    with the oracle."""
     say("full-size decode: generating inputs on the GPU")
     q, k, v, lens = wl.make_decode_inputs(w, device="cuda")
     rng = np.random.default_rng(7)
