@@ -225,6 +225,46 @@ def bench_forward(torch, qfa, wl, w, steps, warmup):
     return sum(a.elapsed_time(b) for a, b in evs) / steps
 
 
+def bench_fwd_lowp(torch, qfa, wl, steps, warmup):
+    """The FP8 workload's forward with P.V on the fp8 matrix unit (qfa_fwd_lowp:
+    fp8 pass, then the fp16 pass over the work items the accuracy gate
+    flagged) against qfa_fwd on the same codes: average kernel-pair time over
+    back-to-back calls, and the fraction of work items that fell back."""
+    w = wl.FP8_ROT
+    q, k, v = wl.make_prefill_inputs(w, device="cuda")
+    qc, qs = qfa.block_quant(q, w.q_block, "fp8")
+    kc, ks = qfa.block_quant(k, w.kv_block, "fp8")
+    vc, vs = qfa.block_quant(v, w.kv_block, "fp8")
+    del q, k, v
+    kw = dict(q_qtype="fp8", k_qtype="fp8", v_qtype="fp8", q_block=w.q_block,
+              kv_block=w.kv_block, softmax_scale=w.softmax_scale, causal=w.causal,
+              out_dtype=wl.torch_dtype(w.out_dtype))
+    f16, _ = qfa.prepare_fwd(qc, qs, kc, ks, vc, vs, **kw)
+    flp, _, ws = qfa.prepare_fwd_lowp(qc, qs, kc, ks, vc, vs, **kw)
+
+    def avg(f):
+        settle(torch, f)
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        evs = [_events(torch) for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            f()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / steps
+    t16, tlp = avg(f16), avg(flp)
+    nitems = ws.numel() // 8
+    flagged = float(ws.cpu()[:8 * nitems].view(nitems, 8).any(dim=1).float().mean())
+    ops = w.attention_ops()
+    return {"workload": w.name, "fwd_ms": round(t16, 4), "fwd_lowp_ms": round(tlp, 4),
+            "speedup": round(t16 / tlp, 3), "fallback_items": round(flagged, 4),
+            "roofline": mfma_roofline(ops, tlp, PEAK_FP8_TFLOPS),
+            "note": "fp8 pass plus the fp16 pass over flagged work items; a flagged item "
+                    "is recomputed whole, so any flag adds about one workgroup's duration"}
+
+
 def bench_rotate_quant(torch, qfa, wl, steps, warmup, flush):
     """Fused rotation + FP8 block quantization of Q (128-row blocks) and K
     (256-row blocks) of the FP8 workload's shape: the pair's time, cache
@@ -430,6 +470,10 @@ def main():
         rec["fwd_int8qk_int4v"] = {"workload": mw.name, "fwd_ms": round(mms, 4),
                                    "roofline": mfma_roofline(mw.attention_ops(), mms, PEAK_INT8_TOPS)}
         log(f"forward {mw.name}: {mms:.3f} ms")
+        rec["fwd_lowp_pv"] = bench_fwd_lowp(torch, qfa, wl, args.steps, args.warmup)
+        log(f"fp8 P.V forward: {rec['fwd_lowp_pv']['fwd_lowp_ms']:.4f} ms against "
+            f"{rec['fwd_lowp_pv']['fwd_ms']:.4f} ms, fallback items "
+            f"{rec['fwd_lowp_pv']['fallback_items']:.2%}")
         rec["rotate_quantize"] = bench_rotate_quant(torch, qfa, wl, args.steps, args.warmup, flush)
         log(f"rotate+quantize: {rec['rotate_quantize']['ms']:.4f} ms cached, "
             f"{rec['rotate_quantize']['ms_flushed']:.4f} ms flushed")

@@ -60,6 +60,11 @@ def lib() -> ctypes.CDLL:
     L.qfa_fwd.argtypes = [vp, vp, i, i, i, vp, vp, i, vp, vp, i, i, i,
                           i, i, i, i, i, i, i, i, f, vp, i, vp]
     L.qfa_fwd.restype = i
+    L.qfa_fwd_lowp.argtypes = [vp, vp, i, i, i, vp, vp, i, vp, vp, i, i, i,
+                          i, i, i, i, i, i, i, i, f, vp, i, vp, sz, vp]
+    L.qfa_fwd_lowp.restype = i
+    L.qfa_fwd_lowp_workspace_bytes.argtypes = [i, i, i, i]
+    L.qfa_fwd_lowp_workspace_bytes.restype = sz
     L.qfa_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.qfa_decode_workspace_bytes.restype = sz
     L.qfa_decode.argtypes = [vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, i, i, vp, f, vp, i,
@@ -365,6 +370,52 @@ def prepare_fwd(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, q_qt
     return launch, out
 
 
+def fwd_lowp_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int) -> int:
+    return int(lib().qfa_fwd_lowp_workspace_bytes(B, Hq, Hkv, Sq))
+
+
+def _lowp_workspace(args, workspace, device):
+    B, Hq, Hkv, Sq = args[13], args[14], args[15], args[16]
+    need = fwd_lowp_workspace_bytes(B, Hq, Hkv, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=device)
+    _dev(workspace, "workspace")
+    if workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
+    return args[:-1] + (_ptr(workspace), workspace.numel(), args[-1]), workspace
+
+
+def fwd_lowp(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, q_qtype: str,
+             k_qtype: str, v_qtype: str, q_block: int, kv_block: int, softmax_scale: float,
+             causal: bool = False, layout: str = "bnsd", out_dtype=torch.float16, out=None,
+             workspace=None, stream=None):
+    """``fwd`` with P.V on the fp8 matrix unit (e4m3 Q/K/V, block scales) and
+    the accuracy-gated fp16 fallback; returns (out, workspace). Byte 8*w + v
+    of the workspace is 1 where wavefront v of work item w fell back."""
+    args, out = _fwd_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, q_qtype,
+                          k_qtype, v_qtype, q_block, kv_block, softmax_scale, causal, layout,
+                          out_dtype, out, stream)
+    args, workspace = _lowp_workspace(args, workspace, q_codes.device)
+    _check("qfa_fwd_lowp", lib().qfa_fwd_lowp(*args))
+    return out, workspace
+
+
+def prepare_fwd_lowp(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, q_qtype: str,
+                     k_qtype: str, v_qtype: str, q_block: int, kv_block: int,
+                     softmax_scale: float, causal: bool = False, layout: str = "bnsd",
+                     out_dtype=torch.float16, out=None, workspace=None, stream=None):
+    """Marshal one ``fwd_lowp`` call once; returns (launch, out, workspace)."""
+    args, out = _fwd_args(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, q_qtype,
+                          k_qtype, v_qtype, q_block, kv_block, softmax_scale, causal, layout,
+                          out_dtype, out, stream)
+    args, workspace = _lowp_workspace(args, workspace, q_codes.device)
+    f = lib().qfa_fwd_lowp
+
+    def launch():
+        _check("qfa_fwd_lowp", f(*args))
+    return launch, out, workspace
+
+
 def decode_workspace_bytes(B: int, Hq: int, S_max: int, D: int) -> int:
     return int(lib().qfa_decode_workspace_bytes(B, Hq, S_max, D))
 
@@ -455,7 +506,8 @@ def prepare_decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtyp
 
 
 __all__ = ["block_quant", "block_quant_multi", "prepare_block_quant_multi", "rotate_block_quant",
-           "prepare_rotate_block_quant", "kv_append", "fwd", "prepare_fwd",
+           "prepare_rotate_block_quant", "kv_append", "fwd", "prepare_fwd", "fwd_lowp",
+           "prepare_fwd_lowp", "fwd_lowp_workspace_bytes",
            "decode", "prepare_decode", "decode_workspace_bytes", "decode_noalloc",
            "decode_noalloc_max_bytes", "lib", "header_functions",
            "QFAError", "QTYPES", "LAYOUTS", "FLOATS", "QMAX", "code_dtype"]

@@ -118,11 +118,15 @@ int qfa_kv_append(const void* x, int x_dtype, const int32_t* positions, void* co
   return from_hip(qfa::launch_kv_append(a, (hipStream_t)stream));
 }
 
-int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
-            int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
-            const void* v_codes, const void* v_scales, int v_qtype, int kv_block,
-            int kv_scale_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int layout,
-            int causal, float softmax_scale, void* out, int out_dtype, void* stream) {
+// Validation shared by the two forward entry points; QFA_OK with *empty set
+// when there is nothing to compute.
+static int check_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
+                     int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
+                     const void* v_codes, const void* v_scales, int v_qtype, int kv_block,
+                     int kv_scale_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                     int layout, int causal, float softmax_scale, const void* out,
+                     int out_dtype, bool* empty) {
+  *empty = false;
   if (!valid_qtype(q_qtype) || !valid_qtype(k_qtype) || !valid_qtype(v_qtype) ||
       !valid_layout(layout) || !valid_float(out_dtype) ||
       (q_scale_dtype != QFA_F32 && q_scale_dtype != QFA_F16) ||
@@ -133,7 +137,10 @@ int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
     return QFA_ERR_SHAPE;
   if (D != 64 && D != 128) return QFA_ERR_UNSUPPORTED;
   if (causal && Sq != Sk) return QFA_ERR_UNSUPPORTED;
-  if (B == 0 || Sq == 0) return QFA_OK;
+  if (B == 0 || Sq == 0) {
+    *empty = true;
+    return QFA_OK;
+  }
   if (Sk < 1) return QFA_ERR_SHAPE;
   if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f || softmax_scale > 3.0e38f)
     return QFA_ERR_SHAPE;
@@ -152,10 +159,50 @@ int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
       !aligned(out, 16) || !aligned(q_scales, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4))
     return QFA_ERR_UNSUPPORTED;
+  return QFA_OK;
+}
+
+int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
+            int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
+            const void* v_codes, const void* v_scales, int v_qtype, int kv_block,
+            int kv_scale_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int layout,
+            int causal, float softmax_scale, void* out, int out_dtype, void* stream) {
+  bool empty = false;
+  const int st = check_fwd(q_codes, q_scales, q_qtype, q_block, q_scale_dtype, k_codes, k_scales,
+                           k_qtype, v_codes, v_scales, v_qtype, kv_block, kv_scale_dtype, B, Hq,
+                           Hkv, Sq, Sk, D, layout, causal, softmax_scale, out, out_dtype, &empty);
+  if (st != QFA_OK || empty) return st;
   qfa::FwdArgs a{q_codes, q_scales, q_qtype, q_block, q_scale_dtype, k_codes, k_scales, k_qtype,
                  v_codes, v_scales, v_qtype, kv_block, kv_scale_dtype, B, Hq, Hkv, Sq, Sk, D,
                  layout, causal, softmax_scale, out, out_dtype};
   return from_hip(qfa::launch_fwd(a, (hipStream_t)stream));
+}
+
+size_t qfa_fwd_lowp_workspace_bytes(int B, int Hq, int Hkv, int Sq) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 1) return 0;
+  return qfa::fwd_lowp_workspace_bytes(B, Hq, Hkv, Sq);
+}
+
+int qfa_fwd_lowp(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
+                 int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
+                 const void* v_codes, const void* v_scales, int v_qtype, int kv_block,
+                 int kv_scale_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int layout,
+                 int causal, float softmax_scale, void* out, int out_dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  const int st = check_fwd(q_codes, q_scales, q_qtype, q_block, q_scale_dtype, k_codes, k_scales,
+                           k_qtype, v_codes, v_scales, v_qtype, kv_block, kv_scale_dtype, B, Hq,
+                           Hkv, Sq, Sk, D, layout, causal, softmax_scale, out, out_dtype, &empty);
+  if (st != QFA_OK || empty) return st;
+  // e4m3 Q/K/V with block scales: K/V blocks covering whole 64-key tiles.
+  if (q_qtype != QFA_FP8_E4M3 || kv_block % 64 != 0) return QFA_ERR_UNSUPPORTED;
+  const size_t need = qfa::fwd_lowp_workspace_bytes(B, Hq, Hkv, Sq);
+  if (!workspace || workspace_bytes < need) return QFA_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return QFA_ERR_UNSUPPORTED;
+  qfa::FwdArgs a{q_codes, q_scales, q_qtype, q_block, q_scale_dtype, k_codes, k_scales, k_qtype,
+                 v_codes, v_scales, v_qtype, kv_block, kv_scale_dtype, B, Hq, Hkv, Sq, Sk, D,
+                 layout, causal, softmax_scale, out, out_dtype};
+  return from_hip(qfa::launch_fwd_lowp(a, workspace, (hipStream_t)stream));
 }
 
 size_t qfa_decode_workspace_bytes(int B, int Hq, int S_max, int D) {

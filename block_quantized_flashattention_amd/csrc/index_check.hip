@@ -128,3 +128,22 @@ extern "C" __attribute__((visibility("default"))) long qfa_ixcheck_fwd(
   if (kinds) *kinds = rep.kinds;
   return rep.violations;
 }
+
+// The forward's work decomposition for a launch of this shape: for workgroup
+// `id`, out[0..3] = (batch, first query head, number of heads, first row) and
+// out[4] = rows per head. Returns the number of workgroups, or -1 for a shape
+// the forward does not take.
+extern "C" __attribute__((visibility("default"))) long qfa_ixcheck_fwd_item(
+    int B, int Hq, int Hkv, int Sq, int causal, int id, int* out) {
+  using namespace qfa::ix;
+  if (B < 1 || Hkv < 1 || Hq % Hkv || Sq < 1) return -1;
+  const FwdShape f = fwd_shape(B, Hq, Hkv, Sq, Sq, 128, false, false, false, 1, 1);
+  if (id < 0 || id >= f.grid) return f.grid;
+  const FwdItem it = fwd_item(id, B, Hkv, f.n_hg, f.n_rb, f.xcd_order, causal);
+  out[0] = it.b;
+  out[1] = fwd_head(it, f.group, f.hpw, 0);
+  out[2] = f.hpw;
+  out[3] = it.rb * f.rph;
+  out[4] = f.rph;
+  return f.grid;
+}

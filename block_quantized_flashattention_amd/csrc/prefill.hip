@@ -71,6 +71,15 @@ constexpr float kRescaleSlack = 12.0f;
 // With per-key scales the fp16 weight is p * sv_j / sv_ref <= p; the smaller
 // slack keeps the weights and their row sums well inside fp16.
 constexpr float kRescaleSlackTok = 8.0f;
+// fp8 P.V (e4m3 probabilities): a slack of 8 keeps them at most 256, below
+// the format's 448.
+constexpr float kRescaleSlackLp = 8.0f;
+// fp8 P.V accuracy gate: a row keeps its fp8 result when its effective number
+// of keys, bounded below by l^2 / S (S = sum over tiles of the tile's largest
+// probability times the tile's sum, at least sum p^2), is at least this.
+constexpr float kNeffMin = 256.0f;
+// Bytes per staged e4m3 V^T row (64 keys and 16 bytes of padding).
+constexpr int kV8Stride = 64 + 16;
 
 struct FwdParams {
   const uint8_t* q;
@@ -91,6 +100,10 @@ struct FwdParams {
   int out_dtype;
   float scale_log2;  // softmax_scale * log2(e)
   int xcd_order;     // 1: XCD-grouped workgroup order
+  // fp8 P.V pass: one byte per (workgroup, wavefront), 1 where a row failed
+  // the accuracy gate. fp16 pass: if set, a workgroup whose bytes are all 0
+  // exits at once (it recomputes only the items the fp8 pass flagged).
+  uint8_t* flags;
 };
 
 // LDS of one workgroup, as separate arrays so that the compiler can tell the
@@ -121,6 +134,14 @@ struct ScaleRing {
 __device__ __forceinline__ int vt_pos(int key) {
   const int g = key >> 4, a = (key >> 2) & 3, i = key & 3;
   return g * 16 + ((((a & 1) << 1) | (a >> 1)) << 2) + i;
+}
+
+// Byte position of key `key` (0..63) in a staged e4m3 V^T row for the fp8
+// P.V product: the 64 keys in the 32x32x64 operand's slot order, lane half h
+// (key bit 2) holding slots 32h + 16 kb + 4 ((key >> 3) & 3) + (key & 3) with
+// kb = key >> 5, the order in which a lane holds its scores.
+__device__ __forceinline__ int vt8_pos(int key) {
+  return 32 * ((key >> 2) & 1) + 16 * (key >> 5) + 4 * ((key >> 3) & 3) + (key & 3);
 }
 
 // Sign-extend eight packed two's-complement nibbles of `w` (element 2k in the
@@ -296,6 +317,27 @@ __device__ __forceinline__ void stage_v(_Float16* vbuf, const Stage<D, KQT, VQT>
   }
 }
 
+// e4m3 V^T for the fp8 P.V product: the raw codes of keys (2kp, 2kp+1),
+// which sit at adjacent positions, as one 2-byte write per channel.
+template <int D, int KQT, int VQT>
+__device__ __forceinline__ void stage_v8(uint8_t* vbuf, const Stage<D, KQT, VQT>& f) {
+  using S = Stage<D, KQT, VQT>;
+  static_assert(VQT == QFA_FP8_E4M3, "fp8 P.V takes e4m3 V");
+  const int tid = threadIdx.x;
+  const int kp = tid % 32, cg = tid / 32;
+  uint8_t* base = vbuf + (cg * S::kVCh) * kV8Stride + vt8_pos(2 * kp);
+#pragma unroll
+  for (int w = 0; w < S::kVSrc / 4; ++w) {
+    const uint32_t a = f.v[0][w], b = f.v[1][w];
+    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+    const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+    *(uint16_t*)(base + (4 * w + 0) * kV8Stride) = (uint16_t)lo;
+    *(uint16_t*)(base + (4 * w + 1) * kV8Stride) = (uint16_t)(lo >> 16);
+    *(uint16_t*)(base + (4 * w + 2) * kV8Stride) = (uint16_t)hi;
+    *(uint16_t*)(base + (4 * w + 3) * kV8Stride) = (uint16_t)(hi >> 16);
+  }
+}
+
 // Scales of one tile, handled by wavefront 0 (lane = key): loaded a tile
 // ahead, then written to the ring slot of the tile. With per-key scales the V
 // scales are divided by the running maximum V scale `vref` (carried by the
@@ -374,9 +416,12 @@ struct QK {
 // 8*(r/4) + 4*half + r%4.
 __device__ __forceinline__ constexpr int key_of(int kb, int r) { return kb * 32 + 8 * (r >> 2) + (r & 3); }
 
-template <int D, int KVM, bool CAUSAL, bool TOK>
+// LPV: P.V on the fp8 matrix unit (e4m3 V and probabilities, block scales
+// only), with the per-row accuracy gate written to p.flags.
+template <int D, int KVM, bool CAUSAL, bool TOK, bool LPV>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   constexpr bool FP8 = KVM == KV_F8_F8;
+  static_assert(!LPV || (FP8 && !TOK), "fp8 P.V: e4m3 V with block scales");
   constexpr int KQT = KVTypes<KVM>::K, VQT = KVTypes<KVM>::V;
   using T = QK<D, FP8>;
   using Op = typename T::Op;
@@ -385,7 +430,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   using G = Geo<D>;
   constexpr int kDB = D / 32;  // 32-channel blocks of the output
   constexpr int kNK = 2 * T::kSteps;  // K operand reads (and QK MFMAs) per tile
-  constexpr int kNV = 4 * kDB;        // V operand reads (and PV MFMAs) per tile
+  constexpr int kNV = LPV ? kDB : 4 * kDB;  // PV MFMAs per tile
+  constexpr int kVR = LPV ? 2 : 1;          // 16-byte V operand reads per PV MFMA
   // INT8 scores with one scale per tile: the integer accumulator starts at
   // the bit pattern kBiasBits of the float kBiasInt * 2^-26, so
   // 'kBiasBits + dot' is the bit pattern of the float (kBiasInt + dot) * 2^-26
@@ -397,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   constexpr uint32_t kBiasBits = 0x3E22F983u;
   constexpr int kBiasInt = 10680707;  // 2^23 + 0x22F983
   static_assert(D <= 128, "biased INT8 scores need |dot| < 2^21");
-  constexpr float kSlack = TOK ? kRescaleSlackTok : kRescaleSlack;
+  constexpr float kSlack = TOK ? kRescaleSlackTok : (LPV ? kRescaleSlackLp : kRescaleSlack);
 
   __shared__ __align__(16) uint8_t kbuf0[G::kKBytes];
   __shared__ __align__(16) uint8_t kbuf1[G::kKBytes];
@@ -412,6 +458,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   const int grp = wave >> 2;   // 0: group A, 1: group B
   const int half = lane >> 5;  // lane half: keys 4*half + {0..3} of every 8
   const int col = lane & 31;   // query row of this lane within the wavefront
+
+  // fp16 pass after an fp8 P.V pass: only the flagged work items.
+  if constexpr (!LPV) {
+    if (p.flags && *(const uint64_t*)(p.flags + (long)blockIdx.x * kWaves) == 0) return;
+  }
 
   // Work item: (batch, KV head, head group, row block).
   const ix::FwdItem it = ix::fwd_item(blockIdx.x, p.B, p.Hkv, p.n_hg, p.n_rb, p.xcd_order, CAUSAL);
@@ -452,6 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   for (int i = 0; i < kDB; ++i) o[i] = (f32x16){};
   float m_run = -INFINITY;  // reference row max (log2 units)
   float l_run = 0.0f;       // row sum of this lane half, in units of exp2(-m_run)
+  float s_run = 0.0f;       // (fp8 P.V) sum over tiles of max p times the tile's sum, units exp2(-2 m_run)
   float sv_cur = 0.0f;      // V scale O is expressed in
   float vref_run = 0.0f;    // (wavefront 0, per-key scales) running max V scale
 
@@ -464,6 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 
   Acc sacc[2];
   f16x8 pb[2][2];  // P^T operand: [32-key block][16-key half]
+  uint32_t pb8[8];  // fp8 P.V: the P^T operand, 32 e4m3 probabilities (slot 4w + byte)
   St pf;
   ScaleRegs sr;
   // Uniform scales of the tile whose softmax comes next, read during the
@@ -486,20 +539,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     // pinned with scheduling fences so that each read has several matrix
     // instructions' time to arrive.
     constexpr int kKR = FP8 ? 2 : 1;              // reads per QK instruction
-    constexpr int kNR = kKR * kNK + (PV ? kNV : 0);
+    constexpr int kNR = kKR * kNK + (PV ? kVR * kNV : 0);
     constexpr int kNM = kNK + (PV ? kNV : 0);
     constexpr int kDepth = 8;
     tile_ks = sc.ks[t % kScaleRing][0];
     tile_vref = sc.vref[t % kScaleRing];
     const uint8_t* kaddr = kb + col * G::kKStride + half * T::kSlice;
     const _Float16* vaddr = vb + col * G::kVStride + half * 8;
+    const uint8_t* vaddr8 = (const uint8_t*)vb + col * kV8Stride + half * 32;
     // P.V comes first, so that the probabilities are dead before the new
     // scores are written (the two can share registers). Read r: V operands
     // (16-key group-major), then K operands in MFMA order (step-major, the
     // two 32-key blocks interleaved).
-    constexpr int kNVR = PV ? kNV : 0;
+    constexpr int kNVM = PV ? kNV : 0;    // PV instructions
+    constexpr int kNVR = kVR * kNVM;      // their reads
     auto rd = [&](int r) __attribute__((always_inline)) -> i32x4 {
       if (r < kNVR) {
+        if constexpr (LPV) {
+          // rows of 32 channels, lane half h: bytes [32h, 32h + 32)
+          const int db = r / 2, part = r % 2;
+          return *(const i32x4*)(vaddr8 + db * 32 * kV8Stride + part * 16);
+        }
         const int g = r / kDB, db = r % kDB;
         return *(const i32x4*)(vaddr + db * 32 * G::kVStride + g * 16);
       }
@@ -512,18 +572,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     for (int r = 0; r < kDepth; ++r) ring[r] = rd(r);
     __builtin_amdgcn_sched_barrier(0);
     // Reads consumed by instructions 0..m.
-    auto consumed = [](int m) constexpr { return m < kNVR ? m + 1 : kNVR + (m + 1 - kNVR) * kKR; };
+    auto consumed = [](int m) constexpr {
+      return m < kNVM ? (m + 1) * kVR : kNVR + (m + 1 - kNVM) * kKR;
+    };
 #pragma unroll
     for (int m = 0; m < kNM; ++m) {
-      const int r0 = m < kNVR ? m : kNVR + (m - kNVR) * kKR;  // first read of this instruction
-      if (m < kNVR) {
-        if constexpr (PV) {
+      // first read of this instruction
+      const int r0 = m < kNVM ? m * kVR : kNVR + (m - kNVM) * kKR;
+      if (m < kNVM) {
+        if constexpr (PV && LPV) {
+          const i32x4 lo = ring[r0 % kDepth], hi = ring[(r0 + 1) % kDepth];
+          const i32x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const i32x8 pa = {(int)pb8[0], (int)pb8[1], (int)pb8[2], (int)pb8[3],
+                            (int)pb8[4], (int)pb8[5], (int)pb8[6], (int)pb8[7]};
+          o[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pa, o[m], 0, 0, 0, 0, 0, 0);
+        } else if constexpr (PV) {
           const int g = m / kDB, db = m % kDB;
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, ring[r0 % kDepth]),
                                                          pb[g >> 1][g & 1], o[db], 0, 0, 0);
         }
       } else {
-        const int s = (m - kNVR) / 2, kb2 = (m - kNVR) % 2;
+        const int s = (m - kNVM) / 2, kb2 = (m - kNVM) % 2;
         Op a;
         if constexpr (FP8) {
           const i32x4 lo = ring[r0 % kDepth], hi = ring[(r0 + 1) % kDepth];
@@ -548,7 +617,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     // Staging of the next tiles and their loads; the compiler may interleave
     // this vector work with the last matrix instructions.
     stage_k<D, KQT, VQT>(kst, pf);
-    stage_v<D, KQT, VQT>(vst, pf, TOK ? sc.vs[t % kScaleRing] : nullptr);
+    if constexpr (LPV) stage_v8<D, KQT, VQT>((uint8_t*)vst, pf);
+    else stage_v<D, KQT, VQT>(vst, pf, TOK ? sc.vs[t % kScaleRing] : nullptr);
     if (wave == 0) stage_scales<TOK, kBiasAcc>(sc, (t + 1) % kScaleRing, sr, p.kv_scale_f16, vref_run);
     fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, tile_n0(t + 2), tile_n0(t + 1));
     if (wave == 0) fetch_scales(sr, p, sbase, tile_n0(t + 2), TOK);
@@ -599,6 +669,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         const float sv_new = sv_t > 0.0f ? sv_t : (sv_cur > 0.0f ? sv_cur : 1.0f);
         const float f = sv_cur > 0.0f ? alpha * (sv_cur / sv_new) : 0.0f;
         l_run *= alpha;
+        if constexpr (LPV) s_run *= alpha * alpha;
 #pragma unroll
         for (int i = 0; i < kDB; ++i) o[i] *= f;
         m_run = m_new;
@@ -611,6 +682,39 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         // into the subtrahend (one rounding, below one unit of dot).
         msub = __builtin_fmaf(-(float)kBiasInt, ck, msub);
         c = ck * 67108864.0f;
+      }
+      if constexpr (LPV) {
+        // e4m3 probabilities in operand slot order (slot 16 kb + r); the row
+        // sum from the unrounded values. Gate statistic: the lane half's keys
+        // fall into four classes (r % 4) of 8; the sum over classes of the
+        // class's largest probability times its sum bounds sum p^2.
+        float lt[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][r], c, msub));
+            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb][r + 1], c, msub));
+            if constexpr (MASK && !CAUSAL) {
+              if (key_of(kb, r) > lim) p0 = 0.0f;
+              if (key_of(kb, r + 1) > lim) p1 = 0.0f;
+            }
+            lt[r & 3] += p0;
+            lt[(r + 1) & 3] += p1;
+            const int slot = 16 * kb + r;
+            if (slot & 2) pb8[slot >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb8[slot >> 2], true);
+            else pb8[slot >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pb8[slot >> 2], false);
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // mc[i] is the class's largest score (before the scale), masked
+          // keys included only as -inf
+          const float pm = mc[i] == -INFINITY ? 0.0f
+                                              : __builtin_amdgcn_exp2f(__builtin_fmaf(mc[i], c, msub));
+          s_run = __builtin_fmaf(pm, lt[i], s_run);
+        }
+        l_run += (lt[0] + lt[1]) + (lt[2] + lt[3]);
+        return;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -706,6 +810,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // K_1, V_0 and the scales of tile 1 in registers.
 #pragma unroll
   for (int i = 0; i < 2; ++i) pb[i][0] = pb[i][1] = (f16x8){};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pb8[i] = 0;
   fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, 0, 0);
   if (wave == 0) fetch_scales(sr, p, sbase, 0, TOK);
   for (int i = tid; i < G::kVElems / 8; i += kThreads) ((uint4*)vbuf1)[i] = make_uint4(0, 0, 0, 0);
@@ -739,6 +845,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 
   // Epilogue: lane holds row qrow, channels 32*db + 8*(r/4) + 4*half + (r%4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if constexpr (LPV) {
+    // Accuracy gate: flag the work item when a row's effective number of
+    // keys may be below kNeffMin (its fp16 pass then recomputes the item).
+    const float s_tot = s_run + __shfl_xor(s_run, 32);
+    const bool fail = qvalid && !(l_tot * l_tot >= kNeffMin * s_tot);
+    const bool any = __builtin_amdgcn_ballot_w64(fail) != 0;
+    if (lane == 0) p.flags[(long)blockIdx.x * kWaves + wave] = any ? 1 : 0;
+  }
   const float inv = sv_cur / l_tot;
   const long hbase = (long)b * p.o_batch + (long)h * p.o_head;
   if (p.out_dtype != QFA_F32) {
@@ -794,13 +908,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 template <int D, int KVM>
 hipError_t launch_kv(const FwdParams& p, int grid, bool causal, bool tok, hipStream_t st) {
   if (causal) {
-    if (tok) fwd_kernel<D, KVM, true, true><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, KVM, true, false><<<grid, kThreads, 0, st>>>(p);
+    if (tok) fwd_kernel<D, KVM, true, true, false><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, true, false, false><<<grid, kThreads, 0, st>>>(p);
   } else {
-    if (tok) fwd_kernel<D, KVM, false, true><<<grid, kThreads, 0, st>>>(p);
-    else fwd_kernel<D, KVM, false, false><<<grid, kThreads, 0, st>>>(p);
+    if (tok) fwd_kernel<D, KVM, false, true, false><<<grid, kThreads, 0, st>>>(p);
+    else fwd_kernel<D, KVM, false, false, false><<<grid, kThreads, 0, st>>>(p);
   }
   return hipGetLastError();
+}
+
+// fp8 P.V pass (writes every work item's flags), then the fp16 pass over the
+// flagged items only.
+template <int D>
+hipError_t launch_lowp(const FwdParams& p, int grid, bool causal, hipStream_t st) {
+  if (causal) fwd_kernel<D, KV_F8_F8, true, false, true><<<grid, kThreads, 0, st>>>(p);
+  else fwd_kernel<D, KV_F8_F8, false, false, true><<<grid, kThreads, 0, st>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_kv<D, KV_F8_F8>(p, grid, causal, false, st);
 }
 
 template <int D>
@@ -816,8 +941,8 @@ hipError_t launch_d(const FwdParams& p, int kvm, int grid, bool causal, bool tok
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  FwdParams p;
+// Kernel parameters of one forward call (shape checked by the C ABI).
+static void fwd_params(const FwdArgs& a, FwdParams& p, ix::FwdShape& f) {
   p.q = (const uint8_t*)a.q;
   p.qs = a.qs;
   p.k = (const uint8_t*)a.k;
@@ -830,9 +955,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.Sq = a.Sq;
   p.Sk = a.Sk;
-  const ix::FwdShape f = ix::fwd_shape(a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.D, a.layout == QFA_BSND,
-                                        a.k_qtype == QFA_INT4, a.v_qtype == QFA_INT4, a.q_block,
-                                        a.kv_block);
+  f = ix::fwd_shape(a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.D, a.layout == QFA_BSND, a.k_qtype == QFA_INT4,
+                    a.v_qtype == QFA_INT4, a.q_block, a.kv_block);
   p.group = f.group;
   p.hpw = f.hpw;
   p.rph = f.rph;
@@ -851,6 +975,13 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   p.out_dtype = a.out_dtype;
   p.scale_log2 = a.softmax_scale * kLog2e;
   p.xcd_order = f.xcd_order;
+  p.flags = nullptr;
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  FwdParams p;
+  ix::FwdShape f;
+  fwd_params(a, p, f);
   const long grid = f.grid;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   // Per-key scales unless every tile lies inside one scale block.
@@ -863,6 +994,23 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   if (kvm < 0) return hipErrorInvalidValue;
   if (a.D == 64) return launch_d<64>(p, kvm, (int)grid, a.causal, tok, stream);
   return launch_d<128>(p, kvm, (int)grid, a.causal, tok, stream);
+}
+
+size_t fwd_lowp_workspace_bytes(int B, int Hq, int Hkv, int Sq) {
+  const ix::FwdShape f = ix::fwd_shape(B, Hq, Hkv, Sq, 1, 128, false, false, false, 1, 1);
+  return (size_t)f.grid * kWaves;
+}
+
+hipError_t launch_fwd_lowp(const FwdArgs& a, void* flags, hipStream_t stream) {
+  FwdParams p;
+  ix::FwdShape f;
+  fwd_params(a, p, f);
+  if (f.grid > 0x7FFFFFFF || f.per_key || a.q_qtype != QFA_FP8_E4M3 ||
+      a.k_qtype != QFA_FP8_E4M3 || a.v_qtype != QFA_FP8_E4M3)
+    return hipErrorInvalidValue;
+  p.flags = (uint8_t*)flags;
+  if (a.D == 64) return launch_lowp<64>(p, (int)f.grid, a.causal, stream);
+  return launch_lowp<128>(p, (int)f.grid, a.causal, stream);
 }
 
 }  // namespace qfa

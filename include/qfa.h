@@ -217,6 +217,47 @@ QFA_API int qfa_fwd(const void* q_codes, const void* q_scales, int q_qtype, int 
             int causal, float softmax_scale, void* out, int out_dtype, void* stream);
 
 /*
+ * qfa_fwd_lowp_workspace_bytes -- bytes of device workspace qfa_fwd_lowp needs
+ * for these sizes (one flag byte per work item and wavefront). Returns 0 for
+ * invalid sizes.
+ */
+QFA_API size_t qfa_fwd_lowp_workspace_bytes(int B, int Hq, int Hkv, int Sq);
+
+/*
+ * qfa_fwd_lowp -- qfa_fwd with the P.V product on the fp8 matrix unit, for
+ * e4m3 Q/K/V ([MindIE-SD] FA quantization, "FP8 Attention": the attention is
+ * computed in the FP8 domain). The probabilities are rounded to e4m3 and
+ * multiplied with the e4m3 V codes at twice the fp16 rate; the softmax, its
+ * row sums and the V scales stay in fp32.
+ *
+ * Accuracy gate: rounding each probability to e4m3 (relative error at most
+ * 2^-4) perturbs a row's output by about 0.03 * sqrt(sum p^2) / sum p times the
+ * spread of its V values, which is small only when many keys carry the row.
+ * Each row bounds its effective number of keys (sum p)^2 / sum p^2 from below
+ * by l^2 / S, S = the sum over 64-key tiles of the tile's largest probability
+ * times the tile's sum; a row with l^2 / S < 256 ("peaky": a few keys
+ * dominate) flags its work item, and a second pass recomputes the flagged
+ * work items exactly as qfa_fwd does (fp16 P.V) over the first pass's output.
+ * The output of a flagged work item is therefore bit-identical to qfa_fwd's.
+ *
+ * Arguments as qfa_fwd, plus
+ *   workspace  device buffer of at least qfa_fwd_lowp_workspace_bytes(B,Hq,Hkv,Sq)
+ *              bytes, 8-byte aligned, owned by the caller; on return (after the
+ *              stream has run the call) byte 8*w + v is 1 when wavefront v of work
+ *              item w fell back to the fp16 product, else 0. Every byte is written.
+ * Supported: q, k and v all FP8_E4M3 with kv_block a multiple of 64 (block
+ * scales); other code types or per-key scales return QFA_ERR_UNSUPPORTED, a
+ * missing or short workspace QFA_ERR_WORKSPACE. Calls that share a workspace
+ * must not overlap.
+ */
+QFA_API int qfa_fwd_lowp(const void* q_codes, const void* q_scales, int q_qtype, int q_block,
+                 int q_scale_dtype, const void* k_codes, const void* k_scales, int k_qtype,
+                 const void* v_codes, const void* v_scales, int v_qtype, int kv_block,
+                 int kv_scale_dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int layout,
+                 int causal, float softmax_scale, void* out, int out_dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
  * qfa_decode_workspace_bytes -- bytes of device workspace qfa_decode needs for
  * these sizes (split-K partial results). Returns 0 for invalid sizes.
  */

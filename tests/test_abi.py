@@ -24,7 +24,7 @@ def test_exports_every_declared_function(L):
     names = qfa.header_functions()
     assert set(names) == {"qfa_version", "qfa_status_string", "qfa_block_quant",
                           "qfa_block_quant_multi", "qfa_rotate_block_quant", "qfa_kv_append",
-                          "qfa_fwd",
+                          "qfa_fwd", "qfa_fwd_lowp", "qfa_fwd_lowp_workspace_bytes",
                           "qfa_decode_workspace_bytes", "qfa_decode",
                           "qfa_decode_noalloc_max_bytes", "qfa_decode_noalloc"}
     for n in names:
@@ -207,3 +207,34 @@ def test_decode_noalloc_validation(L):
     assert dec_na(L, B=32, Hq=32, Hkv=32, S_max=16384) == SCRATCH
     assert dec_na(L, B=32, Hq=32, Hkv=32, S_max=16384, lens=None) == NULL  # validation first
     assert L.qfa_status_string(SCRATCH) != b"unknown status"
+
+
+def fwd_lp(L, ws=P, wsb=1 << 20, **kw):
+    args = dict(q=P, qs=P, qqt=F8, qb=128, qsd=F32, k=P, ks=P, kqt=F8, v=P, vs=P, vqt=F8, kb=256,
+                ksd=F32, B=1, Hq=4, Hkv=2, Sq=300, Sk=300, D=128, layout=BNSD, causal=0, scale=0.1,
+                out=P, odt=F16)
+    args.update(kw)
+    a = args
+    return L.qfa_fwd_lowp(a["q"], a["qs"], a["qqt"], a["qb"], a["qsd"], a["k"], a["ks"], a["kqt"],
+                          a["v"], a["vs"], a["vqt"], a["kb"], a["ksd"], a["B"], a["Hq"], a["Hkv"],
+                          a["Sq"], a["Sk"], a["D"], a["layout"], a["causal"],
+                          ctypes.c_float(a["scale"]), a["out"], a["odt"], ws, wsb, None)
+
+
+def test_fwd_lowp_validation(L):
+    """fp8 P.V: e4m3 Q/K/V with block scales only, a workspace of one byte per
+    work item and wavefront; validated like qfa_fwd before any device call."""
+    need = L.qfa_fwd_lowp_workspace_bytes(1, 4, 2, 300)
+    # 2 KV heads x group 2 (both heads of a group in one workgroup: 128 rows
+    # each) x ceil(300 / 128) row blocks, 8 bytes each
+    assert need == 2 * 3 * 8
+    assert L.qfa_fwd_lowp_workspace_bytes(1, 3, 2, 300) == 0
+    assert fwd_lp(L, qqt=I8, kqt=I8, vqt=I8) == UNSUP
+    assert fwd_lp(L, kb=100) == UNSUP                  # per-key scales
+    assert fwd_lp(L, ws=None) == WS
+    assert fwd_lp(L, wsb=need - 1) == WS
+    assert fwd_lp(L, ws=ctypes.c_void_p(260), wsb=need) == UNSUP  # 8-byte alignment
+    assert fwd_lp(L, qqt=5) == ENUM
+    assert fwd_lp(L, Hq=3) == SHAPE
+    assert fwd_lp(L, v=None) == NULL
+    assert fwd_lp(L, Sq=0, Sk=0, q=None, k=None, v=None, out=None, ws=None) == OK
