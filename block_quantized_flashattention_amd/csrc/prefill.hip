@@ -36,23 +36,32 @@
 //     integer accumulator started at a bit pattern that makes the sum a float
 //     (see kBiasBits), and each probability costs one FMA and one exp2. O is
 //     kept in units of the current V block scale and rescaled when it
-//     changes. With per-key scales (INT4 K/V, one scale per token) each score
-//     takes one more multiply, the fp16 weights are p * sv_j / sv_ref with
-//     sv_ref the running maximum V scale (so every weight stays <= 2^slack
-//     whatever the scales' magnitude), and O is kept in units of sv_ref.
+//     changes. With per-key scales (INT4 K/V, one scale per token) the score
+//     is still one FMA, with per-key constants staged beside the tile
+//     (a_j = sk_j 2^26, b_j = -sk_j kBiasInt), and the V scale goes into the
+//     staged V: code * sv_j / sv_ref in fp16, sv_ref the running maximum V
+//     scale, so O is kept in units of sv_ref.
 //   * The running row max is raised only when a tile's max exceeds it by more
 //     than the slack (log2 units), so the O rescale is skipped on most tiles;
 //     the probabilities stay below 2^slack (exact softmax; fp16 holds them
 //     with its full precision).
 //   * Row sums add the fp16-rounded probabilities with v_dot2_f32_f16, i.e.
 //     exactly the weights the P.V product uses.
-//   * Causal: tiles past the workgroup's last row are never loaded; a
-//     wavefront skips tiles above its rows; the mask is a compile-time
-//     variant used only on tiles that cross a wavefront's diagonal or the
-//     end of the keys. Work is ordered longest first.
+//   * Causal: tiles past the workgroup's last row are never loaded (the
+//     workgroup's wavefronts walk its tiles together; one whose rows all lie
+//     above a tile masks all of its keys); the mask is a compile-time variant
+//     used only on tiles that cross a wavefront's diagonal or the end of the
+//     keys. Work is ordered longest first.
 //   * XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
 //     all work of one (batch, KV head) runs on one XCD and its K/V codes stay
 //     in that XCD's L2.
+//   * fp8 P.V variant (e4m3 Q/K/V with block scales, qfa_fwd_lowp): V is
+//     staged as raw e4m3 bytes in the operand's key order and the
+//     probabilities are rounded to e4m3, one v_mfma_scale_f32_32x32x64_f8f6f4
+//     per 32-channel block per tile. Each row also accumulates a bound on
+//     sum p^2; a row with too few effective keys flags its work item, and the
+//     fp16 kernel, launched again with those flags, recomputes exactly the
+//     flagged items.
 #include <type_traits>
 
 #include "qfa_device.h"
