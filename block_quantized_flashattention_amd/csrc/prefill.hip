@@ -22,9 +22,11 @@
 //     two wavefronts of a SIMD happen to be in the same kind of work.
 //   * The matrix-phase group also stages the next K and V tiles: codes are
 //     loaded into registers two phases ahead and written to LDS (K as bytes,
-//     INT4 widened to INT8; V transposed and converted exactly to fp16), and
-//     the next tiles' loads are issued; its vector instructions fill the
-//     issue slots between its matrix instructions.
+//     INT4 as the offset codes code + 8 with the Q channels permuted to match
+//     and the offset's share of the dot product taken off the accumulator's
+//     start value; V transposed and converted exactly to fp16), and the next
+//     tiles' loads are issued. The matrix-phase wavefront runs at a raised
+//     issue priority.
 //   * Scores are formed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_32x32x32_i8 (INT8 Q/K; INT4 K widened) or
 //     v_mfma_f32_32x32x64_f8f6f4 (FP8 e4m3 Q/K). Each lane then holds one
@@ -153,16 +155,24 @@ __device__ __forceinline__ int vt8_pos(int key) {
   return 32 * ((key >> 2) & 1) + 16 * (key >> 5) + 4 * ((key >> 3) & 3) + (key & 3);
 }
 
-// Sign-extend eight packed two's-complement nibbles of `w` (element 2k in the
-// low nibble of byte k) into eight int8 bytes, returned as two dwords.
-__device__ __forceinline__ uint2 unpack_int4x8(uint32_t w) {
-  uint32_t lo = w & 0x0F0F0F0Fu;         // elements 0,2,4,6
-  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // elements 1,3,5,7
-  lo |= (lo & 0x08080808u) * 0x1Eu;      // copy bit 3 into bits 4..7
-  hi |= (hi & 0x08080808u) * 0x1Eu;
-  const uint32_t o0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-  const uint32_t o1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-  return make_uint2(o0, o1);
+// Eight packed two's-complement nibbles of `w` (element 2k in the low nibble
+// of byte k) as offset bytes, code + 8 in 0..15 (the nibble with its sign bit
+// flipped): elements 0, 2, 4, 6 in the first dword, 1, 3, 5, 7 in the second.
+// Staged K channels are therefore in the order [0 2 4 6 1 3 5 7] within every
+// group of 8; the Q operand is permuted the same way (q_k4_order), and the
+// offset adds 8 * sum(Q codes) to each dot product, which the accumulator's
+// start value takes off again.
+__device__ __forceinline__ uint2 unpack_int4x8_offset(uint32_t w) {
+  const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;
+  const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+  return make_uint2(lo, hi);
+}
+
+// Q bytes of every group of 8 channels put in the order [0 2 4 6 1 3 5 7].
+__device__ __forceinline__ i32x4 q_k4_order(i32x4 q) {
+  const uint32_t a0 = q[0], a1 = q[1], b0 = q[2], b1 = q[3];
+  return (i32x4){(int)__builtin_amdgcn_perm(a1, a0, 0x06040200u), (int)__builtin_amdgcn_perm(a1, a0, 0x07050301u),
+                 (int)__builtin_amdgcn_perm(b1, b0, 0x06040200u), (int)__builtin_amdgcn_perm(b1, b0, 0x07050301u)};
 }
 
 // Bytes 0 and 1 of `u` (signed codes) as an exact fp16 pair: the byte with
@@ -246,10 +256,10 @@ __device__ __forceinline__ void stage_k(uint8_t* kbuf, const Stage<D, KQT, VQT>&
   uint8_t* dst = kbuf + (tid / 8) * Geo<D>::kKStride + (tid % 8) * (D / 8);
   if constexpr (KQT == QFA_INT4) {
     if constexpr (D == 128) {
-      const uint2 a = unpack_int4x8(f.k[0]), b = unpack_int4x8(f.k[1]);
+      const uint2 a = unpack_int4x8_offset(f.k[0]), b = unpack_int4x8_offset(f.k[1]);
       *(uint4*)dst = make_uint4(a.x, a.y, b.x, b.y);
     } else {
-      const uint2 a = unpack_int4x8(f.k[0]);
+      const uint2 a = unpack_int4x8_offset(f.k[0]);
       *(uint2*)dst = a;
     }
   } else if constexpr (D == 128) {
@@ -370,6 +380,25 @@ __device__ __forceinline__ void fetch_scales(ScaleRegs& r, const FwdParams& p, l
   r.vhi = ((const uint16_t*)p.vs)[i1];
 }
 
+// Largest value of v over the wavefront, in every lane: DPP exchanges inside
+// each row of 16 lanes (lane i ^ 1, i ^ 2, then the mirrored lane of its 8 and
+// of its 16), then the four row results read as scalars. No LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // With per-key scales each key gets the two constants of its score,
 // y_j = sk_j * dot_j = fma(x_j, a_j, b_j), where x_j is the accumulator read
 // as a float: for biased INT8 scores x = (kBiasInt + dot) 2^-26, so
@@ -384,11 +413,10 @@ __device__ __forceinline__ void stage_scales(ScaleRing& sm, int slot, const Scal
   if constexpr (TOK) {
     sm.ks[slot][lane] = BIAS ? ks * 67108864.0f : ks;
     sm.kb[slot][lane] = BIAS ? -ks * 10680707.0f : 0.0f;
-    float m = vs;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    vref_run = fmaxf(vref_run, m);
-    sm.vs[slot][lane] = vref_run > 0.0f ? vs / vref_run : 0.0f;
+    vref_run = fmaxf(vref_run, wave_max(vs));
+    // The ratio goes into fp16 (the staged V), so the hardware reciprocal
+    // (1 ulp) is ample.
+    sm.vs[slot][lane] = vref_run > 0.0f ? vs * __builtin_amdgcn_rcpf(vref_run) : 0.0f;
     if (lane == 0) sm.vref[slot] = vref_run;
   } else {
     sm.ks[slot][lane] = ks;
@@ -432,6 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   constexpr bool FP8 = KVM == KV_F8_F8;
   static_assert(!LPV || (FP8 && !TOK), "fp8 P.V: e4m3 V with block scales");
   constexpr int KQT = KVTypes<KVM>::K, VQT = KVTypes<KVM>::V;
+  constexpr bool kK4 = KQT == QFA_INT4;  // K staged as offset codes (unpack_int4x8_offset)
   using T = QK<D, FP8>;
   using Op = typename T::Op;
   using Acc = typename T::Acc;
@@ -490,6 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     for (int s = 0; s < T::kSteps; ++s) {
       qop[s] = T::load(qp + s * 2 * T::kSlice + half * T::kSlice);
       if (!qvalid) qop[s] = (Op){};
+      if constexpr (kK4) qop[s] = q_k4_order(qop[s]);
     }
   }
   const float sq = load_scale(p.qs, ((long)b * p.Hq + h) * p.nqblk + ix::fwd_read_row(qrow, p.Sq) / p.q_block,
@@ -502,9 +532,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 
   // The accumulator start of the biased INT8 scores, kept in registers (an
   // opaque copy, so the compiler does not rebuild the splat for every use).
+  // With offset INT4 K codes the start value also takes off 8 * (sum of the
+  // row's Q codes over both lane halves).
+  int bias0 = (int)kBiasBits;
+  if constexpr (kK4) {
+    int qsum = 0;
+#pragma unroll
+    for (int s = 0; s < T::kSteps; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qsum = __builtin_amdgcn_sdot4(qop[s][i], 0x01010101, qsum, false);
+    qsum += __shfl_xor(qsum, 32);
+    bias0 -= 8 * qsum;
+  }
   i32x16 bias_acc;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) bias_acc[i] = (int)kBiasBits;
+  for (int i = 0; i < 16; ++i) bias_acc[i] = bias0;
   if constexpr (kBiasAcc) asm volatile("" : "+v"(bias_acc));
 
   f32x16 o[kDB];
@@ -843,8 +885,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
       const int tt = j >> 1;
       if ((j & 1) == 0) {
         const bool odd = tt & 1;
+        // The matrix-phase wavefront issues ahead of the softmax wavefront
+        // sharing its SIMD: its matrix instructions are the longer chain.
+        __builtin_amdgcn_s_setprio(1);
         mphase(tt, odd ? kbuf1 : kbuf0, odd ? vbuf0 : vbuf1, odd ? kbuf0 : kbuf1,
                odd ? vbuf1 : vbuf0, std::true_type());
+        __builtin_amdgcn_s_setprio(0);
       } else {
         vphase(tt);
       }
