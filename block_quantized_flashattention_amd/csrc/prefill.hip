@@ -38,9 +38,10 @@
 //     integer accumulator started at a bit pattern that makes the sum a float
 //     (see kBiasBits), and each probability costs one FMA and one exp2. O is
 //     kept in units of the current V block scale and rescaled when it
-//     changes. With per-key scales (INT4 K/V, one scale per token) the score
-//     is still one FMA, with per-key constants staged beside the tile
-//     (a_j = sk_j 2^26, b_j = -sk_j kBiasInt), and the V scale goes into the
+//     changes. With per-key scales (INT4 K/V, one scale per token) the
+//     integer dot product is converted and multiplied by the key's scale
+//     (staged beside the tile; each lane loads its 32 keys' scales into
+//     registers at the end of its matrix phase), and the V scale goes into the
 //     staged V: code * sv_j / sv_ref in fp16, sv_ref the running maximum V
 //     scale, so O is kept in units of sv_ref.
 //   * The running row max is raised only when a tile's max exceeds it by more
@@ -134,8 +135,7 @@ struct Geo {
   static constexpr int kOutStride = D + 8;
 };
 struct ScaleRing {
-  float ks[kScaleRing][kBN];   // per key: K scale (times 2^26 for biased INT8 scores)
-  float kb[kScaleRing][kBN];   // per key: offset removing the INT8 score bias
+  float ks[kScaleRing][kBN];   // per key: K scale
   float vs[kScaleRing][kBN];   // per key: V scale / running maximum V scale
   float vref[kScaleRing];      // the V scale O is expressed in
 };
@@ -399,20 +399,17 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// With per-key scales each key gets the two constants of its score,
-// y_j = sk_j * dot_j = fma(x_j, a_j, b_j), where x_j is the accumulator read
-// as a float: for biased INT8 scores x = (kBiasInt + dot) 2^-26, so
-// a_j = sk_j 2^26 and b_j = -sk_j kBiasInt (one rounding, below one unit of
-// dot); for FP8 scores a_j = sk_j, b_j = 0.
-template <bool TOK, bool BIAS>
+// With per-key scales each key's K scale is staged (the score is the dot
+// product times it) and its V scale as the ratio to the running maximum V
+// scale; with block scales the tile's K scale and V scale.
+template <bool TOK>
 __device__ __forceinline__ void stage_scales(ScaleRing& sm, int slot, const ScaleRegs& r,
                                              bool f16, float& vref_run) {
   const int lane = threadIdx.x & 63;
   const float ks = f16 ? f16_bits_to_f32(r.klo) : __uint_as_float(r.klo | (r.khi << 16));
   const float vs = f16 ? f16_bits_to_f32(r.vlo) : __uint_as_float(r.vlo | (r.vhi << 16));
   if constexpr (TOK) {
-    sm.ks[slot][lane] = BIAS ? ks * 67108864.0f : ks;
-    sm.kb[slot][lane] = BIAS ? -ks * 10680707.0f : 0.0f;
+    sm.ks[slot][lane] = ks;
     vref_run = fmaxf(vref_run, wave_max(vs));
     // The ratio goes into fp16 (the staged V), so the hardware reciprocal
     // (1 ulp) is ample.
@@ -476,8 +473,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // exactly as long as the sum stays in that binade, i.e.
   // -2292099 <= dot < 6096509, which any 8-bit codes with D <= 128 satisfy
   // (|dot| <= 128 * 128 * 128). The scores then need no integer-to-float
-  // conversion, and their max is a float max.
-  constexpr bool kBiasAcc = !FP8;
+  // conversion, and their max is a float max. With per-key scales each score
+  // is multiplied by its key's scale anyway, and the integer dot product is
+  // converted (exactly) instead: one constant per key instead of two.
+  constexpr bool kBiasAcc = !FP8 && !TOK;
+  // INT8 products start from bias_acc (the float bias and/or the INT4 K
+  // offset correction); otherwise from zero.
+  constexpr bool kStartAcc = kBiasAcc || kK4;
   constexpr uint32_t kBiasBits = 0x3E22F983u;
   constexpr int kBiasInt = 10680707;  // 2^23 + 0x22F983
   static_assert(D <= 128, "biased INT8 scores need |dot| < 2^21");
@@ -530,11 +532,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   const uint8_t* vbase = p.v + (long)b * p.v_batch + (long)kvh * p.v_head;
   const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
 
-  // The accumulator start of the biased INT8 scores, kept in registers (an
-  // opaque copy, so the compiler does not rebuild the splat for every use).
-  // With offset INT4 K codes the start value also takes off 8 * (sum of the
-  // row's Q codes over both lane halves).
-  int bias0 = (int)kBiasBits;
+  // The accumulator start of the INT8 scores, kept in registers (an opaque
+  // copy, so the compiler does not rebuild the splat for every use): the
+  // float bias with block scales, and with offset INT4 K codes minus
+  // 8 * (sum of the row's Q codes over both lane halves).
+  int bias0 = kBiasAcc ? (int)kBiasBits : 0;
   if constexpr (kK4) {
     int qsum = 0;
 #pragma unroll
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   i32x16 bias_acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) bias_acc[i] = bias0;
-  if constexpr (kBiasAcc) asm volatile("" : "+v"(bias_acc));
+  if constexpr (kStartAcc) asm volatile("" : "+v"(bias_acc));
 
   f32x16 o[kDB];
 #pragma unroll
@@ -574,6 +576,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // preceding matrix phase (a read at the start of the softmax phase would
   // queue behind the other group's operand reads).
   float tile_ks = 0.0f, tile_vref = 0.0f;
+  // K scales of this lane's 32 keys of that tile (per-key scales), read at
+  // the end of the matrix phase: read in the softmax phase they would wait
+  // behind the other group's operand reads.
+  f32x4 key_s[2][4];
 
   // Matrix phase for tile index t, with K_t in kb and V_{t-1} in vb (PV when
   // the template flag says so): operand reads, the staging of the registers
@@ -652,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
           a = ring[r0 % kDepth];
         }
         if (s == 0) {
-          if constexpr (kBiasAcc) sacc[kb2] = T::mma(a, qop[0], bias_acc);
+          if constexpr (kStartAcc) sacc[kb2] = T::mma(a, qop[0], bias_acc);
           else sacc[kb2] = T::mma(a, qop[0], (Acc){});
         } else {
           sacc[kb2] = T::mma(a, qop[s], sacc[kb2]);
@@ -670,9 +676,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     stage_k<D, KQT, VQT>(kst, pf);
     if constexpr (LPV) stage_v8<D, KQT, VQT>((uint8_t*)vst, pf);
     else stage_v<D, KQT, VQT>(vst, pf, TOK ? sc.vs[t % kScaleRing] : nullptr);
-    if (wave == 0) stage_scales<TOK, kBiasAcc>(sc, (t + 1) % kScaleRing, sr, p.kv_scale_f16, vref_run);
+    if (wave == 0) stage_scales<TOK>(sc, (t + 1) % kScaleRing, sr, p.kv_scale_f16, vref_run);
     fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, tile_n0(t + 2), tile_n0(t + 1));
     if (wave == 0) fetch_scales(sr, p, sbase, tile_n0(t + 2), TOK);
+    if constexpr (TOK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          key_s[kb][rg] = *(const f32x4*)(sc.ks[t % kScaleRing] + kb * 32 + 8 * rg + 4 * half);
+    }
   };
 
   // Softmax of the scores of tile t (in sacc) into pb and the running
@@ -785,8 +798,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
           pb[kb][r >> 3][(r & 7) + 1] = h2[1];
         }
     } else {
-      // Per-key scales: y_j = sk_j dot_j = fma(x_j, a_j, b_j) and the score
-      // in log2 units is cq y_j. The V scales are folded into the staged V
+      // Per-key scales: y_j = sk_j dot_j (the integer dot product converted
+      // exactly, one rounding in the product) and the score in log2 units is
+      // cq y_j. The V scales are folded into the staged V
       // (code * sv_j / sv_ref), so the weights are the probabilities
       // themselves and O is kept in units of sv_ref, which only grows.
       const float vr = tile_vref;
@@ -805,13 +819,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 a4 = *(const f32x4*)(sc.ks[slot] + kb * 32 + 8 * rg + 4 * half);
-          const f32x4 b4 = *(const f32x4*)(sc.kb[slot] + kb * 32 + 8 * rg + 4 * half);
+          const f32x4 a4 = key_s[kb][rg];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * rg + i;
-            const float xv = kBiasAcc ? __int_as_float(sacc[kb][r]) : (float)sacc[kb][r];
-            float yv = __builtin_fmaf(xv, a4[i], b4[i]);
+            float yv = (float)sacc[kb][r] * a4[i];
             if constexpr (MASK && CAUSAL) yv = key_of(kb, r) > lim ? -INFINITY : yv;
             y[kb][r] = yv;
             mc[i] = fmaxf(mc[i], yv);
@@ -867,7 +879,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   if (wave == 0) fetch_scales(sr, p, sbase, 0, TOK);
   for (int i = tid; i < G::kVElems / 8; i += kThreads) ((uint4*)vbuf1)[i] = make_uint4(0, 0, 0, 0);
   stage_k<D, KQT, VQT>(kbuf0, pf);
-  if (wave == 0) stage_scales<TOK, kBiasAcc>(sc, 0, sr, p.kv_scale_f16, vref_run);
+  if (wave == 0) stage_scales<TOK>(sc, 0, sr, p.kv_scale_f16, vref_run);
   fetch_tile<D, KQT, VQT>(pf, p, kbase, vbase, tile_n0(1), 0);
   if (wave == 0) fetch_scales(sr, p, sbase, tile_n0(1), TOK);
   __syncthreads();
