@@ -78,7 +78,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPairs = ix::kFwdPairs;  // (row, head) pairs per workgroup
 constexpr int kBN = ix::kFwdBN;        // keys per tile
-constexpr int kScaleRing = 3;     // tiles of scales in flight
+constexpr int kScaleRing = 4;     // tiles of scales in flight (a power of two)
 constexpr float kRescaleSlack = 12.0f;
 // With per-key scales the fp16 weight is p * sv_j / sv_ref <= p; the smaller
 // slack keeps the weights and their row sums well inside fp16.
@@ -290,8 +290,20 @@ __device__ __forceinline__ void stage_v(_Float16* vbuf, const Stage<D, KQT, VQT>
     *(f16x2*)(base + c * Geo<D>::kVStride) = h;
   };
   if constexpr (VQT == QFA_INT4) {
-    // Nibble c of key a (b) sits in byte c/2 of its word(s); gather byte j of
-    // both keys, then shift each nibble pair under the exponent.
+    // Nibble c of key a (b) sits in byte c/2 of its word(s). Bytes j, j+1 of
+    // both keys are gathered (a in bits 0-15, b in 16-31). With its sign bit
+    // flipped a nibble is code + 8; a low nibble (bits 0-3) goes under the
+    // fp16 exponent of 1024 (1032 + code), a high nibble stays in bits 4-7,
+    // the mantissa bits of weight 1 under the exponent of 64 (72 + code):
+    // both exact, no shift for the high nibble.
+    const f16x2 b_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const f16x2 b_hi = {(_Float16)72.0f, (_Float16)72.0f};
+    auto lo_h = [&](uint32_t w) __attribute__((always_inline)) {
+      return __builtin_bit_cast(f16x2, ((w ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u) - b_lo;
+    };
+    auto hi_h = [&](uint32_t w) __attribute__((always_inline)) {
+      return __builtin_bit_cast(f16x2, ((w ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u) - b_hi;
+    };
 #pragma unroll
     for (int w = 0; w < (S::kVSrc + 3) / 4; ++w) {
       const uint32_t a = f.v[0][w], b = f.v[1][w];
@@ -300,15 +312,12 @@ __device__ __forceinline__ void stage_v(_Float16* vbuf, const Stage<D, KQT, VQT>
         // bytes j, j+1 of a in bytes 0-1, of b in bytes 2-3
         const uint32_t sel = (j == 0) ? 0x05040100u : 0x07060302u;
         const uint32_t u = __builtin_amdgcn_perm(b, a, sel);
-        // channel 2j' + s of byte j' (j' = j, j+1): a in bits 0-3 / b in bits 16-19
-        // after shifting byte j' of each half down
-        const uint32_t pr0 = (u & 0x00FF00FFu);          // byte j of a, byte j of b
-        const uint32_t pr1 = ((u >> 8) & 0x00FF00FFu);   // byte j+1 of a, of b
+        const uint32_t u8 = u >> 8;  // byte j+1 of each key in the low byte
         const int c0 = 8 * w + 2 * j;
-        put(c0 + 0, i4pair_to_h(pr0));
-        put(c0 + 1, i4pair_to_h(pr0 >> 4));
-        put(c0 + 2, i4pair_to_h(pr1));
-        put(c0 + 3, i4pair_to_h(pr1 >> 4));
+        put(c0 + 0, lo_h(u));
+        put(c0 + 1, hi_h(u));
+        put(c0 + 2, lo_h(u8));
+        put(c0 + 3, hi_h(u8));
       }
     }
   } else if constexpr (VQT == QFA_FP8_E4M3) {
@@ -370,33 +379,40 @@ struct ScaleRegs {
 
 __device__ __forceinline__ void fetch_scales(ScaleRegs& r, const FwdParams& p, long sbase, int n0,
                                              bool tok) {
-  const long g = ix::fwd_kv_scale_block(sbase, n0, (int)(threadIdx.x & 63), p.Sk, p.kv_block, tok);
+  // The block relative to the (batch, KV head)'s first, as a 32-bit offset
+  // from a uniform base.
+  const long g = ix::fwd_kv_scale_block(0, n0, (int)(threadIdx.x & 63), p.Sk, p.kv_block, tok);
   // Two 16-bit loads per scale, neither past the scale's own bytes.
   long i0, i1;
   ix::scale_halves(g, p.kv_scale_f16, i0, i1);
-  r.klo = ((const uint16_t*)p.ks)[i0];
-  r.khi = ((const uint16_t*)p.ks)[i1];
-  r.vlo = ((const uint16_t*)p.vs)[i0];
-  r.vhi = ((const uint16_t*)p.vs)[i1];
+  const long base = 2 * (p.kv_scale_f16 ? sbase : 2 * sbase);  // bytes
+  const uint8_t* ks = (const uint8_t*)p.ks + base;
+  const uint8_t* vs = (const uint8_t*)p.vs + base;
+  const uint32_t o0 = 2 * (uint32_t)i0, o1 = 2 * (uint32_t)i1;
+  r.klo = *(const uint16_t*)(ks + o0);
+  r.khi = *(const uint16_t*)(ks + o1);
+  r.vlo = *(const uint16_t*)(vs + o0);
+  r.vhi = *(const uint16_t*)(vs + o1);
 }
 
-// Largest value of v over the wavefront, in every lane: DPP exchanges inside
-// each row of 16 lanes (lane i ^ 1, i ^ 2, then the mirrored lane of its 8 and
-// of its 16), then the four row results read as scalars. No LDS round trip.
+// Largest |v| over the wavefront, in every lane. Magnitudes of floats order
+// as their bit patterns, so the maximum is taken on integers: DPP exchanges
+// inside each row of 16 lanes (lane i ^ 1, i ^ 2, then the mirrored lane of
+// its 8 and of its 16), then the four row results read as scalars. No LDS
+// round trip.
 template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1, 0, 3, 2]
-  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2, 3, 0, 1]
-  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
-  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+__device__ __forceinline__ float wave_max_abs(float v) {
+  uint32_t m = __float_as_uint(v) & 0x7FFFFFFFu;
+  m = max(m, dpp_u32<0xB1>(m));   // quad_perm [1, 0, 3, 2]
+  m = max(m, dpp_u32<0x4E>(m));   // quad_perm [2, 3, 0, 1]
+  m = max(m, dpp_u32<0x141>(m));  // row_half_mirror
+  m = max(m, dpp_u32<0x140>(m));  // row_mirror
+  const uint32_t r0 = __builtin_amdgcn_readlane(m, 0), r1 = __builtin_amdgcn_readlane(m, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(m, 32), r3 = __builtin_amdgcn_readlane(m, 48);
+  return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
 // With per-key scales each key's K scale is staged (the score is the dot
@@ -410,7 +426,9 @@ __device__ __forceinline__ void stage_scales(ScaleRing& sm, int slot, const Scal
   const float vs = f16 ? f16_bits_to_f32(r.vlo) : __uint_as_float(r.vlo | (r.vhi << 16));
   if constexpr (TOK) {
     sm.ks[slot][lane] = ks;
-    vref_run = fmaxf(vref_run, wave_max(vs));
+    // V scales are magnitudes (amax / qmax); the largest |scale| keeps every
+    // ratio within [-1, 1] whatever the caller passes.
+    vref_run = fmaxf(vref_run, wave_max_abs(vs));
     // The ratio goes into fp16 (the staged V), so the hardware reciprocal
     // (1 ulp) is ample.
     sm.vs[slot][lane] = vref_run > 0.0f ? vs * __builtin_amdgcn_rcpf(vref_run) : 0.0f;
@@ -693,7 +711,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // (a wavefront whose rows all lie above the tile masks every key).
   auto softmax = [&](int t, auto mask_c) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
-    const int slot = t % kScaleRing;
     const int lim = lim_base - t * kBN;  // masked iff key_of(kb, r) > lim
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // independent partial row sums
