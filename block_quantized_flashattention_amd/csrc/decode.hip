@@ -713,28 +713,55 @@ void decode_mha_kernel(DecParams p) {
   const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
   const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
 
-  const int t_begin = split * kDecodeChunk + wave * kSWaveTokens;
-  const int t_end = min(t_begin + kSWaveTokens, L);
+  // INT8 cache (kBal): the sequence's nsplit chunks are of equal length (at
+  // most kDecodeChunk) and each wavefront takes an equal share of its chunk
+  // (at most kSWaveTokens), so a workgroup's duration follows its length;
+  // with fixed 1024-token chunks the last, partial chunk of every sequence
+  // leaves wavefronts idle for a whole chunk's time (measured: 14% of the
+  // rate on the ragged decode workload). The packed INT4 cache keeps fixed
+  // chunks: the per-token block-scale handling an equal share needs cost it
+  // more than the balance gained.
+  constexpr bool kBal = !INT4;
+  int t_begin, t_end;
+  if constexpr (kBal) {
+    const int cs = (int)((long)split * L / nsplit), ce = (int)((long)(split + 1) * L / nsplit);
+    const int pw = (ce - cs + kSWaves - 1) / kSWaves;
+    // One value per wavefront (scalar, so the buffer resources below are too).
+    t_begin = __builtin_amdgcn_readfirstlane(cs + wave * pw);
+    t_end = min(t_begin + pw, ce);
+  } else {
+    t_begin = split * kDecodeChunk + wave * kSWaveTokens;
+    t_end = min(t_begin + kSWaveTokens, L);
+  }
   const int t_last = t_end - 1;
 
   float m_blk = -INFINITY, l_blk = 0.0f, wsum = 0.0f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
-  float sk_blk = 1.0f, sv_blk = 1.0f;
+  // Block scales: a wavefront's tokens (at most kSWaveTokens <= kv_block)
+  // lie in block b0 and, with kBal, possibly the next from (b0 + 1) kv_block
+  // on. The K scales go into the score factors; the V scales, with kBal, as
+  // ratios to the larger of the two (sv_ref) in each token's weight, O being
+  // kept in units of sv_ref; otherwise sv_ref is the one block's V scale.
+  float csk0 = 0.0f, csk1 = 0.0f, rv0 = 1.0f, rv1 = 1.0f, sv_ref = 1.0f;
+  int dnd = 0;  // lane's tokens t_begin + tg + j TPS lie in block b0 while j TPS < dnd
 
   if (t_begin < t_end) {
     // ---- scores: sc[j] for token t_begin + j*TPS + tg (log2 units) ----
     float sc[NSUB];
     uint4 kw[2][kSLoadGroup];
-    // Rows [0, L) of this (batch, KV head) through buffer resources: one
-    // 32-bit offset per lane (the host keeps every offset below 2^31), and
-    // rows at or past L read as zero, so no clamp is needed (their scores
-    // are masked).
-    const int span = (L - 1) * (int)p.c_row + kRowBytes;
-    const auto krs = rows_rsrc(p.k + cbase, span);
-    const auto vrs = rows_rsrc(p.v + cbase, span);
-    const int loff = (t_begin + tg) * (int)p.c_row + dc * 16;
+    // This wavefront's rows of the (batch, KV head) through buffer resources
+    // (kBal: [t_begin, t_end); else [t_begin, L)): one 32-bit offset per lane
+    // (the host keeps every offset below 2^31), and rows past the end read as
+    // zero without a memory access, so no clamp is needed (their scores are
+    // masked).
+    const int t0 = kBal ? t_begin : 0;  // first row of the resources (uniform)
+    const long wbase = cbase + (long)t0 * p.c_row;
+    const int span = ((kBal ? t_end : L) - t0 - 1) * (int)p.c_row + kRowBytes;
+    const auto krs = rows_rsrc(p.k + wbase, span);
+    const auto vrs = rows_rsrc(p.v + wbase, span);
+    const int loff = (t_begin - t0 + tg) * (int)p.c_row + dc * 16;
     auto bload = [&](__amdgpu_buffer_rsrc_t rs, int j) {
       const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, loff + j * TPS * (int)p.c_row, 0, 0);
       return make_uint4(r[0], r[1], r[2], r[3]);
@@ -749,12 +776,25 @@ void decode_mha_kernel(DecParams p) {
       for (int i = 0; i < kSLoadGroup; ++i) dst[i] = bload(vrs, g * kSLoadGroup + i);
     };
     kload(kw[0], 0);
-    if constexpr (BLOCK_SCALE) {
-      sk_blk = load_scale(p.ks, sbase + t_begin / p.kv_block, p.kv_scale_f16);
-      sv_blk = load_scale(p.vs, sbase + t_begin / p.kv_block, p.kv_scale_f16);
+    if constexpr (BLOCK_SCALE && kBal) {
+      const int b0 = t_begin / p.kv_block;
+      const int b1 = min(b0 + 1, p.nkblk - 1);
+      dnd = (b0 + 1) * p.kv_block - (t_begin + tg);
+      const float sk0 = load_scale(p.ks, sbase + b0, p.kv_scale_f16);
+      const float sk1 = load_scale(p.ks, sbase + b1, p.kv_scale_f16);
+      const float sv0 = load_scale(p.vs, sbase + b0, p.kv_scale_f16);
+      const float sv1 = load_scale(p.vs, sbase + b1, p.kv_scale_f16);
+      csk0 = p.scale_log2 * sk0;
+      csk1 = p.scale_log2 * sk1;
+      sv_ref = fmaxf(fabsf(sv0), fabsf(sv1));
+      const float inv = sv_ref > 0.0f ? 1.0f / sv_ref : 0.0f;
+      rv0 = sv0 * inv;
+      rv1 = sv1 * inv;
+    } else if constexpr (BLOCK_SCALE) {
+      csk0 = p.scale_log2 * load_scale(p.ks, sbase + t_begin / p.kv_block, p.kv_scale_f16);
+      sv_ref = load_scale(p.vs, sbase + t_begin / p.kv_block, p.kv_scale_f16);
     }
     prep_q();
-    const float csk = p.scale_log2 * sk_blk;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g + 1 < NG) kload(kw[(g + 1) & 1], g + 1);
@@ -798,8 +838,12 @@ void decode_mha_kernel(DecParams p) {
         }
         acc = lane_group_sum<LPT>(acc);
         const int t = t_begin + j * TPS + tg;
-        float c = csk;
-        if constexpr (!BLOCK_SCALE) {
+        float c;
+        if constexpr (BLOCK_SCALE && kBal) {
+          c = j * TPS < dnd ? csk0 : csk1;
+        } else if constexpr (BLOCK_SCALE) {
+          c = csk0;
+        } else {
           c = p.scale_log2 * load_scale(p.ks, sbase + min(t, t_last) / p.kv_block, p.kv_scale_f16);
         }
         sc[j] = t < t_end ? acc * c : -INFINITY;
@@ -865,7 +909,9 @@ void decode_mha_kernel(DecParams p) {
           const float pr = __builtin_amdgcn_exp2f(sc[j] - m_blk);  // 0 for masked tokens
           lp[i & 1] += pr;
           float wt = pr;
-          if constexpr (!BLOCK_SCALE) {
+          if constexpr (BLOCK_SCALE && kBal) {
+            wt *= j * TPS < dnd ? rv0 : rv1;
+          } else if constexpr (!BLOCK_SCALE) {
             const int t = min(t_begin + j * TPS + tg, t_last);
             wt *= load_scale(p.vs, sbase + t / p.kv_block, p.kv_scale_f16);
           }
@@ -888,7 +934,7 @@ void decode_mha_kernel(DecParams p) {
     sum_scatter<LPT, EPL>(o, lane);
     constexpr float kOffV = kI4H ? 1032.0f : kOff;
 #pragma unroll
-    for (int e = 0; e < NF; ++e) o[e] = (o[e] - kOffV * wsum) * sv_blk;
+    for (int e = 0; e < NF; ++e) o[e] = (o[e] - kOffV * wsum) * sv_ref;
   }
 
   // Merge the wavefronts of the workgroup.
@@ -1012,7 +1058,7 @@ template <int D, bool INT4>
 hipError_t launch_dec(const DecParams& p, int B, hipStream_t st) {
   hipError_t e;
   if (p.group == 1) {
-    // Block scales are uniform over a wavefront's 128 tokens.
+    // Block scales: a wavefront's tokens (at most 128) span at most two blocks.
     const bool bs = p.kv_block % kSWaveTokens == 0;
     if (p.q_dtype == QFA_F16)
       e = bs ? launch_mha<D, INT4, true, true>(p, B, st) : launch_mha<D, INT4, true, false>(p, B, st);
