@@ -52,6 +52,11 @@ SMALL = [
     # name, B, Hq, Hkv, D, S_max, lens, kv qtype, kv_block, scale dtype
     ("i8_gqa2", 3, 4, 2, 128, 3000, [1, 1024, 2999], "int8", 256, "f16"),
     ("i8_splits", 2, 2, 2, 128, 4100, [1025, 4100], "int8", 256, "f16"),
+    # one head per KV head, INT8: every sequence is split into ceil(S_max/1024)
+    # chunks, so very short ones leave chunks with no tokens or a few
+    ("i8_short", 3, 2, 2, 128, 3000, [1, 5, 2999], "int8", 256, "f16"),
+    # 128-token blocks: a wavefront's equal share spans two blocks
+    ("i8_r128", 2, 2, 2, 128, 3333, [3333, 1500], "int8", 128, "f32"),
     ("i8_d64_f32s", 2, 3, 3, 64, 700, [700, 17], "int8", 64, "f32"),
     ("i4_tok", 2, 8, 2, 128, 2500, [2500, 300], "int4", 1, "f16"),
     ("i4_blk", 2, 2, 1, 128, 1500, [1200, 1500], "int4", 256, "f16"),
