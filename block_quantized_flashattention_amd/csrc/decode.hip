@@ -85,8 +85,9 @@ struct DecParams {
   long q_head, q_batch;         // element strides of q and out
   int kv_block, nkblk, kv_scale_f16, q_dtype, out_dtype;
   float scale_log2;
-  // Single-head INT8 cache: every sequence in max_splits chunks, so no
-  // workgroup of the grid is empty (else ceil(L / kDecodeChunk) chunks).
+  // Every sequence in max_splits chunks of equal length, so no workgroup of
+  // the grid is empty (grouped heads, and one head per KV head with the INT8
+  // cache); else ceil(L / kDecodeChunk) chunks of kDecodeChunk tokens.
   int all_splits;
 };
 
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int L = min(max(p.lens[b], 1), p.S_max);
-  const int nsplit = (L + kDecodeChunk - 1) / kDecodeChunk;
+  const int nsplit = p.all_splits ? p.max_splits : (L + kDecodeChunk - 1) / kDecodeChunk;
   if (split >= nsplit) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -314,16 +315,24 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
 
   constexpr int kSub = G::kSub;
   constexpr int kBatch = kStep * kSub;  // tokens per load batch
-  const int t_begin = split * kDecodeChunk + wave * kGWaveTokens;
-  const int t_end = min(t_begin + kGWaveTokens, L);
+  // Every sequence in max_splits chunks of equal length (starts at multiples
+  // of kStep) and equal wavefront shares (multiples of kStep, so block
+  // scales stay uniform over a step): a workgroup's duration follows its
+  // length and none is empty (as in the single-head kernel).
+  const int cs = (int)((long)split * L / nsplit) / kStep * kStep;
+  const int ce = split + 1 == nsplit ? L : (int)((long)(split + 1) * L / nsplit) / kStep * kStep;
+  const int pw = ((ce - cs + kGWaves - 1) / kGWaves + kStep - 1) / kStep * kStep;
+  const int t_begin = __builtin_amdgcn_readfirstlane(min(cs + wave * pw, ce));
+  const int t_end = min(t_begin + pw, ce);
   const int nbatch = t_begin < t_end ? (t_end - t_begin + kBatch - 1) / kBatch : 0;
   const long sbase = ((long)b * p.Hkv + kvh) * p.nkblk;
 
   // Rows [0, L) of this (batch, KV head) through buffer resources: rows at or
   // past L read as zero (their scores are masked). Offsets stay below 2^31
   // (the host checks (S_max + chunk) * row stride).
-  const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head;
-  const int span = (L - 1) * (int)p.c_row + G::kRowBytes;
+  // This wavefront's rows [t_begin, t_end): rows past t_end read as zero.
+  const long cbase = (long)b * p.c_batch + (long)kvh * p.c_head + (long)t_begin * p.c_row;
+  const int span = max(t_end - t_begin - 1, 0) * (int)p.c_row + G::kRowBytes;
   const auto krs = rows_rsrc(p.k + cbase, span);
   const auto vrs = rows_rsrc(p.v + cbase, span);
   const int crow = (int)p.c_row;
@@ -341,10 +350,10 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
       }
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
-        bload<G::kKBytes>(r.k[u][tb], krs, (t0 + 16 * tb + n) * crow + g * G::kKBytes);
+        bload<G::kKBytes>(r.k[u][tb], krs, (t0 - t_begin + 16 * tb + n) * crow + g * G::kKBytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        bload<G::kVBytes>(r.v[u][i], vrs, (t0 + 4 * tq + i) * crow + cg * G::kVBytes);
+        bload<G::kVBytes>(r.v[u][i], vrs, (t0 - t_begin + 4 * tq + i) * crow + cg * G::kVBytes);
     }
   };
 
@@ -1153,7 +1162,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.out_dtype = a.out_dtype;
   p.scale_log2 = a.softmax_scale * kLog2e;
   const bool int4 = a.kv_qtype == QFA_INT4;
-  p.all_splits = !int4 && p.group == 1;
+  p.all_splits = p.group > 1 || !int4;
   if (a.D == 64) return int4 ? launch_dec<64, true>(p, a.B, stream) : launch_dec<64, false>(p, a.B, stream);
   return int4 ? launch_dec<128, true>(p, a.B, stream) : launch_dec<128, false>(p, a.B, stream);
 }
