@@ -144,3 +144,32 @@ def test_per_token_path_large_and_small_v(vscale):
                            oracle.dequantize(rk, rks, 1, "int4"),
                            oracle.dequantize(rv, rvs, 1, "int4"), w.softmax_scale, causal=True)
     assert_close(out.double().cpu().numpy() / vscale, ref / vscale, f"V x {vscale:g}")
+
+
+def test_per_token_v_scales_spanning_four_decades():
+    """INT4 K/V with one fp16 scale per token, V rows scaled by 10^u with u
+    uniform in [-2, 2) per token: the staged values are code * sv_j / sv_ref
+    with sv_ref the running maximum V scale, so early small-scale tokens are
+    rescaled when a larger scale arrives and late ones are staged small. The
+    tolerance is stated for unit-variance V: errors are compared in units of
+    the largest V row scale."""
+    w = wl.scaled(wl.GQA_INT4, name="gqa8x2_int4_vspread", Hq=8, Hkv=2, S=333)
+    q, k, v = wl.make_prefill_inputs(w)
+    g = torch.Generator().manual_seed(1234)
+    mag = 10.0 ** (torch.rand(v.shape[0], v.shape[1], v.shape[2], 1, generator=g) * 4.0 - 2.0)
+    v = (v.float() * mag).half()
+    say(f"per-token path, V row magnitudes 1e-2..1e2: V amax {float(v.float().abs().max()):.3g}")
+    qc, qs = qfa.block_quant(q.cuda(), w.q_block, "int8")
+    kc, ks = qfa.block_quant(k.cuda(), 1, "int4", torch.float16)
+    vc, vs = qfa.block_quant(v.cuda(), 1, "int4", torch.float16)
+    out = qfa.fwd(qc, qs, kc, ks, vc, vs, q_qtype="int8", k_qtype="int4", v_qtype="int4",
+                  q_block=w.q_block, kv_block=1, softmax_scale=w.softmax_scale, causal=True,
+                  out_dtype=torch.float32)
+    rq, rqs = oracle.block_quant(q, w.q_block, "int8")
+    rk, rks = oracle.block_quant(k, 1, "int4", "f16")
+    rv, rvs = oracle.block_quant(v, 1, "int4", "f16")
+    ref = oracle.attention(oracle.dequantize(rq, rqs, w.q_block, "int8"),
+                           oracle.dequantize(rk, rks, 1, "int4"),
+                           oracle.dequantize(rv, rvs, 1, "int4"), w.softmax_scale, causal=True)
+    unit = float(mag.max())
+    assert_close(out.double().cpu().numpy() / unit, ref / unit, "V rows 1e-2..1e2")
