@@ -141,12 +141,22 @@ __device__ __forceinline__ float scale_value(typename ScaleT<F16S>::type r) {
 }
 
 // Four signed bytes as two exact fp16 pairs (1024 + (byte ^ 0x80) - 1152).
+template <bool OFF = false>
 __device__ __forceinline__ void i8x4_to_h(uint32_t w, f16x2& lo, f16x2& hi) {
   const uint32_t u = w ^ 0x80808080u;
-  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u)) - bias;
-  hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u)) - bias;
+  lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u));
+  hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x07030602u));
+  if constexpr (!OFF) {
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    lo = lo - bias;
+    hi = hi - bias;
+  }
 }
+
+// The fp16 offset of a code left in offset form (OFF): 1152 + code (INT8),
+// 1032 + code (INT4), both exact.
+template <bool INT4>
+constexpr float kCodeOffset = INT4 ? 1032.0f : 1152.0f;
 
 // Nibbles at bits s..s+3 and 16+s..19+s of w, whose sign bits were already
 // flipped, as the fp16 pair 1032 + code (exact).
@@ -163,19 +173,25 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
 // K operand of k-step j from the lane's K words (D/4 channels of one token).
 // fp16: INT8 channels in order; INT4 in the nibble-pair order
 // (d, d+4, d+1, d+5, d+2, d+6, d+3, d+7) of one word. bf16: channels in order.
-template <bool INT4>
+// OFF: the codes in offset form (kCodeOffset + code).
+template <bool INT4, bool OFF = false>
 __device__ __forceinline__ f16x8 k_operand_f16(const uint32_t* kw, int j) {
   f16x8 r;
   if constexpr (!INT4) {
     f16x2 a, b, c, d;
-    i8x4_to_h(kw[2 * j], a, b);
-    i8x4_to_h(kw[2 * j + 1], c, d);
+    i8x4_to_h<OFF>(kw[2 * j], a, b);
+    i8x4_to_h<OFF>(kw[2 * j + 1], c, d);
     r = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   } else {
     const uint32_t w = kw[j] ^ 0x88888888u;
-    const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const f16x2 a = i4_pair_h(w, 0) - bias, b = i4_pair_h(w, 4) - bias;
-    const f16x2 c = i4_pair_h(w, 8) - bias, d = i4_pair_h(w, 12) - bias;
+    f16x2 a = i4_pair_h(w, 0), b = i4_pair_h(w, 4), c = i4_pair_h(w, 8), d = i4_pair_h(w, 12);
+    if constexpr (!OFF) {
+      const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+      a = a - bias;
+      b = b - bias;
+      c = c - bias;
+      d = d - bias;
+    }
     r = (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   }
   return r;
@@ -243,7 +259,7 @@ struct StepRegs {
 
 // Stage this lane's 4 tokens x D/8 channels of V (codes) into the wavefront's
 // V^T buffer as fp16: channel c of the lane's group, tokens in operand order.
-template <int D, bool INT4>
+template <int D, bool INT4, bool OFF = false>
 __device__ __forceinline__ void stage_v(const uint32_t (&v)[4][DecGeo<D, INT4>::kVWords],
                                         _Float16* vt, int c0, int pos0) {
   using G = DecGeo<D, INT4>;
@@ -257,10 +273,10 @@ __device__ __forceinline__ void stage_v(const uint32_t (&v)[4][DecGeo<D, INT4>::
       const uint32_t d23l = __builtin_amdgcn_perm(v[3][k], v[2][k], 0x05010400u);
       const uint32_t d23h = __builtin_amdgcn_perm(v[3][k], v[2][k], 0x07030602u);
       f16x2 a0, a1, b0, b1, c0h, c1h, e0, e1;
-      i8x4_to_h(d01l, a0, a1);   // channel 4k: tokens 0,1 | channel 4k+1: tokens 0,1
-      i8x4_to_h(d23l, b0, b1);   // the same, tokens 2,3
-      i8x4_to_h(d01h, c0h, c1h); // channels 4k+2, 4k+3: tokens 0,1
-      i8x4_to_h(d23h, e0, e1);   // tokens 2,3
+      i8x4_to_h<OFF>(d01l, a0, a1);   // channel 4k: tokens 0,1 | channel 4k+1: tokens 0,1
+      i8x4_to_h<OFF>(d23l, b0, b1);   // the same, tokens 2,3
+      i8x4_to_h<OFF>(d01h, c0h, c1h); // channels 4k+2, 4k+3: tokens 0,1
+      i8x4_to_h<OFF>(d23h, e0, e1);   // tokens 2,3
       const int c = c0 + 4 * k;
       *(f16x4*)(vt + (c + 0) * kVtStride + pos0) = (f16x4){a0[0], a0[1], b0[0], b0[1]};
       *(f16x4*)(vt + (c + 1) * kVtStride + pos0) = (f16x4){a1[0], a1[1], b1[0], b1[1]};
@@ -268,7 +284,6 @@ __device__ __forceinline__ void stage_v(const uint32_t (&v)[4][DecGeo<D, INT4>::
       *(f16x4*)(vt + (c + 3) * kVtStride + pos0) = (f16x4){c1h[0], c1h[1], e1[0], e1[1]};
     } else {
       // Channels 8k..8k+7: nibble pairs (c, c+4) per token, then token pairs.
-      const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
       uint32_t w[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) w[t] = v[t][k] ^ 0x88888888u;
@@ -277,10 +292,17 @@ __device__ __forceinline__ void stage_v(const uint32_t (&v)[4][DecGeo<D, INT4>::
         uint32_t x[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) x[t] = __builtin_bit_cast(uint32_t, i4_pair_h(w[t], 4 * s));
-        const f16x2 lo01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[1], x[0], 0x05040100u)) - bias;
-        const f16x2 lo23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[3], x[2], 0x05040100u)) - bias;
-        const f16x2 hi01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[1], x[0], 0x07060302u)) - bias;
-        const f16x2 hi23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[3], x[2], 0x07060302u)) - bias;
+        f16x2 lo01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[1], x[0], 0x05040100u));
+        f16x2 lo23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[3], x[2], 0x05040100u));
+        f16x2 hi01 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[1], x[0], 0x07060302u));
+        f16x2 hi23 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(x[3], x[2], 0x07060302u));
+        if constexpr (!OFF) {
+          const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+          lo01 = lo01 - bias;
+          lo23 = lo23 - bias;
+          hi01 = hi01 - bias;
+          hi23 = hi23 - bias;
+        }
         const int c = c0 + 8 * k + s;  // shift 4s: channel s and s + 4 of the word
         *(f16x4*)(vt + c * kVtStride + pos0) = (f16x4){lo01[0], lo01[1], lo23[0], lo23[1]};
         *(f16x4*)(vt + (c + 4) * kVtStride + pos0) = (f16x4){hi01[0], hi01[1], hi23[0], hi23[1]};
@@ -391,6 +413,25 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
     }
   }
 
+  // fp16 query: the K and V operands keep the codes in offset form
+  // (kCodeOffset + code, exact), which saves a subtraction per code pair;
+  // the offset's share of a score, kCodeOffset * sum(q) for head n, and of
+  // O, kCodeOffset times the sum of the fp16 weights, are removed afterwards.
+  constexpr bool kOffs = QM == Q_F16;
+  constexpr float kCO = kCodeOffset<INT4>;
+  float offq = 0.0f;
+  if constexpr (kOffs) {
+    float qs = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G::kKSteps; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qs += (float)qh[j][i];
+    qs += __shfl_xor(qs, 16);
+    qs += __shfl_xor(qs, 32);
+    offq = kCO * qs;
+  }
+  float wsum = 0.0f;  // (kOffs) this lane's sum of the fp16 weights of head n, in o's units
+
   f32x4 o[G::kCB];
 #pragma unroll
   for (int cb = 0; cb < G::kCB; ++cb) o[cb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
@@ -400,9 +441,10 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
   // down when a larger one arrives), so the fp16 weights p sv / sv_ref stay
   // at most 2^kSlack.
   float sv_ref = 0.0f;
+  float inv_ref = 0.0f;  // 1 / sv_ref (0 while sv_ref is 0), updated when sv_ref changes
 
   auto step = [&](const Regs& r, int u, int t0) __attribute__((always_inline)) {
-    stage_v<D, INT4>(r.v[u], vt, cg * (D / 8), pos0);
+    stage_v<D, INT4, kOffs>(r.v[u], vt, cg * (D / 8), pos0);
 
     // Scores: two 16-token blocks.
     f32x4 sacc[2];
@@ -412,7 +454,7 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
 #pragma unroll
       for (int j = 0; j < G::kKSteps; ++j) {
         if constexpr (QM == Q_F16) {
-          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand_f16<INT4>(r.k[u][tb], j),
+          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand_f16<INT4, kOffs>(r.k[u][tb], j),
                                                             qh[j], sacc[tb], 0, 0, 0);
         } else {
           const bf16x8 ka = k_operand_bf16<INT4>(r.k[u][tb], j);
@@ -427,6 +469,7 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
     // 4g + i) and their V scales.
     float y[8], sv[8];
     const float ck_blk = BS ? scale_value<F16S>(r.ks[u]) * p.scale_log2 : 0.0f;
+    const float ckoff = -offq * ck_blk;  // block scales: the offset's share, scaled
     const float sv_blk = BS ? scale_value<F16S>(r.vs[u]) : 0.0f;
     float sv_max = sv_blk;
 #pragma unroll
@@ -441,7 +484,8 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
           svt = scale_value<F16S>(raw_scale<F16S>(p.vs, blk));
           sv_max = fmaxf(sv_max, t < t_end ? svt : 0.0f);
         }
-        y[4 * tb + i] = t < t_end ? sacc[tb][i] * ck : -INFINITY;
+        const float yv = BS ? __builtin_fmaf(sacc[tb][i], ck, ckoff) : (sacc[tb][i] - offq) * ck;
+        y[4 * tb + i] = t < t_end ? yv : -INFINITY;
         sv[4 * tb + i] = svt;
       }
     if constexpr (!BS) {
@@ -466,18 +510,25 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
       const float lalpha = m_new == m_ref ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
       for (int cb = 0; cb < G::kCB; ++cb) o[cb] *= alpha;
+      wsum *= alpha;
       l_sum *= lalpha;
       m_ref = m_new;
+      if (sv_new != sv_ref) inv_ref = 1.0f / sv_new;  // sv_new > 0 here
       sv_ref = sv_new;
     }
     const float mref = m_ref == -INFINITY ? 0.0f : m_ref;
-    const float inv_ref = sv_ref > 0.0f ? 1.0f / sv_ref : 0.0f;
     f16x8 pb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float pr = __builtin_amdgcn_exp2f(y[i] - mref);
       l_sum += pr;
       pb[i] = (_Float16)(pr * (sv[i] * inv_ref));
+    }
+    if constexpr (kOffs) {
+      const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int i = 0; i < 8; i += 2)
+        wsum = __builtin_amdgcn_fdot2((f16x2){pb[i], pb[i + 1]}, one, wsum, false);
     }
 
     // P.V: the staged V^T rows of this lane's channels, tokens in slot order.
@@ -518,6 +569,12 @@ __global__ __launch_bounds__(64 * kGWaves, QM == Q_F32 ? 2 : 3) void decode_gqa_
 
   l_sum += __shfl_xor(l_sum, 16);
   l_sum += __shfl_xor(l_sum, 32);
+  if constexpr (kOffs) {
+    wsum += __shfl_xor(wsum, 16);
+    wsum += __shfl_xor(wsum, 32);
+#pragma unroll
+    for (int cb = 0; cb < G::kCB; ++cb) o[cb] -= kCO * wsum;
+  }
 
   // Merge the four wavefronts (o in V-scale units: times sv_ref).
   __syncthreads();

@@ -26,6 +26,8 @@ SMALL = [
     wl.scaled(wl.FP8_ROT, name="fp8_rot_causal_s200", B=2, Hq=1, Hkv=1, S=200, causal=True),
     wl.scaled(wl.GQA_INT4, name="gqa8x2_int4_s257", Hq=8, Hkv=2, S=257),
     wl.scaled(wl.GQA_INT4, name="gqa4x1_int4_noncausal_s129", Hq=4, Hkv=1, S=129, causal=False),
+    # Q blocks of 48 rows: a wavefront's 32 rows can span two Q scales.
+    wl.scaled(wl.GQA_INT4, name="gqa8x2_int4_qblock48_s200", Hq=8, Hkv=2, S=200, q_block=48),
     wl.scaled(wl.GQA_INT4, name="int8qk_int4v_s300", Hq=2, Hkv=2, S=300, k_qtype="int8",
               kv_block=256, kv_scale_dtype="f32"),
     wl.scaled(wl.INT8_CAUSAL, name="int8_kvblock64_s200", Hq=2, Hkv=1, S=200, kv_block=64),
