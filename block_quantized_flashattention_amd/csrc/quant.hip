@@ -601,9 +601,16 @@ __global__ __launch_bounds__(64 * kRotWaves * W, 4) void rot_quant_kernel(RotPar
   // bytes so that the 32 rows of a wavefront's 4-byte writes hit distinct
   // banks; then each row is written with 16-byte (or 4-byte) coalesced stores.
   uint8_t* cs = (uint8_t*)ws;
+  // The row and lane half are derived again from the thread index (through
+  // an opaque copy, so the compiler does not keep the earlier values live
+  // across the matrix instructions: under the 128-register cap that cost a
+  // spill).
+  int tid2 = threadIdx.x;
+  asm volatile("" : "+v"(tid2));
+  const int half2 = (tid2 >> 5) & 1;
 #pragma unroll
   for (int tt = 0; tt < 1; ++tt) {
-    const int trow = (wave + NW * tt) * 32 + col;
+    const int trow = ((tid2 >> 6) + NW * tt) * 32 + (tid2 & 31);
     if (trow >= rows) continue;
 #pragma unroll
     for (int ib = 0; ib < kIB; ++ib)
@@ -613,7 +620,7 @@ __global__ __launch_bounds__(64 * kRotWaves * W, 4) void rot_quant_kernel(RotPar
         float t[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) t[i] = quotient<QT == QFA_FP8_E4M3>(acc[tt][ib][4 * g + i], sc, rcp, fast);
-        *(uint32_t*)(cs + trow * kCS + ib * 32 + 8 * g + 4 * half) = zero ? 0u : encode4<QT>(t);
+        *(uint32_t*)(cs + trow * kCS + ib * 32 + 8 * g + 4 * half2) = zero ? 0u : encode4<QT>(t);
       }
   }
   __syncthreads();
