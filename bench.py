@@ -261,8 +261,8 @@ def bench_fwd_lowp(torch, qfa, wl, steps, warmup):
     return {"workload": w.name, "fwd_ms": round(t16, 4), "fwd_lowp_ms": round(tlp, 4),
             "speedup": round(t16 / tlp, 3), "fallback_items": round(flagged, 4),
             "roofline": mfma_roofline(ops, tlp, PEAK_FP8_TFLOPS),
-            "note": "fp8 pass plus the fp16 pass over flagged work items; a flagged item "
-                    "is recomputed whole, so any flag adds about one workgroup's duration"}
+            "note": "one launch: fp8 P.V, and a workgroup whose gate flags a row recomputes "
+                    "its work item with the fp16 product before exiting"}
 
 
 def bench_rotate_quant(torch, qfa, wl, steps, warmup, flush):

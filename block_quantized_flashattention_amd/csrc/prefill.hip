@@ -63,8 +63,9 @@
 //     probabilities are rounded to e4m3, one v_mfma_scale_f32_32x32x64_f8f6f4
 //     per 32-channel block per tile. Each row also accumulates a bound on
 //     sum p^2; a row with too few effective keys flags its work item, and the
-//     fp16 kernel, launched again with those flags, recomputes exactly the
-//     flagged items.
+//     same workgroup then recomputes the item with the fp16 product (the fp16
+//     kernel's code), so only flagged items pay for the fallback and their
+//     recomputation overlaps with the rest of the grid.
 #include <type_traits>
 
 #include "qfa_device.h"
@@ -112,9 +113,8 @@ struct FwdParams {
   int out_dtype;
   float scale_log2;  // softmax_scale * log2(e)
   int xcd_order;     // 1: XCD-grouped workgroup order
-  // fp8 P.V pass: one byte per (workgroup, wavefront), 1 where a row failed
-  // the accuracy gate. fp16 pass: if set, a workgroup whose bytes are all 0
-  // exits at once (it recomputes only the items the fp8 pass flagged).
+  // fp8 P.V forward: one byte per (workgroup, wavefront), 1 where a row
+  // failed the accuracy gate. Unused by the fp16 forward.
   uint8_t* flags;
 };
 
@@ -468,10 +468,15 @@ struct QK {
 // 8*(r/4) + 4*half + r%4.
 __device__ __forceinline__ constexpr int key_of(int kb, int r) { return kb * 32 + 8 * (r >> 2) + (r & 3); }
 
-// LPV: P.V on the fp8 matrix unit (e4m3 V and probabilities, block scales
-// only), with the per-row accuracy gate written to p.flags.
+// One work item of the forward, computed by the whole workgroup in the LDS
+// buffers passed in. LPV: P.V on the fp8 matrix unit (e4m3 V and
+// probabilities, block scales only), with the per-row accuracy gate written to
+// p.flags; returns true, without writing any output, when a row of the work
+// item failed the gate. The fp16 path writes the output and returns false.
 template <int D, int KVM, bool CAUSAL, bool TOK, bool LPV>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
+__device__ __forceinline__ bool fwd_item(const FwdParams& p, uint8_t* kbuf0, uint8_t* kbuf1,
+                                         _Float16* vbuf0, _Float16* vbuf1, ScaleRing& sc,
+                                         uint16_t* obuf) {
   constexpr bool FP8 = KVM == KV_F8_F8;
   static_assert(!LPV || (FP8 && !TOK), "fp8 P.V: e4m3 V with block scales");
   constexpr int KQT = KVTypes<KVM>::K, VQT = KVTypes<KVM>::V;
@@ -503,24 +508,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   static_assert(D <= 128, "biased INT8 scores need |dot| < 2^21");
   constexpr float kSlack = TOK ? kRescaleSlackTok : (LPV ? kRescaleSlackLp : kRescaleSlack);
 
-  __shared__ __align__(16) uint8_t kbuf0[G::kKBytes];
-  __shared__ __align__(16) uint8_t kbuf1[G::kKBytes];
-  __shared__ __align__(16) _Float16 vbuf0[G::kVElems];
-  __shared__ __align__(16) _Float16 vbuf1[G::kVElems];
-  __shared__ __align__(16) ScaleRing sc;
-  __shared__ __align__(16) uint16_t obuf[kWaves * 32 * G::kOutStride];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int grp = wave >> 2;   // 0: group A, 1: group B
   const int half = lane >> 5;  // lane half: keys 4*half + {0..3} of every 8
   const int col = lane & 31;   // query row of this lane within the wavefront
-
-  // fp16 pass after an fp8 P.V pass: only the flagged work items.
-  if constexpr (!LPV) {
-    if (p.flags && *(const uint64_t*)(p.flags + (long)blockIdx.x * kWaves) == 0) return;
-  }
 
   // Work item: (batch, KV head, head group, row block).
   const ix::FwdItem it = ix::fwd_item(blockIdx.x, p.B, p.Hkv, p.n_hg, p.n_rb, p.xcd_order, CAUSAL);
@@ -930,12 +923,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
   // Epilogue: lane holds row qrow, channels 32*db + 8*(r/4) + 4*half + (r%4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if constexpr (LPV) {
-    // Accuracy gate: flag the work item when a row's effective number of
-    // keys may be below kNeffMin (its fp16 pass then recomputes the item).
+    // Accuracy gate: flag the wavefront when a row's effective number of keys
+    // may be below kNeffMin; if any wavefront is flagged, the workgroup
+    // writes nothing here and recomputes the whole item with the fp16 product.
     const float s_tot = s_run + __shfl_xor(s_run, 32);
     const bool fail = qvalid && !(l_tot * l_tot >= kNeffMin * s_tot);
     const bool any = __builtin_amdgcn_ballot_w64(fail) != 0;
     if (lane == 0) p.flags[(long)blockIdx.x * kWaves + wave] = any ? 1 : 0;
+    if (__syncthreads_or(fail)) return true;
   }
   const float inv = sv_cur / l_tot;
   const long hbase = (long)b * p.o_batch + (long)h * p.o_head;
@@ -973,9 +968,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         *(uint4*)((uint16_t*)p.out + hbase + (long)(wrow0 + row) * p.o_row + c * 8) =
             *(const uint4*)(so + row * kOS + c * 8);
     }
-    return;
+    return false;
   }
-  if (!qvalid) return;
+  if (!qvalid) return false;
   const long obase = hbase + (long)qrow * p.o_row;
 #pragma unroll
   for (int db = 0; db < kDB; ++db) {
@@ -986,6 +981,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
           (f32x4){o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv, o[db][4 * rg + 2] * inv,
                   o[db][4 * rg + 3] * inv};
     }
+  }
+  return false;
+}
+
+// The forward kernel: one work item per workgroup. With LPV the item is first
+// computed with the fp8 P.V product; a workgroup whose gate flagged a row
+// recomputes the item at once with the fp16 product, exactly as the fp16
+// kernel does, so the fallback costs only the flagged items' own time and
+// overlaps with the rest of the grid.
+template <int D, int KVM, bool CAUSAL, bool TOK, bool LPV>
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
+  using G = Geo<D>;
+  __shared__ __align__(16) uint8_t kbuf0[G::kKBytes];
+  __shared__ __align__(16) uint8_t kbuf1[G::kKBytes];
+  __shared__ __align__(16) _Float16 vbuf0[G::kVElems];
+  __shared__ __align__(16) _Float16 vbuf1[G::kVElems];
+  __shared__ __align__(16) ScaleRing sc;
+  __shared__ __align__(16) uint16_t obuf[kWaves * 32 * G::kOutStride];
+  if constexpr (LPV) {
+    if (!fwd_item<D, KVM, CAUSAL, TOK, true>(p, kbuf0, kbuf1, vbuf0, vbuf1, sc, obuf)) return;
+    // Every wavefront has left the fp8 pass's last barrier (the gate's
+    // reduction is one), so its LDS buffers are free.
+    fwd_item<D, KVM, CAUSAL, TOK, false>(p, kbuf0, kbuf1, vbuf0, vbuf1, sc, obuf);
+  } else {
+    fwd_item<D, KVM, CAUSAL, TOK, false>(p, kbuf0, kbuf1, vbuf0, vbuf1, sc, obuf);
   }
 }
 
@@ -1001,15 +1021,13 @@ hipError_t launch_kv(const FwdParams& p, int grid, bool causal, bool tok, hipStr
   return hipGetLastError();
 }
 
-// fp8 P.V pass (writes every work item's flags), then the fp16 pass over the
-// flagged items only.
+// fp8 P.V forward with the in-kernel fp16 fallback; writes every work item's
+// flags.
 template <int D>
 hipError_t launch_lowp(const FwdParams& p, int grid, bool causal, hipStream_t st) {
   if (causal) fwd_kernel<D, KV_F8_F8, true, false, true><<<grid, kThreads, 0, st>>>(p);
   else fwd_kernel<D, KV_F8_F8, false, false, true><<<grid, kThreads, 0, st>>>(p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_kv<D, KV_F8_F8>(p, grid, causal, false, st);
+  return hipGetLastError();
 }
 
 template <int D>

@@ -79,9 +79,9 @@ struct FwdArgs {
 // Returns hipErrorInvalidValue for a combination without a compiled kernel.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // The forward with P.V on the fp8 matrix unit (e4m3 Q/K/V with block
-// scales): an fp8 pass that writes one flag byte per (workgroup, wavefront)
-// to `flags` (fwd_lowp_workspace_bytes of them), then the fp16 pass over the
-// flagged work items.
+// scales): one launch that writes one flag byte per (workgroup, wavefront)
+// to `flags` (fwd_lowp_workspace_bytes of them); a workgroup with a flagged
+// wavefront recomputes its work item with the fp16 product before it exits.
 size_t fwd_lowp_workspace_bytes(int B, int Hq, int Hkv, int Sq);
 hipError_t launch_fwd_lowp(const FwdArgs& a, void* flags, hipStream_t stream);
 

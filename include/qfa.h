@@ -236,9 +236,10 @@ QFA_API size_t qfa_fwd_lowp_workspace_bytes(int B, int Hq, int Hkv, int Sq);
  * Each row bounds its effective number of keys (sum p)^2 / sum p^2 from below
  * by l^2 / S, S = the sum over 64-key tiles of the tile's largest probability
  * times the tile's sum; a row with l^2 / S < 256 ("peaky": a few keys
- * dominate) flags its work item, and a second pass recomputes the flagged
- * work items exactly as qfa_fwd does (fp16 P.V) over the first pass's output.
- * The output of a flagged work item is therefore bit-identical to qfa_fwd's.
+ * dominate) flags its work item, and the workgroup that computed the item
+ * recomputes it at once exactly as qfa_fwd does (fp16 P.V) before writing any
+ * of it, in the same launch. The output of a flagged work item is therefore
+ * bit-identical to qfa_fwd's, and a flag costs only that item's second pass.
  *
  * Arguments as qfa_fwd, plus
  *   workspace  device buffer of at least qfa_fwd_lowp_workspace_bytes(B,Hq,Hkv,Sq)
