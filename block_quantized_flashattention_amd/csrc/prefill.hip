@@ -39,7 +39,8 @@
 //     (see kBiasBits), and each probability costs one FMA and one exp2. O is
 //     kept in units of the current V block scale and rescaled when it
 //     changes. With per-key scales (INT4 K/V, one scale per token) the
-//     integer dot product is converted and multiplied by the key's scale
+//     integer dot product (read off the same biased accumulator with one
+//     subtraction, exact) is multiplied by the key's scale
 //     (staged beside the tile; each lane loads its 32 keys' scales into
 //     registers at the end of its matrix phase), and the V scale goes into the
 //     staged V: code * sv_j / sv_ref in fp16, sv_ref the running maximum V
@@ -497,12 +498,16 @@ __device__ __forceinline__ bool fwd_item(const FwdParams& p, uint8_t* kbuf0, uin
   // -2292099 <= dot < 6096509, which any 8-bit codes with D <= 128 satisfy
   // (|dot| <= 128 * 128 * 128). The scores then need no integer-to-float
   // conversion, and their max is a float max. With per-key scales each score
-  // is multiplied by its key's scale anyway, and the integer dot product is
-  // converted (exactly) instead: one constant per key instead of two.
+  // is multiplied by its key's scale anyway: the accumulator starts at the
+  // same bias and x - kBiasInt 2^-26 = dot 2^-26 (exact, one subtraction,
+  // cheaper than an integer-to-float conversion) is scaled by the key's
+  // scale, the 2^26 going into the row's factor: one constant per key
+  // instead of two.
   constexpr bool kBiasAcc = !FP8 && !TOK;
   // INT8 products start from bias_acc (the float bias and/or the INT4 K
   // offset correction); otherwise from zero.
-  constexpr bool kStartAcc = kBiasAcc || kK4;
+  constexpr bool kTokBias = !FP8 && TOK;  // per-key scales on the biased accumulator
+  constexpr bool kStartAcc = kBiasAcc || kK4 || kTokBias;
   constexpr uint32_t kBiasBits = 0x3E22F983u;
   constexpr int kBiasInt = 10680707;  // 2^23 + 0x22F983
   static_assert(D <= 128, "biased INT8 scores need |dot| < 2^21");
@@ -547,7 +552,7 @@ __device__ __forceinline__ bool fwd_item(const FwdParams& p, uint8_t* kbuf0, uin
   // copy, so the compiler does not rebuild the splat for every use): the
   // float bias with block scales, and with offset INT4 K codes minus
   // 8 * (sum of the row's Q codes over both lane halves).
-  int bias0 = kBiasAcc ? (int)kBiasBits : 0;
+  int bias0 = (kBiasAcc || kTokBias) ? (int)kBiasBits : 0;
   if constexpr (kK4) {
     int qsum = 0;
 #pragma unroll
@@ -808,9 +813,9 @@ __device__ __forceinline__ bool fwd_item(const FwdParams& p, uint8_t* kbuf0, uin
           pb[kb][r >> 3][(r & 7) + 1] = h2[1];
         }
     } else {
-      // Per-key scales: y_j = sk_j dot_j (the integer dot product converted
-      // exactly, one rounding in the product) and the score in log2 units is
-      // cq y_j. The V scales are folded into the staged V
+      // Per-key scales: y_j = sk_j dot_j (the dot product exact, one rounding
+      // in the product; INT8 y_j carries a factor 2^-26, taken back in cqe)
+      // and the score in log2 units is cq y_j. The V scales are folded into the staged V
       // (code * sv_j / sv_ref), so the weights are the probabilities
       // themselves and O is kept in units of sv_ref, which only grows.
       const float vr = tile_vref;
@@ -822,7 +827,7 @@ __device__ __forceinline__ bool fwd_item(const FwdParams& p, uint8_t* kbuf0, uin
       }
       // A zero Q scale makes every score of the row 0; the floor keeps -inf
       // (masked) times it from giving NaN.
-      const float cqe = fmaxf(cq, 1e-30f);
+      const float cqe = fmaxf(cq, 1e-30f) * (kTokBias ? 67108864.0f : 1.0f);
       float y[2][16];
       float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -833,7 +838,9 @@ __device__ __forceinline__ bool fwd_item(const FwdParams& p, uint8_t* kbuf0, uin
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * rg + i;
-            float yv = (float)sacc[kb][r] * a4[i];
+            // x - B = dot 2^-26 exactly (the 2^26 is folded into cqe).
+            float yv = kTokBias ? (__int_as_float(sacc[kb][r]) - __int_as_float(kBiasBits)) * a4[i]
+                                : (float)sacc[kb][r] * a4[i];
             if constexpr (MASK && CAUSAL) yv = key_of(kb, r) > lim ? -INFINITY : yv;
             y[kb][r] = yv;
             mc[i] = fmaxf(mc[i], yv);
