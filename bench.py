@@ -14,7 +14,10 @@ Sub-objects: the same step on the INT8 causal (``int8_causal_h32_s4096``) and
 FP8 rotated (``fp8_rot_b2_h24_s4608``) workloads, the tiny INT8 workload's
 latency, the quantizer and the fused rotate+quantize (after a 512 MiB cache
 flush and cache-resident), the INT8 and INT4 KV-cache decode (after a flush),
-the KV append, and the mixed INT8 Q/K + INT4 V forward.
+the KV append, and the mixed INT8 Q/K + INT4 V forward. ``attainable`` holds what
+plain library kernels reach on the same box (fp16 and INT8
+GEMMs, a 512 MiB copy), and every MFMA roofline carries ``frac_attainable``
+against the INT8 GEMM.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -360,6 +363,53 @@ def bench_decode(torch, qfa, wl, w, steps, warmup, flush, prof):
             "roofline": hbm_roofline(nbytes, ms, profiled_traffic(prof, DECODE_SRC))}
 
 
+def measure_attainable(torch, flush):
+    """What plain library kernels reach on this machine, on the same stream and
+    clocks as the timed kernels, so that the MFMA roofline fractions can be
+    read against a measured ceiling as well as the nominal peak: a 8192^3
+    fp16 GEMM, where torch provides it a 8192^3 INT8 GEMM (torch._int_mm),
+    and a 512 MiB device copy (read + write bytes; torch's copy is no
+    read-only ceiling, so HBM fractions stay against the nominal 8 TB/s)."""
+    dst = torch.empty_like(flush)
+    copy_ms = time_calls(torch, lambda: dst.copy_(flush), 7)
+    del dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.float16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.float16)
+    gemm_ms = time_calls(torch, lambda: torch.matmul(a, b), 7)
+    r = {"hbm_copy_gbs": round(2 * FLUSH_BYTES / (copy_ms * 1e-3) / 1e9, 1),
+         "fp16_gemm_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+         "int8_gemm_tops": None,
+         "note": "copy: torch copy_ of 512 MiB, read + write bytes; gemm: torch.matmul / "
+                 "torch._int_mm, 8192^3; medians of 7"}
+    del a, b
+    try:
+        a8 = torch.randint(-127, 128, (n, n), device="cuda", dtype=torch.int8)
+        b8 = torch.randint(-127, 128, (n, n), device="cuda", dtype=torch.int8)
+        i8_ms = time_calls(torch, lambda: torch._int_mm(a8, b8), 7)
+        r["int8_gemm_tops"] = round(2 * n ** 3 / (i8_ms * 1e-3) / 1e12, 1)
+        del a8, b8
+    except Exception as e:  # not every torch build has an INT8 GEMM on this GPU
+        log(f"int8 gemm probe unavailable: {type(e).__name__}")
+    torch.cuda.empty_cache()
+    return r
+
+
+def add_attainable(rec, att):
+    """frac_attainable beside every MFMA roofline's frac: the achieved rate
+    over the INT8 GEMM's (the dense INT8 and FP8 peaks are equal)."""
+    def visit(d):
+        for k, v in d.items():
+            if isinstance(v, dict):
+                if k.startswith("roofline"):
+                    if v.get("bound") == "mfma":
+                        ref = att["int8_gemm_tops"]
+                        v["frac_attainable"] = round(v["achieved"] / ref, 4) if ref else None
+                else:
+                    visit(v)
+    visit(rec)
+
+
 def cpu_baseline(wl, target_s=10.0):
     """The oracle (quantize + float64 causal attention) on blocks of 512 query
     rows of the headline workload, cycling over heads and row blocks until
@@ -486,6 +536,10 @@ def main():
                                     "decode_int4_kv_b32_h32_gqa16.md")):
                 rec[key] = bench_decode(torch, qfa, wl, dwl, args.steps, args.warmup, flush, prof)
                 log(f"{key} {rec[key]['ms']:.3f} ms, {rec[key]['value']:.0f} GB/s")
+    att = measure_attainable(torch, flush)
+    log(f"attainable: {att}")
+    rec["attainable"] = att
+    add_attainable(rec, att)
     if args.copy_probe:
         # A plain elementwise copy of known size: reads 1 GiB (fp32), writes 512 MiB (fp16).
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
