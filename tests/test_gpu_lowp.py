@@ -134,3 +134,31 @@ def test_peaky_rows_fall_back():
     q = qf.to(q.dtype)
     frac = _run(w, q, k, v)
     assert frac > 0.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bsnd_equals_bnsd(causal):
+    """The layout changes addresses only: with BSND tensors the fp8 P.V forward
+    gives the BNSD outputs bit for bit and the same flags, including the work
+    items its workgroups recompute with the fp16 product (causal rows near the
+    start are carried by few keys and flag)."""
+    w = wl.scaled(wl.FP8_ROT, name=f"fp8_layouts_c{int(causal)}", B=2, Hq=4, Hkv=2, S=777,
+                  causal=causal, rotate_qk=False)
+    say(f"lowp layouts case {w.name}")
+    q, k, v = wl.make_prefill_inputs(w)
+    sdt = SDT[w.kv_scale_dtype]
+    qc, qs = qfa.block_quant(q.cuda(), w.q_block, "fp8", SDT[w.q_scale_dtype])
+    kc, ks = qfa.block_quant(k.cuda(), w.kv_block, "fp8", sdt)
+    vc, vs = qfa.block_quant(v.cuda(), w.kv_block, "fp8", sdt)
+    kw = dict(q_qtype="fp8", k_qtype="fp8", v_qtype="fp8", q_block=w.q_block,
+              kv_block=w.kv_block, softmax_scale=w.softmax_scale, causal=w.causal,
+              out_dtype=wl.torch_dtype(w.out_dtype))
+    o1, f1 = qfa.fwd_lowp(qc, qs, kc, ks, vc, vs, layout="bnsd", **kw)
+    t = lambda x: x.transpose(1, 2).contiguous()  # noqa: E731
+    o2, f2 = qfa.fwd_lowp(t(qc), qs, t(kc), ks, t(vc), vs, layout="bsnd", **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(f1.cpu(), f2.cpu()), "flags differ between layouts"
+    assert torch.equal(o2.transpose(1, 2).cpu().view(torch.int16), o1.cpu().view(torch.int16)), \
+        "outputs differ between layouts"
+    if causal:
+        assert int(f1.cpu().sum()) > 0, "causal rows near the start must flag"
