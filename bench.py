@@ -307,8 +307,8 @@ def bench_rotate_quant(torch, qfa, wl, steps, warmup, flush):
 def bench_kv_append(torch, qfa, wl, steps, warmup):
     """One decode step's cache update on the decode workload's shape: the new K
     and V rows of every sequence quantized into INT8 caches (fp16 scales per
-    256 rows), at positions inside existing blocks. Average time of the pair
-    from per-call HIP events."""
+    256 rows), at positions inside existing blocks: both rows in one launch, and
+    as two launches. Average times from per-call HIP events."""
     w = wl.DECODE
     gen = torch.Generator(device="cuda").manual_seed(w.seed)
     kc = torch.randint(-127, 128, (w.B, w.Hkv, w.S_max, w.D), generator=gen, device="cuda",
@@ -323,22 +323,29 @@ def bench_kv_append(torch, qfa, wl, steps, warmup):
     xv = torch.randn(w.B, w.Hkv, w.D, generator=gen, device="cuda").to(torch.float16)
     ak = qfa.kv_append(xk, pos, kc, ks, w.kv_block, "int8", prepare=True)
     av = qfa.kv_append(xv, pos, vc, vs, w.kv_block, "int8", prepare=True)
+    akv = qfa.kv_append_kv(xk, xv, pos, kc, ks, vc, vs, w.kv_block, "int8", prepare=True)
 
     def pair():
         ak()
         av()
-    for _ in range(warmup + 5):
-        pair()
-    torch.cuda.synchronize()
-    evs = [_events(torch) for _ in range(steps)]
-    for a, b in evs:
-        a.record()
-        pair()
-        b.record()
-    torch.cuda.synchronize()
-    return {"workload": w.name, "ms": round(sum(a.elapsed_time(b) for a, b in evs) / steps, 4),
-            "note": "latency of one decode step's K and V row appends (two launches); "
-                    "no roofline: a few KB per call"}
+
+    def avg(fn):
+        for _ in range(warmup + 5):
+            fn()
+        torch.cuda.synchronize()
+        evs = [_events(torch) for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / steps
+    two = avg(pair)
+    one = avg(akv)
+    return {"workload": w.name, "ms": round(one, 4), "ms_two_calls": round(two, 4),
+            "note": "latency of one decode step's K and V row appends: one qfa_kv_append_kv "
+                    "launch (ms), two qfa_kv_append launches (ms_two_calls); no roofline: a few "
+                    "KB per call"}
 
 
 def bench_decode(torch, qfa, wl, w, steps, warmup, flush, prof):

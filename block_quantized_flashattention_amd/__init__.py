@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.qfa_block_quant_multi.restype = i
     L.qfa_kv_append.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
     L.qfa_kv_append.restype = i
+    L.qfa_kv_append_kv.argtypes = [vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    L.qfa_kv_append_kv.restype = i
     L.qfa_rotate_block_quant.argtypes = [vp, i, vp, i, i, i, i, i, i, i, vp, vp, i, vp]
     L.qfa_rotate_block_quant.restype = i
     L.qfa_fwd.argtypes = [vp, vp, i, i, i, vp, vp, i, vp, vp, i, i, i,
@@ -259,6 +261,42 @@ def kv_append(x: torch.Tensor, positions: torch.Tensor, codes: torch.Tensor,
         return launch
     _check("qfa_kv_append", f(*args))
     return codes, scales
+
+
+def kv_append_kv(xk: torch.Tensor, xv: torch.Tensor, positions: torch.Tensor,
+                 k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                 v_scales: torch.Tensor, kv_block: int, qtype: str, layout: str = "bnsd",
+                 stream=None, prepare: bool = False):
+    """``kv_append`` of a decode step's K and V rows in one launch (see
+    qfa_kv_append_kv); returns (k_codes, k_scales, v_codes, v_scales), or with
+    ``prepare=True`` a launcher that repeats the marshalled call."""
+    for t, n in ((xk, "xk"), (xv, "xv"), (positions, "positions"), (k_codes, "k_codes"),
+                 (k_scales, "k_scales"), (v_codes, "v_codes"), (v_scales, "v_scales")):
+        _dev(t, n)
+    if positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    B, H, D = xk.shape
+    _expect(xv, (B, H, D), (xk.dtype,), "xv")
+    S_max = k_codes.shape[2] if layout == "bnsd" else k_codes.shape[1]
+    cs = (B, H, S_max, D) if layout == "bnsd" else (B, S_max, H, D)
+    for c, s, n in ((k_codes, k_scales, "k"), (v_codes, v_scales, "v")):
+        _expect(c, _code_shape(cs, qtype), (code_dtype(qtype),), f"{n}_codes")
+        _expect(s, (B, H, -(-S_max // kv_block)), _SCALE_DTYPES, f"{n}_scales")
+    if v_scales.dtype != k_scales.dtype:
+        raise ValueError("k_scales and v_scales must have the same dtype")
+    _expect(positions, (B,), (torch.int32,), "positions")
+    if xk.dtype not in FLOATS:
+        raise ValueError(f"xk has dtype {xk.dtype}")
+    args = (_ptr(xk), _ptr(xv), FLOATS[xk.dtype], _ptr(positions), _ptr(k_codes), _ptr(k_scales),
+            _ptr(v_codes), _ptr(v_scales), B, H, S_max, D, LAYOUTS[layout], kv_block,
+            QTYPES[qtype], FLOATS[k_scales.dtype], _stream(stream))
+    f = lib().qfa_kv_append_kv
+    if prepare:
+        def launch():
+            _check("qfa_kv_append_kv", f(*args))
+        return launch
+    _check("qfa_kv_append_kv", f(*args))
+    return k_codes, k_scales, v_codes, v_scales
 
 
 def rotate_block_quant(x: torch.Tensor, w: torch.Tensor, block_rows: int, qtype: str,
@@ -506,7 +544,7 @@ def prepare_decode(q, k_cache, v_cache, k_scales, v_scales, seq_lens, *, kv_qtyp
 
 
 __all__ = ["block_quant", "block_quant_multi", "prepare_block_quant_multi", "rotate_block_quant",
-           "prepare_rotate_block_quant", "kv_append", "fwd", "prepare_fwd", "fwd_lowp",
+           "prepare_rotate_block_quant", "kv_append", "kv_append_kv", "fwd", "prepare_fwd", "fwd_lowp",
            "prepare_fwd_lowp", "fwd_lowp_workspace_bytes",
            "decode", "prepare_decode", "decode_workspace_bytes", "decode_noalloc",
            "decode_noalloc_max_bytes", "lib", "header_functions",

@@ -100,21 +100,53 @@ int qfa_rotate_block_quant(const void* x, int x_dtype, const void* w, int B, int
   return from_hip(qfa::launch_rotate_block_quant(a, (hipStream_t)stream));
 }
 
-int qfa_kv_append(const void* x, int x_dtype, const int32_t* positions, void* codes, void* scales,
-                  int B, int H, int S_max, int D, int layout, int kv_block, int qtype,
-                  int scale_dtype, void* stream) {
+// Checks of one cache's arguments for qfa_kv_append and qfa_kv_append_kv;
+// QFA_OK with *empty set when B * H == 0 (nothing to launch).
+static int kv_append_check(const void* x, int x_dtype, const int32_t* positions, void* codes,
+                           void* scales, int B, int H, int S_max, int D, int layout, int kv_block,
+                           int qtype, int scale_dtype, bool* empty) {
+  *empty = false;
   if (!valid_float(x_dtype) || !valid_layout(layout) || !valid_qtype(qtype) ||
       (scale_dtype != QFA_F32 && scale_dtype != QFA_F16))
     return QFA_ERR_ENUM;
   if (B < 0 || H < 0 || S_max < 1 || D < 8 || D % 8 != 0 || kv_block < 1) return QFA_ERR_SHAPE;
   if (qtype == QFA_FP8_E4M3 || D > (qtype == QFA_INT4 ? 512 : 256)) return QFA_ERR_UNSUPPORTED;
-  if ((long)B * H == 0) return QFA_OK;
+  if ((long)B * H == 0) {
+    *empty = true;
+    return QFA_OK;
+  }
   if (!x || !positions || !codes || !scales) return QFA_ERR_NULL;
   if (!aligned(x, x_dtype == QFA_F32 ? 4 : 2) || !aligned(positions, 4) ||
       !aligned(scales, scale_dtype == QFA_F16 ? 2 : 4))
     return QFA_ERR_UNSUPPORTED;
+  return QFA_OK;
+}
+
+int qfa_kv_append(const void* x, int x_dtype, const int32_t* positions, void* codes, void* scales,
+                  int B, int H, int S_max, int D, int layout, int kv_block, int qtype,
+                  int scale_dtype, void* stream) {
+  bool empty;
+  const int st = kv_append_check(x, x_dtype, positions, codes, scales, B, H, S_max, D, layout,
+                                 kv_block, qtype, scale_dtype, &empty);
+  if (st != QFA_OK || empty) return st;
   qfa::AppendArgs a{x, x_dtype, positions, codes, scales, B, H, S_max, D, layout, kv_block, qtype,
-                    scale_dtype};
+                    scale_dtype, nullptr, nullptr, nullptr};
+  return from_hip(qfa::launch_kv_append(a, (hipStream_t)stream));
+}
+
+int qfa_kv_append_kv(const void* xk, const void* xv, int x_dtype, const int32_t* positions,
+                     void* k_codes, void* k_scales, void* v_codes, void* v_scales, int B, int H,
+                     int S_max, int D, int layout, int kv_block, int qtype, int scale_dtype,
+                     void* stream) {
+  bool empty;
+  int st = kv_append_check(xk, x_dtype, positions, k_codes, k_scales, B, H, S_max, D, layout,
+                           kv_block, qtype, scale_dtype, &empty);
+  if (st != QFA_OK || empty) return st;
+  st = kv_append_check(xv, x_dtype, positions, v_codes, v_scales, B, H, S_max, D, layout,
+                       kv_block, qtype, scale_dtype, &empty);
+  if (st != QFA_OK) return st;
+  qfa::AppendArgs a{xk, x_dtype, positions, k_codes, k_scales, B, H, S_max, D, layout, kv_block,
+                    qtype, scale_dtype, xv, v_codes, v_scales};
   return from_hip(qfa::launch_kv_append(a, (hipStream_t)stream));
 }
 

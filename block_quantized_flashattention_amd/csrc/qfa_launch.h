@@ -55,6 +55,11 @@ struct AppendArgs {
   int kv_block;
   int qtype;
   int scale_dtype;
+  // A second cache updated in the same launch (the V row of a decode step),
+  // same sizes and types; x2 null for one cache.
+  const void* x2;
+  void* codes2;
+  void* scales2;
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);

@@ -652,8 +652,9 @@ hipError_t launch_rot_qt(const RotParams& p, int qtype, long grid, int w, hipStr
 }
 
 // ---- Appending one token to a quantized KV cache -------------------------
-// One workgroup per (batch, KV head) puts the new row at position p of the
-// sequence into block r = p / R. When the block already has rows, a nonzero
+// One workgroup per (batch, KV head) and cache puts the new row at position p
+// of the sequence into block r = p / R (with a second cache, the K and V rows
+// of a decode step in one launch: workgroups B*H.. take the second). When the block already has rows, a nonzero
 // scale s and fl32(max|x| / s) <= qmax (or x is all zero), only the new row is
 // quantized, with s. Otherwise the block is requantized as a whole: its old
 // rows' values fl32(code * s) and the new row get a new scale from their
@@ -664,6 +665,10 @@ struct AppendParams {
   const int32_t* pos;
   char* codes;
   void* scales;
+  const void* x2;  // second cache (workgroups BH..2 BH - 1), or null
+  char* codes2;
+  void* scales2;
+  int BH;          // B * H: workgroups per cache
   int H, S_max, D, R, nblk;
   long c_row, c_head, c_batch;  // byte strides of codes
   int x_dtype, scale_f16;
@@ -713,7 +718,12 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
   constexpr int kPer = QT == QFA_INT4 ? 2 : 1;  // channels per code byte
   constexpr float kQmax = QT == QFA_INT4 ? 7.0f : 127.0f;
   __shared__ uint32_t red[kAppendThreads / 64];
-  const int bh = blockIdx.x;
+  // Which cache this workgroup updates (uniform selects, no branch).
+  const bool second = (int)blockIdx.x >= p.BH;
+  const int bh = second ? (int)blockIdx.x - p.BH : (int)blockIdx.x;
+  const void* x = second ? p.x2 : p.x;
+  char* codes = second ? p.codes2 : p.codes;
+  void* scales = second ? p.scales2 : p.scales;
   const int b = bh / p.H, h = bh % p.H;
   const int pp = p.pos[b];
   if (pp < 0 || pp >= p.S_max) return;  // the whole workgroup leaves
@@ -724,14 +734,14 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
   // The block's stored scale, requested with the new row (used only when the
   // block already has rows).
   const long si = (long)bh * p.nblk + r;
-  const float s_stored = load_scale(p.scales, si, p.scale_f16);
+  const float s_stored = load_scale(scales, si, p.scale_f16);
   // The new row: this thread's code byte holds channels kPer*tid .. + kPer-1.
   float xv[kPer];
   uint32_t ax = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     xv[j] = 0.0f;
-    if (tid < nbytes) xv[j] = load_value(p.x, ((long)b * p.H + h) * p.D + kPer * tid + j, p.x_dtype);
+    if (tid < nbytes) xv[j] = load_value(x, ((long)b * p.H + h) * p.D + kPer * tid + j, p.x_dtype);
     ax = max(ax, __float_as_uint(xv[j]) & 0x7FFFFFFFu);
   }
   ax = wg_max(ax, red);
@@ -739,7 +749,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
   const float s_old = nold == 0 ? 0.0f : s_stored;
   bool fits = false;
   if (nold > 0) fits = s_old > 0.0f ? amax_x / s_old <= kQmax : amax_x == 0.0f;
-  char* cb = p.codes + (long)b * p.c_batch + (long)h * p.c_head;
+  char* cb = codes + (long)b * p.c_batch + (long)h * p.c_head;
 
   float s = s_old;
   if (!fits) {
@@ -765,8 +775,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendParams 
     s = amax / kQmax;
     if (p.scale_f16) s = (float)(_Float16)s;
     if (tid == 0) {
-      if (p.scale_f16) ((uint16_t*)p.scales)[si] = (uint16_t)f32_to_f16_bits(s);
-      else ((float*)p.scales)[si] = s;
+      if (p.scale_f16) ((uint16_t*)scales)[si] = (uint16_t)f32_to_f16_bits(s);
+      else ((float*)scales)[si] = s;
     }
   }
   const bool zero = !(s != 0.0f);
@@ -861,6 +871,9 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
   p.pos = a.positions;
   p.codes = (char*)a.codes;
   p.scales = a.scales;
+  p.x2 = a.x2;
+  p.codes2 = (char*)a.codes2;
+  p.scales2 = a.scales2;
   p.H = a.H;
   p.S_max = a.S_max;
   p.D = a.D;
@@ -877,9 +890,11 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
   p.c_batch = (long)a.H * a.S_max * cD;
   p.x_dtype = a.x_dtype;
   p.scale_f16 = a.scale_dtype == QFA_F16;
-  const long grid = (long)a.B * a.H;
+  const long bh = (long)a.B * a.H;
+  const long grid = a.x2 ? 2 * bh : bh;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  p.BH = (int)bh;
   if (a.qtype == QFA_INT4) kv_append_kernel<QFA_INT4><<<grid, kAppendThreads, 0, stream>>>(p);
   else kv_append_kernel<QFA_INT8><<<grid, kAppendThreads, 0, stream>>>(p);
   return hipGetLastError();

@@ -176,6 +176,21 @@ QFA_API int qfa_kv_append(const void* x, int x_dtype, const int32_t* positions, 
                           void* scales, int B, int H, int S_max, int D, int layout, int kv_block,
                           int qtype, int scale_dtype, void* stream);
 
+/*
+ * qfa_kv_append_kv -- qfa_kv_append on the K cache and the V cache of one
+ * decode step in a single launch ([Ascend-INT8] section 3, as qfa_kv_append):
+ * row positions[b] of sequence b receives xk[b, h, :] in (k_codes, k_scales)
+ * and xv[b, h, :] in (v_codes, v_scales), each cache updated exactly as
+ * qfa_kv_append updates it (byte-identical to two calls). Both caches have
+ * the sizes, layout, code type and scale type given; they must not overlap.
+ * Arguments, limits and error codes as qfa_kv_append, checked for the K
+ * arguments first, then for the V ones; nothing is launched on an error.
+ */
+QFA_API int qfa_kv_append_kv(const void* xk, const void* xv, int x_dtype,
+                             const int32_t* positions, void* k_codes, void* k_scales,
+                             void* v_codes, void* v_scales, int B, int H, int S_max, int D,
+                             int layout, int kv_block, int qtype, int scale_dtype, void* stream);
+
 QFA_API int qfa_rotate_block_quant(const void* x, int x_dtype, const void* w, int B, int N, int S,
                                    int D, int layout, int block_rows, int qtype, void* codes,
                                    void* scales, int scale_dtype, void* stream);

@@ -24,6 +24,7 @@ def test_exports_every_declared_function(L):
     names = qfa.header_functions()
     assert set(names) == {"qfa_version", "qfa_status_string", "qfa_block_quant",
                           "qfa_block_quant_multi", "qfa_rotate_block_quant", "qfa_kv_append",
+                          "qfa_kv_append_kv",
                           "qfa_fwd", "qfa_fwd_lowp", "qfa_fwd_lowp_workspace_bytes",
                           "qfa_decode_workspace_bytes", "qfa_decode",
                           "qfa_decode_noalloc_max_bytes", "qfa_decode_noalloc"}
@@ -124,6 +125,27 @@ def test_kv_append_validation(L):
     assert app(L, scales=None) == NULL
     assert app(L, scales=ctypes.c_void_p(257)) == UNSUP
     assert app(L, B=0, x=None, pos=None, codes=None, scales=None) == OK
+
+
+def app2(L, xk=P, xv=P, dt=F16, pos=P, kc=P, ks=P, vc=P, vs=P, B=2, H=4, S=512, D=128,
+         layout=BNSD, R=256, qt=I8, sdt=F16):
+    return L.qfa_kv_append_kv(xk, xv, dt, pos, kc, ks, vc, vs, B, H, S, D, layout, R, qt, sdt,
+                              None)
+
+
+def test_kv_append_kv_validation(L):
+    """The K and V append in one launch checks both caches' arguments as the
+    single append does, and launches nothing on an error."""
+    assert app2(L, dt=7) == ENUM
+    assert app2(L, qt=F8) == UNSUP
+    assert app2(L, D=12) == SHAPE
+    assert app2(L, xk=None) == NULL
+    assert app2(L, xv=None) == NULL
+    assert app2(L, vc=None) == NULL
+    assert app2(L, vs=None) == NULL
+    assert app2(L, ks=ctypes.c_void_p(257)) == UNSUP
+    assert app2(L, vs=ctypes.c_void_p(257)) == UNSUP
+    assert app2(L, B=0, xk=None, xv=None, pos=None, kc=None, ks=None, vc=None, vs=None) == OK
 
 
 def fwd(L, q=P, qs=P, qqt=I8, qb=128, qsd=F32, k=P, ks=P, kqt=I8, v=P, vs=P, vqt=I8, kb=256,

@@ -93,3 +93,41 @@ def test_kv_append_row_dtypes(xdt, qtype):
     x[0] *= 0.25
     x[1] *= 40.0
     _append_and_check(codes, scales, x.to(xdt), [200, R + 100, 599], R, qtype, "bnsd")
+
+
+@pytest.mark.parametrize("qtype,layout,sdt", [("int8", "bnsd", "f16"), ("int4", "bsnd", "f32"),
+                                              ("int4", "bnsd", "f16")])
+def test_kv_append_kv_equals_two_appends(qtype, layout, sdt):
+    """qfa_kv_append_kv (K and V rows of a decode step in one launch) leaves
+    both caches byte-identical to two qfa_kv_append calls, with rows that fit
+    their block's scale, rows that force a requantization, a new block and an
+    out-of-range position, over three steps; the K cache also matches the
+    oracle."""
+    B, H, S, D, R = 4, 3, 600, 128, 256
+    say(f"kv append K+V {qtype} {layout} {sdt}")
+    kc, ks = _cache(B, H, S, D, R, qtype, sdt, layout, seed=31)
+    vc, vs = _cache(B, H, S, D, R, qtype, sdt, layout, seed=32)
+    kc2, ks2, vc2, vs2 = kc.clone(), ks.clone(), vc.clone(), vs.clone()
+    gen = torch.Generator().manual_seed(12)
+    pos0 = [R, R + 5, S - 3, -1]
+    for step in range(3):
+        pos = torch.tensor([p + step if p >= 0 else p for p in pos0], dtype=torch.int32).cuda()
+        xk = torch.randn(B, H, D, generator=gen).to(torch.float16)
+        xv = torch.randn(B, H, D, generator=gen).to(torch.float16)
+        xk[step % B] *= 40.0
+        xv[(step + 1) % B] *= 40.0
+        before_c, before_s = kc.cpu().numpy().copy(), ks.cpu().numpy().copy()
+        qfa.kv_append_kv(xk.cuda(), xv.cuda(), pos, kc, ks, vc, vs, R, qtype, layout)
+        qfa.kv_append(xk.cuda(), pos, kc2, ks2, R, qtype, layout)
+        qfa.kv_append(xv.cuda(), pos, vc2, vs2, R, qtype, layout)
+        torch.cuda.synchronize()
+        for a, b, n in ((kc, kc2, "K codes"), (ks, ks2, "K scales"), (vc, vc2, "V codes"),
+                        (vs, vs2, "V scales")):
+            assert torch.equal(a.cpu().view(torch.uint8) if a.element_size() == 1 else a.cpu(),
+                               b.cpu().view(torch.uint8) if b.element_size() == 1 else b.cpu()), \
+                f"{n} differ at step {step}"
+        ref_c, ref_s = oracle.kv_append(before_c, before_s, xk, pos.cpu().tolist(), R, qtype, sdt,
+                                        layout)
+        np.testing.assert_array_equal(ks.cpu().numpy().view(np.uint8), ref_s.view(np.uint8))
+        np.testing.assert_array_equal(kc.cpu().numpy().view(np.uint8),
+                                      np.asarray(ref_c).view(np.uint8))
