@@ -164,3 +164,33 @@ def test_rows_past_length_are_ignored(qt, R, layout):
             ref.append(oracle.decode(q[b:b + 1, grp].double().numpy(), kh, vh, [L], w.softmax_scale))
             got.append(out[b:b + 1, grp].double().cpu().numpy())
     assert_close(np.concatenate(got), np.concatenate(ref), f"{w.name} stale rows")
+
+
+def _decode_sweep(n=16, seed=77):
+    """Seeded random small decode configurations: INT8 or INT4 cache, D,
+    group size 1..16, lengths anywhere in [1, S_max] (not multiples of the
+    block or chunk), block or per-token scales, scale dtype and layout."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        qt = str(rng.choice(["int8", "int4"]))
+        Hkv = int(rng.choice([1, 2]))
+        group = int(rng.choice([1, 2, 4, 16]))
+        D = int(rng.choice([64, 128]))
+        S_max = int(rng.integers(2, 3500))
+        B = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.integers(1, S_max + 1, B)]
+        R = int(rng.choice([1, 64, 128, 256])) if qt == "int4" else int(rng.choice([64, 128, 256]))
+        cases.append((f"sweep{i}_{qt}_g{group}", B, Hkv * group, Hkv, D, S_max, lens, qt, R,
+                      str(rng.choice(["f16", "f32"])), str(rng.choice(["bnsd", "bsnd"]))))
+    return cases
+
+
+_SWEEP = _decode_sweep()
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,S_max,lens,qt,R,sdt,layout", _SWEEP,
+                         ids=[f"{c[0]}_{c[7]}_r{c[8]}_{c[10]}" for c in _SWEEP])
+def test_decode_seeded_sweep(name, B, Hq, Hkv, D, S_max, lens, qt, R, sdt, layout):
+    """Random small decode shapes (fixed seed) against the oracle, every head."""
+    test_small_decode(name, B, Hq, Hkv, D, S_max, lens, qt, R, sdt, layout)

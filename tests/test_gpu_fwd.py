@@ -175,3 +175,37 @@ def test_per_token_v_scales_spanning_four_decades():
                            oracle.dequantize(rv, rvs, 1, "int4"), w.softmax_scale, causal=True)
     unit = float(mag.max())
     assert_close(out.double().cpu().numpy() / unit, ref / unit, "V rows 1e-2..1e2")
+
+
+def _sweep_cases(n=24, seed=2024):
+    """Seeded random small forward configurations: code-type combination,
+    D, GQA group, ragged S, causal or not, block sizes (per-key scales when
+    the K/V block does not cover 64-key tiles, per-token for INT4), scale
+    dtypes and layout."""
+    rng = np.random.default_rng(seed)
+    bases = [wl.INT8_CAUSAL, wl.FP8_ROT, wl.GQA_INT4, wl.INT8QK_INT4V]
+    cases = []
+    for i in range(n):
+        base = bases[i % len(bases)]
+        Hkv = int(rng.choice([1, 2]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        D = int(rng.choice([64, 128]))
+        S = int(rng.integers(1, 420))
+        kvb = int(rng.choice([1, 16, 64, 96, 256])) if base.k_qtype == "int4" else \
+            int(rng.choice([32, 64, 96, 256]))
+        qb = int(rng.choice([16, 48, 64, 128]))
+        sdt = str(rng.choice(["f32", "f16"]))
+        w = wl.scaled(base, name=f"sweep{i}_{base.q_qtype}_{base.k_qtype}{base.v_qtype}",
+                      B=int(rng.integers(1, 3)), Hq=Hkv * group, Hkv=Hkv, S=S, D=D,
+                      causal=bool(rng.integers(0, 2)), q_block=qb, kv_block=kvb,
+                      q_scale_dtype=sdt, kv_scale_dtype=str(rng.choice(["f32", "f16"])),
+                      softmax_scale=float(np.float32(1 / np.sqrt(D))), rotate_qk=False,
+                      k_outlier_channels=min(base.k_outlier_channels, 2))
+        cases.append((w, str(rng.choice(["bnsd", "bsnd"]))))
+    return cases
+
+
+@pytest.mark.parametrize("w,layout", _sweep_cases(), ids=lambda c: getattr(c, "name", c))
+def test_seeded_sweep(w, layout):
+    """Random small shapes (fixed seed) against the oracle, every row."""
+    prefill_parity(w, layout=layout)
